@@ -1,0 +1,192 @@
+/*
+ * kvq.h — C ABI of the MI355X (gfx950) KV-cache vector codec.
+ *
+ * The codec works on one head_dim row ("vector") of a K or V cache at a time:
+ *   norm      n = ||v||_2, stored as f32 inside the record
+ *             [arc PR #98 "TurboQuant KV storage for DeepSeek-V4", section "What landed"];
+ *   rotation  u = H_m (s (.) v), H_m the unnormalised Sylvester Hadamard matrix and s a seeded
+ *             +-1 diagonal [kakeyaturbo PR #15 "v1.3 PPL on vLLM", commits "M4 Phase A" and
+ *             "M4 Phase B"]; optionally v = B^T (x - mu) first, a rank-r PCA projection
+ *             ["M4 Phase A", "M5"];
+ *   scale     z = u / n, i.e. unit-variance units ["M4 Phase B"];
+ *   quantize  code_i = #{k : z_i > t_k}, t_k the midpoints of a Gaussian Lloyd-Max table at b bits
+ *             ["M4 Phase A"; larql PR #196, turbo-quant commit: one N(0,1) table per bit width];
+ *   pack      b bit-planes of the codes + f32 norm = m*b/8 + 4 bytes per record (260 B at
+ *             head_dim 512, 4 bits) [arc PR #98, "What landed" bytes table];
+ *   outliers  optional sparse (coordinate, value) list for |z_i| > T, applied at decode before
+ *             the inverse rotation [PR #15, calibrated Lloyd-Max + outlier commit and "M5"].
+ * Its inverse, a rotated-domain score q.k over packed K, and a two-region cache (bf16 tail +
+ * packed history) with chunked eviction [arc PR #98, "Eviction is chunked, on purpose"]
+ * complete the library.
+ *
+ * Record format v1 (little-endian), for coded length m (m = head_dim, or proj_rank with PCA)
+ * and b bits:
+ *   plane position of coordinate i:  pi(i) = (i mod 8) * (m/8) + floor(i/8)
+ *   word[g*b + p], g in [0, m/32), p in [0, b): bit j = bit p of the code of the coordinate
+ *                                              whose plane position is 32*g + j
+ *   then one f32: the norm n.  Record size = m*b/8 + 4 bytes, always a multiple of 4.
+ * Records of n vectors are stored back to back (stride = kvq_record_bytes()).
+ *
+ * Conventions for every call below.
+ *  - Pointers named *_dev are device memory (HIP), *_host host memory. The caller owns all of
+ *    them; the library allocates nothing and keeps no device state.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously;
+ *    argument errors are detected on the host before anything is enqueued and nothing is then
+ *    launched. A launch failure maps to KVQ_E_DEVICE.
+ *  - All sizes and offsets are 64-bit.
+ *  - On error, kvq_last_error() (thread-local) names the offending argument and value.
+ *  - Rows of bf16 input must start 16-byte aligned: the base pointer 16-byte aligned and
+ *    leading dimensions multiples of 8 elements. Records must be 4-byte aligned.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_E_NULL = 1,       /* a required pointer is NULL                                    */
+  KVQ_E_DIM = 2,        /* head_dim / proj_rank not supported                            */
+  KVQ_E_BITS = 3,       /* bits outside 1..4                                             */
+  KVQ_E_CENTROIDS = 4,  /* custom table not strictly ascending or not finite             */
+  KVQ_E_STRIDE = 5,     /* misaligned pointer or leading dimension                       */
+  KVQ_E_OUTLIER = 6,    /* outlier request invalid (T < 0, m > 256, missing buffers)     */
+  KVQ_E_CAPACITY = 7,   /* a capacity is too small (outlier list, cache region, workspace) */
+  KVQ_E_CACHE = 8,      /* cache struct not built by kvq_cache_init, or built for another codec */
+  KVQ_E_DEVICE = 9,     /* HIP launch / runtime error                                    */
+  KVQ_E_ARG = 10        /* any other invalid argument (negative size, flags != 0, ...)   */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+/* Codec descriptor: caller-owned POD in host memory. */
+typedef struct kvq_codec {
+  uint32_t head_dim;          /* D in {64, 128, 256, 512}                                    */
+  uint32_t bits;              /* b in 1..4                                                   */
+  uint32_t proj_rank;         /* 0: rotate all D coordinates (m = D).
+                                 r in {32, 64, 128, 256}, r < D: PCA projection to r
+                                 coordinates, then rotation over r (m = r)                   */
+  uint32_t flags;             /* reserved, must be 0                                         */
+  uint64_t seed;              /* seed of the +-1 sign diagonal (SplitMix64 stream)           */
+  float outlier_T;            /* 0: no side list. > 0: coordinates with |z| > T are listed
+                                 (requires m <= 256). Units: rotated, normalised (z).        */
+  uint32_t reserved0;         /* must be 0                                                   */
+  const float* centroids_host;   /* f32[2^b] strictly ascending, or NULL = Gaussian Lloyd-Max */
+  const uint16_t* basis_dev;     /* PCA only: bf16 [D][r] row-major, column j = basis vector j */
+  const float* mean_dev;         /* PCA only: f32 [D] mean mu, or NULL = zero mean            */
+} kvq_codec;
+
+/* Outlier side list, CSR by vector. Entry e of vector v is at offsets[v] + e; within a vector
+ * entries are in ascending coordinate order. idx = coordinate index i in [0, m) of the rotated
+ * vector, val = bf16 bits of z_i (round to nearest even). */
+typedef struct kvq_outliers {
+  uint32_t* offsets_dev;   /* [n+1]: written by kvq_encode, read by kvq_decode. offsets[n] is
+                              the total count, which may exceed capacity (entries past
+                              capacity are not written; kvq_decode ignores them)             */
+  uint8_t* idx_dev;        /* [capacity]                                                     */
+  uint16_t* val_dev;       /* [capacity]                                                     */
+  int64_t capacity;        /* entries                                                        */
+  void* workspace_dev;     /* encode only: scratch of kvq_encode_workspace_bytes() bytes,
+                              16-byte aligned; contents need not be initialised              */
+  int64_t workspace_bytes;
+} kvq_outliers;
+
+/* Two-region cache of one (layer, kv-head) stream [arc PR #98, "What landed"]: a bf16 ring
+ * `tail` of the newest rows and a region `packed` of records of older rows. Lengths live on
+ * the host, so no eviction decision needs a device->host synchronisation. Fields are written
+ * only by the library; callers read them. */
+typedef struct kvq_cache {
+  uint64_t magic;          /* set by kvq_cache_init                                          */
+  uint64_t codec_key;      /* fingerprint of the codec the cache was built for               */
+  void* packed_dev;        /* records [packed_cap]                                            */
+  int64_t packed_len, packed_cap;   /* in records (= tokens)                                 */
+  void* tail_dev;          /* bf16 ring [tail_cap][D]                                         */
+  int64_t tail_head;       /* ring slot of the oldest dense row                               */
+  int64_t tail_len, tail_cap;       /* in rows                                               */
+  int32_t window, margin;  /* retention floor = window + max(t_new - 1, margin)               */
+} kvq_cache;
+
+/* Number of tokens moved from the dense tail to the packed region per eviction step
+ * [arc PR #98, "Eviction is chunked, on purpose": EVICT_CHUNK = 128]. */
+#define KVQ_EVICT_CHUNK 128
+
+/* Bytes of one record for this codec: m*b/8 + 4. Returns 0 for an invalid codec. */
+size_t kvq_record_bytes(const kvq_codec* codec);
+
+/* Workspace bytes kvq_encode needs for n vectors when codec->outlier_T > 0 (0 otherwise). */
+size_t kvq_encode_workspace_bytes(const kvq_codec* codec, int64_t n);
+
+/* Host copies of the tables the kernels use, for inspection and tests: centroids f32[2^b],
+ * decision thresholds f32[2^b - 1] (f32 of the midpoints of adjacent centroids), and the sign
+ * diagonal int8[m] (+1 / -1). Any output pointer may be NULL. */
+kvq_status kvq_codec_tables(const kvq_codec* codec, float* centroids_host, float* thresholds_host,
+                            int8_t* signs_host);
+
+/* Encode n vectors. x_dev: bf16 [n][ld_x] (row i at x_dev + i*ld_x elements, first D used).
+ * records_dev: n records. ol: required iff codec->outlier_T > 0, else must be NULL.
+ * ol_total_host: optional; when non-NULL the call synchronises the stream, stores the total
+ * outlier count and returns KVQ_E_CAPACITY if it exceeds ol->capacity.
+ * [kakeyaturbo PR #15, commits "M4 Phase A", "M4 Phase B"; arc PR #98, "What landed"] */
+kvq_status kvq_encode(const kvq_codec* codec, const void* x_dev, int64_t n, int64_t ld_x,
+                      void* records_dev, const kvq_outliers* ol, int64_t* ol_total_host,
+                      void* stream);
+
+/* Decode n records into y_dev [n][ld_y] of dtype y_dtype (bf16: round to nearest even).
+ * x^ = mu + B (n/m) s (.) H_m z^, with z^_i = centroid[code_i] or the outlier value.
+ * ol: NULL, or the side list kvq_encode wrote for these records.
+ * [kakeyaturbo PR #15, commit "M5"] */
+kvq_status kvq_decode(const kvq_codec* codec, const void* records_dev, int64_t n,
+                      const kvq_outliers* ol, void* y_dev, kvq_dtype y_dtype, int64_t ld_y,
+                      void* stream);
+
+/* Raw attention logits over packed K without materialising dense K
+ * [arc PR #98 / #94 kernel commit: paged attention over packed K]:
+ *   scores[b][h][t] = q[b][h] . decode(records[b][h / (Hq/Hkv)][t])
+ * computed in the rotated domain as (n_t/m) * sum_i q'_i z^_{t,i}, q' = H_m (s (.) q) (with PCA
+ * q' = H_r (s (.) B^T q) plus the constant q.mu). No 1/sqrt(D), softcap or softmax.
+ * q_dev: bf16, element q[b][h][d] at q_dev + b*q_sb + h*q_sh + d.
+ * records_dev: record (b, kv, t) at index b*rec_sb + kv*rec_sh + t.
+ * scores_dev: f32, score (b, h, t) at scores_dev + b*s_sb + h*s_sh + t.
+ * Hq must be a multiple of Hkv (query heads h*Hkv/Hq share kv head). Outlier lists are not
+ * consulted (score requires codec->outlier_T == 0). */
+kvq_status kvq_score_packed(const kvq_codec* codec, const void* q_dev, int32_t B, int32_t Hq,
+                            int64_t q_sb, int64_t q_sh, const void* records_dev, int32_t Hkv,
+                            int64_t T, int64_t rec_sb, int64_t rec_sh, float* scores_dev,
+                            int64_t s_sb, int64_t s_sh, void* stream);
+
+/* Build an empty cache over caller-owned buffers: packed_dev holds packed_cap records,
+ * tail_dev holds tail_cap bf16 rows of head_dim. window >= 0, margin >= 0. Host only.
+ * Outlier lists are not supported in caches (codec->outlier_T must be 0). */
+kvq_status kvq_cache_init(const kvq_codec* codec, kvq_cache* cache, void* packed_dev,
+                          int64_t packed_cap, void* tail_dev, int64_t tail_cap, int32_t window,
+                          int32_t margin);
+
+/* Append t_new bf16 rows (new_rows_dev[c]: [t_new][D] contiguous) to each of n_caches caches,
+ * then evict whole chunks of KVQ_EVICT_CHUNK oldest dense rows into the packed region while
+ *   tail_len >= window + max(t_new - 1, margin) + KVQ_EVICT_CHUNK
+ * [arc PR #98, "What landed" (dense-tail bound) and "Mutation runs" (retention floor)].
+ * t_new = 0 flushes. All caches must be built for `codec`; each decides its own eviction count.
+ * Updates the host-side lengths; evicted_host (optional, int64[n_caches]) receives the chunks evicted per cache.
+ * No device->host synchronisation. Errors (capacity, foreign cache) leave every cache as it was. */
+kvq_status kvq_append_evict_chunk(const kvq_codec* codec, kvq_cache* const* caches,
+                                  int32_t n_caches, const void* const* new_rows_dev,
+                                  int64_t t_new, void* stream, int64_t* evicted_host);
+
+/* Message for the last error on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+/* ABI version of this header; record format version. */
+#define KVQ_ABI_VERSION 1
+#define KVQ_RECORD_FORMAT 1
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

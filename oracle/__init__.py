@@ -1,0 +1,256 @@
+"""Plain CPU reference ("oracle") of the KV-cache vector codec.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the CPU-baseline leg of
+the benchmark, never by the library. It shares no code with the GPU path; the C source
+(kvq_oracle.c) is built here with gcc, single-threaded, -O2 without fast-math.
+
+Functions follow the passages cited in kvq_oracle.c. The two-region cache model at the bottom
+follows arc PR #98 ("What landed": dense tail bounded by window + max(t_q - 1, margin) +
+EVICT_CHUNK; "Eviction is chunked, on purpose": EVICT_CHUNK = 128; "Mutation runs": margin 16).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_LIB = os.path.join(_HERE, "libkvq_oracle.so")
+
+FLAG_NEAR_BOUNDARY = 1
+FLAG_NEAR_T = 2
+EVICT_CHUNK = 128
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, no threads, no intrinsics)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-fPIC", "-shared",
+                        "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"],
+                       check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _RefCodec(ctypes.Structure):
+    _fields_ = [("D", ctypes.c_int32), ("bits", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("pad", ctypes.c_int32), ("seed", ctypes.c_uint64), ("T", ctypes.c_double),
+                ("centroids", ctypes.c_void_p), ("basis", ctypes.c_void_p),
+                ("mean", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        _lib.kvq_ref_lloyd_max_gaussian.argtypes = [ctypes.c_int, P, P]
+        _lib.kvq_ref_lloyd_max_gaussian.restype = ctypes.c_int
+        _lib.kvq_ref_thresholds.argtypes = [P, ctypes.c_int, P]
+        _lib.kvq_ref_signs.argtypes = [ctypes.c_uint64, ctypes.c_int, P]
+        _lib.kvq_ref_fwht_rows.argtypes = [P, I64, ctypes.c_int]
+        _lib.kvq_ref_splitmix64.argtypes = [ctypes.c_uint64, ctypes.c_int, P]
+        _lib.kvq_ref_record_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+        _lib.kvq_ref_plane_position.argtypes = [ctypes.c_int, ctypes.c_int]
+        _lib.kvq_ref_unpack_codes.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P]
+        _lib.kvq_ref_encode.argtypes = [ctypes.POINTER(_RefCodec), I64, P, I64, P, P, P, P, P,
+                                        P, P, P, I64]
+        _lib.kvq_ref_encode.restype = I64
+        _lib.kvq_ref_decode.argtypes = [ctypes.POINTER(_RefCodec), I64, P, P, P, P, I64, P]
+        _lib.kvq_ref_score.argtypes = [ctypes.POINTER(_RefCodec), I64, P, P, P]
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+# --------------------------------------------------------------------------------------------
+# Tables and signs
+
+_TABLES: dict[int, tuple[np.ndarray, np.ndarray]] = {}
+
+
+def gaussian_table(bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """(f64 centroids, f32 centroids) of the N(0,1) Lloyd-Max quantiser with 2^bits cells."""
+    if bits not in _TABLES:
+        L = 1 << bits
+        c64 = np.zeros(L, np.float64)
+        c32 = np.zeros(L, np.float32)
+        it = lib().kvq_ref_lloyd_max_gaussian(bits, _p(c64), _p(c32))
+        if it < 0:
+            raise RuntimeError(f"Lloyd-Max iteration failed for bits={bits}")
+        _TABLES[bits] = (c64, c32)
+    c64, c32 = _TABLES[bits]
+    return c64.copy(), c32.copy()
+
+
+def thresholds(c32: np.ndarray) -> np.ndarray:
+    c32 = np.ascontiguousarray(c32, np.float32)
+    t = np.zeros(len(c32) - 1, np.float32)
+    lib().kvq_ref_thresholds(_p(c32), len(c32), _p(t))
+    return t
+
+
+def signs(seed: int, m: int) -> np.ndarray:
+    s = np.zeros(m, np.int8)
+    lib().kvq_ref_signs(seed, m, _p(s))
+    return s
+
+
+def splitmix64(seed: int, n: int) -> np.ndarray:
+    out = np.zeros(n, np.uint64)
+    lib().kvq_ref_splitmix64(seed, n, _p(out))
+    return out
+
+
+def fwht_rows(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a, np.float64).copy()
+    n, m = a.reshape(-1, a.shape[-1]).shape
+    lib().kvq_ref_fwht_rows(_p(a), n, m)
+    return a
+
+
+def record_bytes(m: int, bits: int) -> int:
+    return lib().kvq_ref_record_bytes(m, bits)
+
+
+def plane_position(i: int, m: int) -> int:
+    return lib().kvq_ref_plane_position(i, m)
+
+
+def unpack_codes(m: int, bits: int, rec: np.ndarray) -> tuple[np.ndarray, float]:
+    rec = np.ascontiguousarray(rec, np.uint8)
+    codes = np.zeros(m, np.uint8)
+    nrm = np.zeros(1, np.float32)
+    lib().kvq_ref_unpack_codes(m, bits, _p(rec), _p(codes), _p(nrm))
+    return codes, float(nrm[0])
+
+
+# --------------------------------------------------------------------------------------------
+# Codec
+
+
+class Codec:
+    """Parameters of one codec as the oracle sees them (host arrays only)."""
+
+    def __init__(self, D: int, bits: int, seed: int, r: int = 0, T: float = 0.0,
+                 centroids: np.ndarray | None = None, basis_bf16: np.ndarray | None = None,
+                 mean: np.ndarray | None = None):
+        self.D, self.bits, self.seed, self.r, self.T = D, bits, seed, r, float(T)
+        self.m = r if r > 0 else D
+        if centroids is None:
+            centroids = gaussian_table(bits)[1]
+        self.centroids = np.ascontiguousarray(centroids, np.float32)
+        self.basis = None if basis_bf16 is None else np.ascontiguousarray(basis_bf16, np.uint16)
+        self.mean = None if mean is None else np.ascontiguousarray(mean, np.float32)
+        if r > 0 and (self.basis is None or self.basis.shape != (D, r)):
+            raise ValueError("PCA codec needs a bf16 basis of shape [D][r]")
+        self.rec_bytes = record_bytes(self.m, bits)
+
+    def _c(self) -> _RefCodec:
+        return _RefCodec(self.D, self.bits, self.r, 0, self.seed, self.T,
+                         _p(self.centroids), _p(self.basis), _p(self.mean))
+
+
+def encode(cd: Codec, x_bf16: np.ndarray, ol_cap: int | None = None) -> dict:
+    """Encode rows of x (uint16 bf16 bits, shape [n, D]). Returns a dict with records
+    ([n, rec_bytes] u8), codes and flags ([n, m] u8), z ([n, m] f64), norms ([n] f64) and, when
+    T > 0, the outlier CSR (offsets [n+1] u32, idx u8, val u16 bf16 bits, total)."""
+    x = np.ascontiguousarray(x_bf16, np.uint16).reshape(-1, cd.D)
+    n = x.shape[0]
+    rec = np.zeros((n, cd.rec_bytes), np.uint8)
+    codes = np.zeros((n, cd.m), np.uint8)
+    flags = np.zeros((n, cd.m), np.uint8)
+    z = np.zeros((n, cd.m), np.float64)
+    norms = np.zeros(n, np.float64)
+    out = dict(records=rec, codes=codes, flags=flags, z=z, norms=norms)
+    c = cd._c()
+    if cd.T > 0:
+        cap = n * cd.m if ol_cap is None else ol_cap
+        off = np.zeros(n + 1, np.uint32)
+        idx = np.zeros(max(cap, 1), np.uint8)
+        val = np.zeros(max(cap, 1), np.uint16)
+        total = lib().kvq_ref_encode(ctypes.byref(c), n, _p(x), cd.D, _p(rec), _p(codes),
+                                     _p(flags), _p(z), _p(norms), _p(off), _p(idx), _p(val), cap)
+        out.update(offsets=off, idx=idx[:min(total, cap)], val=val[:min(total, cap)],
+                   total=int(total))
+    else:
+        lib().kvq_ref_encode(ctypes.byref(c), n, _p(x), cd.D, _p(rec), _p(codes), _p(flags),
+                             _p(z), _p(norms), None, None, None, 0)
+    return out
+
+
+def encode_records(cd: Codec, x_bf16: np.ndarray) -> np.ndarray:
+    """Records only (no per-coordinate outputs): the form the CPU baseline times."""
+    x = np.ascontiguousarray(x_bf16, np.uint16).reshape(-1, cd.D)
+    n = x.shape[0]
+    rec = np.zeros((n, cd.rec_bytes), np.uint8)
+    c = cd._c()
+    lib().kvq_ref_encode(ctypes.byref(c), n, _p(x), cd.D, _p(rec), None, None, None, None,
+                         None, None, None, 0)
+    return rec
+
+
+def decode(cd: Codec, records: np.ndarray, offsets=None, idx=None, val=None) -> np.ndarray:
+    """Decode records ([n, rec_bytes] u8) to f64 [n, D]."""
+    rec = np.ascontiguousarray(records, np.uint8).reshape(-1, cd.rec_bytes)
+    n = rec.shape[0]
+    y = np.zeros((n, cd.D), np.float64)
+    c = cd._c()
+    if offsets is not None:
+        off = np.ascontiguousarray(offsets, np.uint32)
+        ix = np.ascontiguousarray(idx, np.uint8)
+        vv = np.ascontiguousarray(val, np.uint16)
+        lib().kvq_ref_decode(ctypes.byref(c), n, _p(rec), _p(off), _p(ix), _p(vv), len(ix), _p(y))
+    else:
+        lib().kvq_ref_decode(ctypes.byref(c), n, _p(rec), None, None, None, 0, _p(y))
+    return y
+
+
+def score(cd: Codec, q_bf16: np.ndarray, records: np.ndarray) -> np.ndarray:
+    """q . decode(record) for paired rows: q [n, D] bf16 bits, records [n, rec_bytes]."""
+    q = np.ascontiguousarray(q_bf16, np.uint16).reshape(-1, cd.D)
+    rec = np.ascontiguousarray(records, np.uint8).reshape(-1, cd.rec_bytes)
+    assert q.shape[0] == rec.shape[0]
+    out = np.zeros(q.shape[0], np.float64)
+    lib().kvq_ref_score(ctypes.byref(cd._c()), q.shape[0], _p(q), _p(rec), _p(out))
+    return out
+
+
+# --------------------------------------------------------------------------------------------
+# Two-region cache model [arc PR #98]: a dense tail (list of bf16 rows) and a packed region.
+
+
+def retention_floor(window: int, t_new: int, margin: int) -> int:
+    """Rows the dense tail must keep after appending t_new rows: the raw span the next t_new
+    queries can reach (t_new + window - 1), never less than window + margin."""
+    return window + max(t_new - 1, margin)
+
+
+class CacheModel:
+    def __init__(self, cd: Codec, window: int, margin: int = 16):
+        self.cd, self.window, self.margin = cd, window, margin
+        self.tail: list[np.ndarray] = []       # oldest first, each [D] uint16
+        self.packed: list[np.ndarray] = []     # records, oldest first
+
+    def append_evict(self, rows_bf16: np.ndarray) -> int:
+        rows = np.ascontiguousarray(rows_bf16, np.uint16).reshape(-1, self.cd.D)
+        t_new = rows.shape[0]
+        self.tail.extend(list(rows))
+        floor = retention_floor(self.window, t_new, self.margin)
+        chunks = 0
+        while len(self.tail) >= floor + EVICT_CHUNK:
+            block = np.stack(self.tail[:EVICT_CHUNK])
+            self.packed.extend(list(encode_records(self.cd, block)))
+            del self.tail[:EVICT_CHUNK]
+            chunks += 1
+        return chunks
