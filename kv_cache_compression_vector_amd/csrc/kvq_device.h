@@ -1,0 +1,110 @@
+// kvq_device.h — device-side building blocks shared by the gfx950 codec kernels.
+//
+// Lane layout used by every kernel that works on whole vectors: a vector of coded length M is
+// held by LPV = M/8 consecutive lanes, lane c holding the 8 consecutive coordinates 8c..8c+7
+// (one 16-byte bf16 load). A 64-wide wavefront therefore holds VPW = 64/LPV vectors.
+//
+// With that layout, ballot of "bit p of the code of slot j" over the wave gives, for each
+// vector, the M/8 bits of plane positions j*(M/8) + c, c = 0..M/8-1 — the record's bit-plane
+// order pi(i) = (i mod 8)*(M/8) + floor(i/8) — so packing needs only scalar bit moves.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kMaxLevels = 16;
+
+// Codec tables, passed by value as kernel arguments (they live in the kernarg segment).
+struct Tables {
+  float t[15];            // decision thresholds, ascending (2^b - 1 used)
+  float c[16];            // centroids (2^b used)
+  uint32_t sign_words[16];// bit i of the M-bit string = 1 where s_i = -1
+  float T;                // outlier threshold (0 = off)
+  float inv_m;            // 1/M
+  int32_t pad[2];
+};
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// f32 -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Per-lane XOR masks that flip the bf16 sign bits of the 8 coordinates held by chunk c
+// (dword k holds coordinates 2k, 2k+1 in its low / high half).
+template <int M>
+__device__ __forceinline__ void chunk_sign_masks(const Tables& tab, int c, uint32_t (&sm)[4]) {
+  const uint32_t byte = (tab.sign_words[(c >> 2) & 15] >> (8 * (c & 3))) & 0xFFu;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    sm[k] = (((byte >> (2 * k)) & 1u) << 15) | (((byte >> (2 * k + 1)) & 1u) << 31);
+}
+
+// Partner value across lanes: lane ^ mask within the wave.
+__device__ __forceinline__ float lane_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Unnormalised Walsh-Hadamard transform (Sylvester order) of the M coordinates held by the
+// LPV lanes of a vector: coordinate bits 0..2 are the slot index inside the lane, bits 3.. are
+// the lane index c. The element whose butterfly bit is 0 receives a + b, the other a - b.
+template <int LPV>
+__device__ __forceinline__ void fwht_vector(float (&v)[8], int c) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((j & h) == 0) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+#pragma unroll
+  for (int m = 1; m < LPV; m <<= 1) {
+    const bool upper = (c & m) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = lane_xor(v[j], m);
+      v[j] = upper ? (p - v[j]) : (v[j] + p);
+    }
+  }
+}
+
+// Sum over the LPV lanes of one vector (all of them receive the total).
+template <int LPV>
+__device__ __forceinline__ float vector_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < LPV; m <<= 1) x += lane_xor(x, m);
+  return x;
+}
+
+// Integer sum over the LPV lanes of one vector.
+template <int LPV>
+__device__ __forceinline__ uint32_t vector_sum_u32(uint32_t x) {
+#pragma unroll
+  for (int m = 1; m < LPV; m <<= 1) x += (uint32_t)__shfl_xor((int)x, m, 64);
+  return x;
+}
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+// v_writelane_b32 through the LLVM intrinsic (not inline asm), so that the compiler's hazard
+// recognizer inserts the wait state needed after a VALU write of the SGPR it reads.
+extern "C" __device__ int kvq_llvm_writelane_i32(int, int, int) __asm("llvm.amdgcn.writelane.i32");
+
+// Write the wave-uniform value `val` into lane LANE of `old`.
+template <int LANE>
+__device__ __forceinline__ uint32_t write_lane(uint32_t val, uint32_t old) {
+  return (uint32_t)kvq_llvm_writelane_i32((int)__builtin_amdgcn_readfirstlane(val), LANE, (int)old);
+}
+
+// Low `bits` bits set.
+__host__ __device__ constexpr uint64_t low_mask(int bits) {
+  return bits >= 64 ? ~0ull : ((1ull << bits) - 1ull);
+}
+
+}  // namespace kvq

@@ -1,0 +1,452 @@
+// kvq_encode.hip — encode kernels: bf16 rows -> packed records (+ optional outlier lists).
+//
+// Per vector [kakeyaturbo PR #15, commits "M4 Phase A" / "M4 Phase B"; arc PR #98 "What
+// landed"]: n = ||v||, u = H_M (s (.) v), z = u/n, code_i = #{k : z_i > t_k}, b bit-planes + the
+// f32 norm. One wavefront holds 64/(M/8) vectors, 8 coordinates per lane; the rotation is a
+// butterfly network inside the lane and across the vector's lanes; the quantiser's compare
+// masks are wave ballots, which are exactly the record's bit-planes.
+#include "kvq_device.h"
+#include "kvq_kernels.h"
+
+namespace kvq {
+
+// Bit-planes of the codes of one slot (one coordinate per lane) for the whole wave.
+//  SYM: the table is antisymmetric (c_{L-1-k} = -c_k exactly, so the middle threshold is 0 and
+//       the thresholds come in +-pairs). Top plane = (z > 0); the remaining planes come from the
+//       count of positive thresholds below |z|, complemented for negative z. This agrees with
+//       #{k : z > t_k} everywhere except exactly on a threshold.
+//  otherwise: thermometer masks z > t_k and the planes of their count.
+template <int BITS, bool SYM>
+__device__ __forceinline__ void code_planes(float z, const Tables& tab, uint64_t (&pl)[BITS]) {
+  constexpr int L = 1 << BITS;
+  if constexpr (SYM) {
+    const uint64_t pos = ballot64(z > 0.0f);
+    const float az = fabsf(z);
+    uint64_t a[L / 2 + 1];
+    a[0] = ~0ull;
+#pragma unroll
+    for (int k = 1; k < L / 2; ++k) a[k] = ballot64(az > tab.t[L / 2 - 1 + k]);
+    a[L / 2] = 0ull;
+#pragma unroll
+    for (int p = 0; p < BITS - 1; ++p) {
+      uint64_t cp = 0;
+#pragma unroll
+      for (int v = 1; v < L / 2; ++v)
+        if ((v >> p) & 1) cp |= a[v] & ~a[v + 1];
+      pl[p] = ~(cp ^ pos);
+    }
+    pl[BITS - 1] = pos;
+  } else {
+    uint64_t mk[L];
+#pragma unroll
+    for (int k = 0; k < L - 1; ++k) mk[k] = ballot64(z > tab.t[k]);
+    mk[L - 1] = 0ull;
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) {
+      uint64_t cp = 0;
+#pragma unroll
+      for (int v = 1; v < L; ++v)
+        if ((v >> p) & 1) cp |= mk[v - 1] & ~mk[v];
+      pl[p] = cp;
+    }
+  }
+}
+
+// Record word (g, p) of the vector held by lanes [s*LPV, s*LPV + LPV), from the per-slot planes.
+template <int M, int BITS>
+__device__ __forceinline__ uint32_t record_word(const uint64_t (&pl)[8][BITS], int s, int g, int p) {
+  constexpr int LPV = M / 8;
+  if constexpr (LPV >= 32) {
+    const int j = (32 * g) / LPV, c0 = (32 * g) % LPV;
+    return (uint32_t)(pl[j][p] >> (s * LPV + c0));
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 32 / LPV; ++e) {
+      const int j = (32 * g) / LPV + e;
+      w |= (uint32_t)((pl[j][p] >> (s * LPV)) & low_mask(LPV)) << (e * LPV);
+    }
+    return w;
+  }
+}
+
+// Move every record word of the wave's vectors from scalar registers into its storing lane:
+// word w of vector s goes to lane s*LPV + w % LPV of out[w / LPV].
+template <int M, int BITS, int IDX, int NOUT>
+__device__ __forceinline__ void store_words(const uint64_t (&pl)[8][BITS], uint32_t (&out)[NOUT]) {
+  constexpr int LPV = M / 8, VPW = 64 / LPV, NWC = (M / 32) * BITS;
+  if constexpr (IDX < VPW * NWC) {
+    constexpr int s = IDX / NWC, w = IDX % NWC, g = w / BITS, p = w % BITS;
+    out[w / LPV] = write_lane<s * LPV + (w % LPV)>(record_word<M, BITS>(pl, s, g, p), out[w / LPV]);
+    store_words<M, BITS, IDX + 1, NOUT>(pl, out);
+  }
+}
+
+// Quantise the rotated coordinates u[8] (norm n) of every vector of the wave and store the
+// records. Lanes of vectors that do not exist (valid == false) take part in the ballots only.
+template <int M, int BITS, bool SYM>
+__device__ __forceinline__ void quantize_store(const float (&u)[8], float n, bool valid,
+                                               int64_t vec, int sub, int c, const Tables& tab,
+                                               uint8_t* __restrict__ rec) {
+  constexpr int LPV = M / 8, VPW = 64 / LPV, NWC = (M / 32) * BITS, NWT = NWC + 1;
+  constexpr int NOUT = (NWT + LPV - 1) / LPV;
+  const float rn = n > 0.0f ? 1.0f / n : 0.0f;
+  uint64_t pl[8][BITS];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) code_planes<BITS, SYM>(u[j] * rn, tab, pl[j]);
+  uint32_t out[NOUT];
+#pragma unroll
+  for (int r = 0; r < NOUT; ++r) out[r] = 0u;
+  store_words<M, BITS, 0, NOUT>(pl, out);
+  // the norm word: lane (NWC % LPV) of each vector, register NWC / LPV
+  if (c == NWC % LPV) out[NWC / LPV] = __float_as_uint(n);
+  if (valid) {
+    uint32_t* r32 = reinterpret_cast<uint32_t*>(rec + vec * (int64_t)(NWT * 4));
+#pragma unroll
+    for (int r = 0; r < NOUT; ++r) {
+      const int w = r * LPV + c;
+      if (w < NWT) r32[w] = out[r];
+    }
+  }
+}
+
+// Load the 8 coordinates of chunk c of row `vec`, apply the sign diagonal, return f32 values
+// and the lane's partial sum of squares.
+__device__ __forceinline__ float load_signed_chunk(const uint16_t* __restrict__ row, int c,
+                                                   const uint32_t (&sm)[4], bool valid,
+                                                   float (&v)[8]) {
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  if (valid) raw = *reinterpret_cast<const uint4*>(row + 8 * c);
+  const uint32_t w[4] = {raw.x ^ sm[0], raw.y ^ sm[1], raw.z ^ sm[2], raw.w ^ sm[3]};
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = bf16lo_to_f32(w[k]);
+    v[2 * k + 1] = bf16hi_to_f32(w[k]);
+    ss = fmaf(v[2 * k], v[2 * k], ss);
+    ss = fmaf(v[2 * k + 1], v[2 * k + 1], ss);
+  }
+  return ss;
+}
+
+template <int M, int BITS, bool SYM>
+__global__ __launch_bounds__(256) void k_encode(EncodeArgs a) {
+  constexpr int LPV = M / 8, VPW = 64 / LPV;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPV, c = lane % LPV;
+  uint32_t sm[4];
+  chunk_sign_masks<M>(a.tab, c, sm);
+  const int64_t n_iter = (a.n + VPW - 1) / VPW;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < n_iter; it += (int64_t)gridDim.x * 4) {
+    const int64_t vec = it * VPW + sub;
+    const bool valid = vec < a.n;
+    float v[8];
+    const float ss = load_signed_chunk(a.x + vec * a.ld, c, sm, valid, v);
+    const float n = sqrtf(vector_sum<LPV>(ss));
+    fwht_vector<LPV>(v, c);
+    quantize_store<M, BITS, SYM>(v, n, valid, vec, sub, c, a.tab, a.rec);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Outlier side list [kakeyaturbo PR #15, calibrated Lloyd-Max + outlier commit: coordinates
+// with |scaled residual| > T become sparse (index, value) overrides]. CSR order (vectors in
+// input order, ascending coordinate inside a vector) is produced in one pass: each workgroup
+// takes a tile of consecutive vectors by ticket, scans its counts in LDS, and obtains the
+// tile's global offset by a decoupled look-back over the status words of earlier tiles.
+
+constexpr int kOutlierIters = 4;  // wave iterations per tile
+
+template <int M>
+constexpr int outlier_tile() { return 4 * (64 / (M / 8)) * kOutlierIters; }
+
+constexpr uint64_t kFlagAggregate = 1ull << 62;
+constexpr uint64_t kFlagInclusive = 2ull << 62;
+constexpr uint64_t kValueMask = (1ull << 62) - 1;
+constexpr int kMaxSpin = 1 << 22;
+
+// Exclusive prefix of the tiles before `tile`, publishing this tile's aggregate first and its
+// inclusive prefix last. Every earlier tile holds an earlier ticket, so it is running or done
+// and publishes without waiting on later tiles: the wait always ends. A bounded spin records
+// an error instead of waiting forever.
+__device__ uint64_t tile_lookback(uint64_t* status, uint32_t* err, int64_t tile, uint64_t agg) {
+  if (tile == 0) {
+    __hip_atomic_store(&status[0], kFlagInclusive | agg, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    return 0;
+  }
+  __hip_atomic_store(&status[tile], kFlagAggregate | agg, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t prefix = 0;
+  int64_t j = tile - 1;
+  int spin = 0;
+  while (j >= 0) {
+    const uint64_t s = __hip_atomic_load(&status[j], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t flag = s & ~kValueMask;
+    if (flag == 0) {
+      if (++spin > kMaxSpin) {
+        atomicOr(err, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    prefix += s & kValueMask;
+    if (flag == kFlagInclusive) break;
+    --j;
+  }
+  __hip_atomic_store(&status[tile], kFlagInclusive | (prefix + agg), __ATOMIC_RELEASE,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  return prefix;
+}
+
+// Block-wide exclusive scan of one value per thread (256 threads); returns the total too.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* s_wave, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) before += s_wave[w];
+    total += s_wave[w];
+  }
+  return before + incl - x;
+}
+
+template <int M, int BITS, bool SYM>
+__global__ __launch_bounds__(256) void k_encode_ol(EncodeArgs a) {
+  constexpr int LPV = M / 8, VPW = 64 / LPV, U = kOutlierIters, TILE = outlier_tile<M>();
+  static_assert(TILE <= 256, "one count per thread");
+  __shared__ uint32_t s_ticket;
+  __shared__ uint32_t s_cnt[256];
+  __shared__ uint32_t s_wave[4];
+  __shared__ uint64_t s_prefix;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPV, c = lane % LPV;
+  if (threadIdx.x == 0) s_ticket = atomicAdd(a.ws_ticket, 1u);
+  s_cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t tile = s_ticket;
+  const int64_t base = tile * TILE;
+  uint32_t sm[4];
+  chunk_sign_masks<M>(a.tab, c, sm);
+  const float T = a.tab.T;
+  float z[U][8];
+  uint64_t om[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int local = (u * 4 + wave) * VPW + sub;
+    const int64_t vec = base + local;
+    const bool valid = vec < a.n;
+    float v[8];
+    const float ss = load_signed_chunk(a.x + vec * a.ld, c, sm, valid, v);
+    const float n = sqrtf(vector_sum<LPV>(ss));
+    fwht_vector<LPV>(v, c);
+    quantize_store<M, BITS, SYM>(v, n, valid, vec, sub, c, a.tab, a.rec);
+    const float rn = n > 0.0f ? 1.0f / n : 0.0f;
+    uint32_t cl = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      z[u][j] = v[j] * rn;
+      const bool o = valid && fabsf(z[u][j]) > T;
+      om[u][j] = ballot64(o);
+      cl += o ? 1u : 0u;
+    }
+    const uint32_t cv = vector_sum_u32<LPV>(cl);
+    if (c == 0) s_cnt[local] = cv;
+  }
+  __syncthreads();
+  uint32_t agg = 0;
+  const uint32_t excl = block_exclusive_scan(s_cnt[threadIdx.x], s_wave, agg);
+  if (threadIdx.x == 0) s_prefix = tile_lookback(a.ws_status, a.ws_error, tile, agg);
+  __syncthreads();  // every thread has read s_cnt; s_prefix is published
+  const uint64_t prefix = s_prefix;
+  s_cnt[threadIdx.x] = excl;  // reuse: exclusive offset inside the tile
+  if (threadIdx.x < TILE && base + threadIdx.x < a.n)
+    a.ol_off[base + threadIdx.x] = (uint32_t)(prefix + excl);
+  if (threadIdx.x == 0 && base + TILE >= a.n) a.ol_off[a.n] = (uint32_t)(prefix + agg);
+  __syncthreads();
+  const uint64_t vec_lanes = low_mask(LPV) << (sub * LPV);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int local = (u * 4 + wave) * VPW + sub;
+    const int64_t vec = base + local;
+    if (vec >= a.n) continue;
+    uint32_t below = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t mk = om[u][j] & vec_lanes;
+      below += __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+    }
+    uint64_t pos = prefix + s_cnt[local] + below;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (fabsf(z[u][j]) > T) {
+        if (pos < (uint64_t)a.ol_cap) {
+          a.ol_idx[pos] = (uint8_t)(8 * c + j);
+          a.ol_val[pos] = (uint16_t)f32_to_bf16_rne(z[u][j]);
+        }
+        ++pos;
+      }
+    }
+  }
+}
+
+template <int M, int BITS, bool SYM>
+static hipError_t launch_encode_ol_t(const EncodeArgs& a, int64_t n_tiles, hipStream_t st) {
+  if (n_tiles < 1) return hipSuccess;
+  if (n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_encode_ol<M, BITS, SYM>), dim3((unsigned)n_tiles), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int M>
+static hipError_t launch_encode_ol_m(int bits, bool sym, const EncodeArgs& a, int64_t nt,
+                                     hipStream_t st) {
+  switch (bits * 2 + (sym ? 1 : 0)) {
+    case 2: return launch_encode_ol_t<M, 1, false>(a, nt, st);
+    case 3: return launch_encode_ol_t<M, 1, true>(a, nt, st);
+    case 4: return launch_encode_ol_t<M, 2, false>(a, nt, st);
+    case 5: return launch_encode_ol_t<M, 2, true>(a, nt, st);
+    case 6: return launch_encode_ol_t<M, 3, false>(a, nt, st);
+    case 7: return launch_encode_ol_t<M, 3, true>(a, nt, st);
+    case 8: return launch_encode_ol_t<M, 4, false>(a, nt, st);
+    case 9: return launch_encode_ol_t<M, 4, true>(a, nt, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+int64_t encode_outlier_tile_vectors(int m) {
+  switch (m) {
+    case 32: return outlier_tile<32>();
+    case 64: return outlier_tile<64>();
+    case 128: return outlier_tile<128>();
+    case 256: return outlier_tile<256>();
+  }
+  return 64;
+}
+
+hipError_t launch_encode_outliers(int m, int bits, bool sym, const EncodeArgs& a,
+                                  int64_t n_tiles, hipStream_t st) {
+  switch (m) {
+    case 64: return launch_encode_ol_m<64>(bits, sym, a, n_tiles, st);
+    case 128: return launch_encode_ol_m<128>(bits, sym, a, n_tiles, st);
+    case 256: return launch_encode_ol_m<256>(bits, sym, a, n_tiles, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------------------------------
+// Eviction: encode whole chunks of the oldest dense rows of several caches in one launch
+// [arc PR #98, "Eviction is chunked, on purpose"]. Row r of cache k is row r of the
+// concatenation (tail ring from its head, then the new rows). Chunks are 128 rows and a wave
+// never straddles two caches (64/(M/8) divides 128).
+template <int M, int BITS, bool SYM>
+__global__ __launch_bounds__(256) void k_evict(EvictArgs a) {
+  constexpr int LPV = M / 8, VPW = 64 / LPV;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPV, c = lane % LPV;
+  uint32_t sm[4];
+  chunk_sign_masks<M>(a.tab, c, sm);
+  const int64_t n_iter = a.total_rows / VPW;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < n_iter; it += (int64_t)gridDim.x * 4) {
+    const int64_t g0 = it * VPW;
+    int k = 0;
+    while (k + 1 < a.n_caches && g0 >= a.c[k + 1].row_begin) ++k;
+    const EvictCache& ec = a.c[k];
+    const int64_t r = g0 - ec.row_begin + sub;
+    const uint16_t* row = r < ec.tail_len
+                              ? ec.tail + ((ec.tail_head + r) % ec.tail_cap) * a.D
+                              : ec.fresh + (r - ec.tail_len) * a.D;
+    float v[8];
+    const float ss = load_signed_chunk(row, c, sm, true, v);
+    const float n = sqrtf(vector_sum<LPV>(ss));
+    fwht_vector<LPV>(v, c);
+    quantize_store<M, BITS, SYM>(v, n, true, r, sub, c, a.tab, ec.dst);
+  }
+}
+
+template <int M, int BITS, bool SYM>
+static hipError_t launch_evict_t(const EvictArgs& a, hipStream_t st) {
+  constexpr int VPW = 64 / (M / 8);
+  const int64_t n_iter = a.total_rows / VPW;
+  int64_t blocks = (n_iter + 3) / 4;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL((k_evict<M, BITS, SYM>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int M>
+static hipError_t launch_evict_m(int bits, bool sym, const EvictArgs& a, hipStream_t st) {
+  switch (bits * 2 + (sym ? 1 : 0)) {
+    case 2: return launch_evict_t<M, 1, false>(a, st);
+    case 3: return launch_evict_t<M, 1, true>(a, st);
+    case 4: return launch_evict_t<M, 2, false>(a, st);
+    case 5: return launch_evict_t<M, 2, true>(a, st);
+    case 6: return launch_evict_t<M, 3, false>(a, st);
+    case 7: return launch_evict_t<M, 3, true>(a, st);
+    case 8: return launch_evict_t<M, 4, false>(a, st);
+    case 9: return launch_evict_t<M, 4, true>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_evict(int m, int bits, bool sym, const EvictArgs& a, hipStream_t st) {
+  switch (m) {
+    case 64: return launch_evict_m<64>(bits, sym, a, st);
+    case 128: return launch_evict_m<128>(bits, sym, a, st);
+    case 256: return launch_evict_m<256>(bits, sym, a, st);
+    case 512: return launch_evict_m<512>(bits, sym, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers
+
+template <int M, int BITS, bool SYM>
+static hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t st) {
+  constexpr int VPW = 64 / (M / 8);
+  const int64_t n_iter = (a.n + VPW - 1) / VPW;
+  int64_t blocks = (n_iter + 3) / 4;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL((k_encode<M, BITS, SYM>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int M>
+static hipError_t launch_encode_m(int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
+  switch (bits * 2 + (sym ? 1 : 0)) {
+    case 2: return launch_encode_t<M, 1, false>(a, st);
+    case 3: return launch_encode_t<M, 1, true>(a, st);
+    case 4: return launch_encode_t<M, 2, false>(a, st);
+    case 5: return launch_encode_t<M, 2, true>(a, st);
+    case 6: return launch_encode_t<M, 3, false>(a, st);
+    case 7: return launch_encode_t<M, 3, true>(a, st);
+    case 8: return launch_encode_t<M, 4, false>(a, st);
+    case 9: return launch_encode_t<M, 4, true>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_encode(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
+  switch (m) {
+    case 32: return launch_encode_m<32>(bits, sym, a, st);
+    case 64: return launch_encode_m<64>(bits, sym, a, st);
+    case 128: return launch_encode_m<128>(bits, sym, a, st);
+    case 256: return launch_encode_m<256>(bits, sym, a, st);
+    case 512: return launch_encode_m<512>(bits, sym, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

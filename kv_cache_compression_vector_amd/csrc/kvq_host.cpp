@@ -1,0 +1,515 @@
+// kvq_host.cpp — the C ABI: argument validation, codec tables, dispatch to the gfx950 kernels.
+//
+// The library keeps no device state and allocates no device memory: tables travel as kernel
+// arguments, scratch comes from the caller. Every error is reported before anything is
+// enqueued, as a typed status plus a thread-local message naming the argument and its value
+// (refusal instead of silent fallback: arc PR #98, "Two refusals rather than fallbacks";
+// kakeyaturbo PR #15, "M2" commit: validate at the boundary).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/kvq.h"
+#include "kvq_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kvq_status ok() {
+  g_last_error.clear();
+  return KVQ_OK;
+}
+
+kvq_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(KVQ_E_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Gaussian Lloyd-Max tables. Lloyd's optimality conditions for N(0,1): boundaries are midpoints
+// of adjacent centroids and each centroid is the mean of N(0,1) over its cell,
+// (pdf(a) - pdf(b)) / (cdf(b) - cdf(a)); iterated to a fixed point (one table per bit width:
+// larql PR #196 turbo-quant commit; kakeyaturbo PR #15 "M4 Phase A" centroids_gaussian).
+
+double normal_pdf(double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) * 0.3989422804014327; }
+
+// Probability of (a, b) under N(0,1), taken from whichever tail keeps it accurate.
+double normal_cell_mass(double a, double b) {
+  const double r2 = 0.7071067811865476;
+  if (a >= 0.0) return 0.5 * (std::erfc(a * r2) - std::erfc(b * r2));
+  if (b <= 0.0) return 0.5 * (std::erfc(-b * r2) - std::erfc(-a * r2));
+  return 1.0 - 0.5 * std::erfc(b * r2) - 0.5 * std::erfc(-a * r2);
+}
+
+struct GaussTable {
+  bool ready = false;
+  float c[16];
+};
+
+GaussTable g_gauss[5];
+std::mutex g_gauss_mu;
+
+const float* gaussian_centroids(int bits) {
+  std::lock_guard<std::mutex> lk(g_gauss_mu);
+  GaussTable& gt = g_gauss[bits];
+  if (gt.ready) return gt.c;
+  const int L = 1 << bits;
+  double c[16], edge[17];
+  for (int k = 0; k < L; ++k) c[k] = 6.0 * (k + 0.5) / L - 3.0;
+  for (int iter = 0; iter < 200000; ++iter) {
+    edge[0] = -INFINITY;
+    edge[L] = INFINITY;
+    for (int k = 1; k < L; ++k) edge[k] = 0.5 * (c[k - 1] + c[k]);
+    double delta = 0.0;
+    for (int k = 0; k < L; ++k) {
+      const double nc = (normal_pdf(edge[k]) - normal_pdf(edge[k + 1])) /
+                        normal_cell_mass(edge[k], edge[k + 1]);
+      delta = std::fmax(delta, std::fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (delta < 1e-14) break;
+  }
+  for (int k = 0; k < L / 2; ++k) {  // exact antisymmetry
+    const double h = 0.5 * (c[L - 1 - k] - c[k]);
+    c[k] = -h;
+    c[L - 1 - k] = h;
+  }
+  for (int k = 0; k < L; ++k) gt.c[k] = (float)c[k];
+  gt.ready = true;
+  return gt.c;
+}
+
+// Sign diagonal: SplitMix64 (Steele, Lea & Flood 2014) — state += golden-ratio increment, the
+// output mix applied to the state; s_i = -1 when the top bit of output i is set.
+uint64_t splitmix64_next(uint64_t& state) {
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Codec validation
+
+struct Resolved {
+  int D, m, bits, L;
+  bool pca, sym, outliers;
+  kvq::Tables tab;
+};
+
+bool is_pow2_in(uint32_t v, uint32_t lo, uint32_t hi) {
+  return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+kvq_status resolve_codec(const kvq_codec* cd, Resolved& r) {
+  if (!cd) return fail(KVQ_E_NULL, "codec is NULL");
+  if (!is_pow2_in(cd->head_dim, 64, 512))
+    return fail(KVQ_E_DIM, "head_dim=%u not supported (64, 128, 256, 512)", cd->head_dim);
+  if (cd->bits < 1 || cd->bits > 4) return fail(KVQ_E_BITS, "bits=%u outside 1..4", cd->bits);
+  if (cd->flags != 0) return fail(KVQ_E_ARG, "flags=%u must be 0", cd->flags);
+  if (cd->reserved0 != 0) return fail(KVQ_E_ARG, "reserved0=%u must be 0", cd->reserved0);
+  r.D = (int)cd->head_dim;
+  r.bits = (int)cd->bits;
+  r.L = 1 << r.bits;
+  r.pca = cd->proj_rank != 0;
+  if (r.pca) {
+    if (!is_pow2_in(cd->proj_rank, 32, 256) || cd->proj_rank >= cd->head_dim)
+      return fail(KVQ_E_DIM, "proj_rank=%u not supported (32..256, power of two, < head_dim=%u)",
+                  cd->proj_rank, cd->head_dim);
+    if (!cd->basis_dev) return fail(KVQ_E_NULL, "proj_rank=%u needs basis_dev", cd->proj_rank);
+  }
+  r.m = r.pca ? (int)cd->proj_rank : r.D;
+  if (!(cd->outlier_T >= 0.0f) || std::isinf(cd->outlier_T))
+    return fail(KVQ_E_OUTLIER, "outlier_T=%g must be finite and >= 0", (double)cd->outlier_T);
+  r.outliers = cd->outlier_T > 0.0f;
+  if (r.outliers && r.m > 256)
+    return fail(KVQ_E_OUTLIER, "outlier lists need coded length <= 256 (u8 index), got m=%d", r.m);
+  std::memset(&r.tab, 0, sizeof(r.tab));
+  const float* c = cd->centroids_host ? cd->centroids_host : gaussian_centroids(r.bits);
+  for (int k = 0; k < r.L; ++k) {
+    if (!std::isfinite(c[k]))
+      return fail(KVQ_E_CENTROIDS, "centroids[%d]=%g is not finite", k, (double)c[k]);
+    if (k > 0 && !(c[k] > c[k - 1]))
+      return fail(KVQ_E_CENTROIDS, "centroids not strictly ascending at %d (%g <= %g)", k,
+                  (double)c[k], (double)c[k - 1]);
+    r.tab.c[k] = c[k];
+  }
+  for (int k = 0; k + 1 < r.L; ++k)
+    r.tab.t[k] = (float)(0.5 * ((double)c[k] + (double)c[k + 1]));
+  r.sym = true;
+  for (int k = 0; k < r.L; ++k)
+    if (c[r.L - 1 - k] != -c[k]) r.sym = false;
+  uint64_t st = cd->seed;
+  for (int i = 0; i < r.m; ++i)
+    if (splitmix64_next(st) >> 63) r.tab.sign_words[i >> 5] |= 1u << (i & 31);
+  r.tab.T = cd->outlier_T;
+  r.tab.inv_m = 1.0f / (float)r.m;
+  return ok();
+}
+
+size_t record_bytes(const Resolved& r) { return (size_t)r.m * r.bits / 8 + 4; }
+
+// Fingerprint of everything that changes the bytes a cache holds.
+uint64_t codec_key(const kvq_codec* cd, const Resolved& r) {
+  uint64_t h = 0xcbf29ce484222325ull;
+  auto mix = [&](const void* p, size_t n) {
+    const unsigned char* b = static_cast<const unsigned char*>(p);
+    for (size_t i = 0; i < n; ++i) h = (h ^ b[i]) * 0x100000001b3ull;
+  };
+  mix(&cd->head_dim, 4);
+  mix(&cd->bits, 4);
+  mix(&cd->proj_rank, 4);
+  mix(&cd->seed, 8);
+  mix(&cd->outlier_T, 4);
+  mix(r.tab.c, sizeof(float) * r.L);
+  return h;
+}
+
+constexpr uint64_t kCacheMagic = 0x4b56514341434845ull;  // "KVQCACHE"
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+size_t kvq_record_bytes(const kvq_codec* codec) {
+  Resolved r;
+  if (resolve_codec(codec, r) != KVQ_OK) return 0;
+  return record_bytes(r);
+}
+
+size_t kvq_encode_workspace_bytes(const kvq_codec* codec, int64_t n) {
+  Resolved r;
+  if (resolve_codec(codec, r) != KVQ_OK || n < 0) return 0;
+  if (!r.outliers) return 0;
+  const int64_t tile = kvq::encode_outlier_tile_vectors(r.m);
+  const int64_t tiles = (n + tile - 1) / tile;
+  return (size_t)(16 + 8 * tiles);
+}
+
+kvq_status kvq_codec_tables(const kvq_codec* codec, float* centroids_host,
+                            float* thresholds_host, int8_t* signs_host) {
+  Resolved r;
+  kvq_status st = resolve_codec(codec, r);
+  if (st != KVQ_OK) return st;
+  if (centroids_host) std::memcpy(centroids_host, r.tab.c, sizeof(float) * r.L);
+  if (thresholds_host) std::memcpy(thresholds_host, r.tab.t, sizeof(float) * (r.L - 1));
+  if (signs_host)
+    for (int i = 0; i < r.m; ++i)
+      signs_host[i] = ((r.tab.sign_words[i >> 5] >> (i & 31)) & 1u) ? (int8_t)-1 : (int8_t)1;
+  return ok();
+}
+
+kvq_status kvq_encode(const kvq_codec* codec, const void* x_dev, int64_t n, int64_t ld_x,
+                      void* records_dev, const kvq_outliers* ol, int64_t* ol_total_host,
+                      void* stream) {
+  Resolved r;
+  kvq_status st = resolve_codec(codec, r);
+  if (st != KVQ_OK) return st;
+  if (n < 0) return fail(KVQ_E_ARG, "n=%lld is negative", (long long)n);
+  if (ld_x < r.D) return fail(KVQ_E_STRIDE, "ld_x=%lld < head_dim=%d", (long long)ld_x, r.D);
+  if (ld_x % 8) return fail(KVQ_E_STRIDE, "ld_x=%lld is not a multiple of 8 elements", (long long)ld_x);
+  if (n > 0 && (!x_dev || !records_dev)) return fail(KVQ_E_NULL, "x_dev or records_dev is NULL");
+  if (n > 0 && !aligned(x_dev, 16)) return fail(KVQ_E_STRIDE, "x_dev is not 16-byte aligned");
+  if (n > 0 && !aligned(records_dev, 4)) return fail(KVQ_E_STRIDE, "records_dev is not 4-byte aligned");
+  if (r.outliers) {
+    if (!ol) return fail(KVQ_E_OUTLIER, "outlier_T=%g > 0 needs an outlier list", (double)codec->outlier_T);
+    if (!ol->offsets_dev || (ol->capacity > 0 && (!ol->idx_dev || !ol->val_dev)))
+      return fail(KVQ_E_NULL, "outlier list buffers are NULL");
+    if (ol->capacity < 0) return fail(KVQ_E_OUTLIER, "outlier capacity=%lld < 0", (long long)ol->capacity);
+    const size_t need = kvq_encode_workspace_bytes(codec, n);
+    if (ol->workspace_bytes < (int64_t)need || !ol->workspace_dev)
+      return fail(KVQ_E_CAPACITY, "outlier workspace %lld bytes < %zu needed",
+                  (long long)ol->workspace_bytes, need);
+    if (!aligned(ol->workspace_dev, 16)) return fail(KVQ_E_STRIDE, "workspace_dev is not 16-byte aligned");
+  } else if (ol) {
+    return fail(KVQ_E_OUTLIER, "outlier list given but outlier_T == 0");
+  }
+  if (ol_total_host && !r.outliers)
+    return fail(KVQ_E_OUTLIER, "ol_total_host given but outlier_T == 0");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kvq::EncodeArgs a{};
+  a.tab = r.tab;
+  a.x = static_cast<const uint16_t*>(x_dev);
+  a.ld = ld_x;
+  a.n = n;
+  a.rec = static_cast<uint8_t*>(records_dev);
+  if (r.pca) {
+    a.basis = codec->basis_dev;
+    a.mean = codec->mean_dev;
+  }
+  if (!r.outliers) {
+    if (n == 0) return ok();
+    if (r.pca) return from_hip(kvq::launch_encode_pca(r.D, r.m, r.bits, r.sym, false, a, 0, s), "encode_pca");
+    return from_hip(kvq::launch_encode(r.m, r.bits, r.sym, a, s), "encode");
+  }
+  // outlier path: tiles + decoupled look-back over a caller workspace
+  const int64_t tile = kvq::encode_outlier_tile_vectors(r.m);
+  const int64_t n_tiles = (n + tile - 1) / tile;
+  uint32_t* ws = static_cast<uint32_t*>(ol->workspace_dev);
+  a.ws_ticket = ws;
+  a.ws_error = ws + 1;
+  a.ws_status = reinterpret_cast<uint64_t*>(ws + 4);
+  a.ol_off = ol->offsets_dev;
+  a.ol_idx = ol->idx_dev;
+  a.ol_val = ol->val_dev;
+  a.ol_cap = ol->capacity;
+  hipError_t e = kvq::launch_clear_u32(ws, 4 + 2 * n_tiles, s);
+  if (e != hipSuccess) return from_hip(e, "encode workspace clear");
+  if (n == 0) {
+    e = hipMemcpyAsync(ol->offsets_dev, ws, sizeof(uint32_t), hipMemcpyDeviceToDevice, s);
+  } else if (r.pca) {
+    e = kvq::launch_encode_pca(r.D, r.m, r.bits, r.sym, true, a, n_tiles, s);
+  } else {
+    e = kvq::launch_encode_outliers(r.m, r.bits, r.sym, a, n_tiles, s);
+  }
+  if (e != hipSuccess) return from_hip(e, "encode_outliers");
+  if (ol_total_host) {
+    uint32_t tot = 0, err = 0;
+    e = hipMemcpyAsync(&tot, ol->offsets_dev + n, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(&err, ws + 1, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return from_hip(e, "encode outlier total");
+    *ol_total_host = tot;
+    if (err) return fail(KVQ_E_DEVICE, "outlier prefix scan gave up waiting (error word %u)", err);
+    if ((int64_t)tot > ol->capacity)
+      return fail(KVQ_E_CAPACITY, "outlier count %u exceeds capacity %lld", tot, (long long)ol->capacity);
+  }
+  return ok();
+}
+
+kvq_status kvq_decode(const kvq_codec* codec, const void* records_dev, int64_t n,
+                      const kvq_outliers* ol, void* y_dev, kvq_dtype y_dtype, int64_t ld_y,
+                      void* stream) {
+  Resolved r;
+  kvq_status st = resolve_codec(codec, r);
+  if (st != KVQ_OK) return st;
+  if (n < 0) return fail(KVQ_E_ARG, "n=%lld is negative", (long long)n);
+  if (y_dtype != KVQ_F32 && y_dtype != KVQ_BF16) return fail(KVQ_E_ARG, "y_dtype=%d unknown", (int)y_dtype);
+  if (ld_y < r.D) return fail(KVQ_E_STRIDE, "ld_y=%lld < head_dim=%d", (long long)ld_y, r.D);
+  if (ld_y % 8) return fail(KVQ_E_STRIDE, "ld_y=%lld is not a multiple of 8 elements", (long long)ld_y);
+  if (n > 0 && (!records_dev || !y_dev)) return fail(KVQ_E_NULL, "records_dev or y_dev is NULL");
+  if (n > 0 && !aligned(y_dev, 16)) return fail(KVQ_E_STRIDE, "y_dev is not 16-byte aligned");
+  if (n > 0 && !aligned(records_dev, 4)) return fail(KVQ_E_STRIDE, "records_dev is not 4-byte aligned");
+  if (ol && !r.outliers) return fail(KVQ_E_OUTLIER, "outlier list given but outlier_T == 0");
+  if (ol && (!ol->offsets_dev || (ol->capacity > 0 && (!ol->idx_dev || !ol->val_dev))))
+    return fail(KVQ_E_NULL, "outlier list buffers are NULL");
+  if (n == 0) return ok();
+  kvq::DecodeArgs a{};
+  a.tab = r.tab;
+  a.rec = static_cast<const uint8_t*>(records_dev);
+  a.n = n;
+  if (ol) {
+    a.ol_off = ol->offsets_dev;
+    a.ol_idx = ol->idx_dev;
+    a.ol_val = ol->val_dev;
+    a.ol_cap = ol->capacity;
+  }
+  a.y = y_dev;
+  a.ld = ld_y;
+  a.basis = codec->basis_dev;
+  a.mean = codec->mean_dev;
+  return from_hip(kvq::launch_decode(r.D, r.m, r.bits, ol != nullptr, y_dtype == KVQ_BF16, a,
+                                     static_cast<hipStream_t>(stream)),
+                  "decode");
+}
+
+kvq_status kvq_score_packed(const kvq_codec* codec, const void* q_dev, int32_t B, int32_t Hq,
+                            int64_t q_sb, int64_t q_sh, const void* records_dev, int32_t Hkv,
+                            int64_t T, int64_t rec_sb, int64_t rec_sh, float* scores_dev,
+                            int64_t s_sb, int64_t s_sh, void* stream) {
+  Resolved r;
+  kvq_status st = resolve_codec(codec, r);
+  if (st != KVQ_OK) return st;
+  if (r.outliers) return fail(KVQ_E_OUTLIER, "score reads codes and norms only: outlier_T must be 0");
+  if (B < 0 || Hq < 0 || Hkv < 0 || T < 0) return fail(KVQ_E_ARG, "negative size (B=%d Hq=%d Hkv=%d T=%lld)", B, Hq, Hkv, (long long)T);
+  if (B == 0 || Hq == 0 || T == 0) return ok();
+  if (Hkv == 0 || Hq % Hkv) return fail(KVQ_E_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int group = Hq / Hkv;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(KVQ_E_ARG, "Hq/Hkv=%d not supported (1, 2, 4, 8)", group);
+  if (B * Hkv > 65535) return fail(KVQ_E_ARG, "B*Hkv=%d exceeds 65535", B * Hkv);
+  if (!q_dev || !records_dev || !scores_dev) return fail(KVQ_E_NULL, "q_dev, records_dev or scores_dev is NULL");
+  if (!aligned(q_dev, 16) || q_sb % 8 || q_sh % 8)
+    return fail(KVQ_E_STRIDE, "q rows must be 16-byte aligned (q_sb=%lld, q_sh=%lld elements)", (long long)q_sb, (long long)q_sh);
+  if (!aligned(records_dev, 4)) return fail(KVQ_E_STRIDE, "records_dev is not 4-byte aligned");
+  if (!aligned(scores_dev, 4)) return fail(KVQ_E_STRIDE, "scores_dev is not 4-byte aligned");
+  if (q_sb < 0 || q_sh < 0 || rec_sb < 0 || rec_sh < 0 || s_sb < 0 || s_sh < 0)
+    return fail(KVQ_E_STRIDE, "negative stride");
+  kvq::ScoreArgs a{};
+  a.tab = r.tab;
+  a.q = static_cast<const uint16_t*>(q_dev);
+  a.q_sb = q_sb;
+  a.q_sh = q_sh;
+  a.rec = static_cast<const uint8_t*>(records_dev);
+  a.rec_sb = rec_sb;
+  a.rec_sh = rec_sh;
+  a.T = T;
+  a.s = scores_dev;
+  a.s_sb = s_sb;
+  a.s_sh = s_sh;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.basis = codec->basis_dev;
+  a.mean = codec->mean_dev;
+  return from_hip(kvq::launch_score(r.D, r.m, r.bits, group, a, static_cast<hipStream_t>(stream)),
+                  "score_packed");
+}
+
+kvq_status kvq_cache_init(const kvq_codec* codec, kvq_cache* cache, void* packed_dev,
+                          int64_t packed_cap, void* tail_dev, int64_t tail_cap, int32_t window,
+                          int32_t margin) {
+  Resolved r;
+  kvq_status st = resolve_codec(codec, r);
+  if (st != KVQ_OK) return st;
+  if (!cache) return fail(KVQ_E_NULL, "cache is NULL");
+  if (r.outliers || r.pca)
+    return fail(KVQ_E_ARG, "caches hold Hadamard records without outlier lists (proj_rank=%u, outlier_T=%g)",
+                codec->proj_rank, (double)codec->outlier_T);
+  if (packed_cap < 0 || tail_cap <= 0 || window < 0 || margin < 0)
+    return fail(KVQ_E_ARG, "packed_cap=%lld tail_cap=%lld window=%d margin=%d", (long long)packed_cap,
+                (long long)tail_cap, window, margin);
+  if (!tail_dev || (packed_cap > 0 && !packed_dev)) return fail(KVQ_E_NULL, "cache buffers are NULL");
+  if (!aligned(tail_dev, 16)) return fail(KVQ_E_STRIDE, "tail_dev is not 16-byte aligned");
+  if (packed_dev && !aligned(packed_dev, 4)) return fail(KVQ_E_STRIDE, "packed_dev is not 4-byte aligned");
+  std::memset(cache, 0, sizeof(*cache));
+  cache->magic = kCacheMagic;
+  cache->codec_key = codec_key(codec, r);
+  cache->packed_dev = packed_dev;
+  cache->packed_cap = packed_cap;
+  cache->tail_dev = tail_dev;
+  cache->tail_cap = tail_cap;
+  cache->window = window;
+  cache->margin = margin;
+  return ok();
+}
+
+kvq_status kvq_append_evict_chunk(const kvq_codec* codec, kvq_cache* const* caches,
+                                  int32_t n_caches, const void* const* new_rows_dev,
+                                  int64_t t_new, void* stream, int64_t* evicted_host) {
+  Resolved r;
+  kvq_status st = resolve_codec(codec, r);
+  if (st != KVQ_OK) return st;
+  if (n_caches < 0 || t_new < 0) return fail(KVQ_E_ARG, "n_caches=%d t_new=%lld", n_caches, (long long)t_new);
+  if (n_caches == 0) return ok();
+  if (!caches) return fail(KVQ_E_NULL, "caches is NULL");
+  if (t_new > 0 && !new_rows_dev) return fail(KVQ_E_NULL, "new_rows_dev is NULL with t_new=%lld", (long long)t_new);
+  const uint64_t key = codec_key(codec, r);
+  const int64_t rb = (int64_t)record_bytes(r);
+  const int64_t C = KVQ_EVICT_CHUNK;
+  // Plan every cache first; nothing is changed or launched unless all of them are valid.
+  struct Plan { int64_t k, keep_from; };
+  Plan* plan = new Plan[n_caches];
+  for (int i = 0; i < n_caches; ++i) {
+    const kvq_cache* c = caches[i];
+    if (!c) { delete[] plan; return fail(KVQ_E_NULL, "caches[%d] is NULL", i); }
+    if (c->magic != kCacheMagic) { delete[] plan; return fail(KVQ_E_CACHE, "caches[%d] was not built by kvq_cache_init", i); }
+    if (c->codec_key != key) { delete[] plan; return fail(KVQ_E_CACHE, "caches[%d] was built for another codec", i); }
+    if (t_new > 0 && !new_rows_dev[i]) { delete[] plan; return fail(KVQ_E_NULL, "new_rows_dev[%d] is NULL", i); }
+    if (t_new > 0 && !aligned(new_rows_dev[i], 16)) { delete[] plan; return fail(KVQ_E_STRIDE, "new_rows_dev[%d] is not 16-byte aligned", i); }
+    const int64_t floor = (int64_t)c->window + (t_new - 1 > c->margin ? t_new - 1 : (int64_t)c->margin);
+    const int64_t total = c->tail_len + t_new;
+    const int64_t k = total >= floor ? (total - floor) / C : 0;
+    if (c->packed_len + k * C > c->packed_cap) {
+      delete[] plan;
+      return fail(KVQ_E_CAPACITY, "caches[%d]: packed region full (%lld + %lld > %lld records)", i,
+                  (long long)c->packed_len, (long long)(k * C), (long long)c->packed_cap);
+    }
+    if (total - k * C > c->tail_cap) {
+      delete[] plan;
+      return fail(KVQ_E_CAPACITY, "caches[%d]: dense tail needs %lld rows > tail_cap %lld", i,
+                  (long long)(total - k * C), (long long)c->tail_cap);
+    }
+    plan[i].k = k;
+    plan[i].keep_from = k * C > c->tail_len ? k * C - c->tail_len : 0;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  // 1) encode the evicted chunks (up to kMaxEvictCaches caches per launch)
+  for (int i0 = 0; i0 < n_caches && e == hipSuccess; i0 += kvq::kMaxEvictCaches) {
+    kvq::EvictArgs a{};
+    a.tab = r.tab;
+    a.D = r.D;
+    int64_t rows = 0;
+    int nc = 0;
+    for (int i = i0; i < n_caches && i < i0 + kvq::kMaxEvictCaches; ++i) {
+      if (plan[i].k == 0) continue;
+      const kvq_cache* c = caches[i];
+      kvq::EvictCache& ec = a.c[nc++];
+      ec.tail = static_cast<const uint16_t*>(c->tail_dev);
+      ec.fresh = t_new > 0 ? static_cast<const uint16_t*>(new_rows_dev[i]) : nullptr;
+      ec.dst = static_cast<uint8_t*>(c->packed_dev) + c->packed_len * rb;
+      ec.tail_cap = c->tail_cap;
+      ec.tail_head = c->tail_head;
+      ec.tail_len = c->tail_len;
+      ec.rows = plan[i].k * C;
+      ec.row_begin = rows;
+      rows += ec.rows;
+    }
+    a.n_caches = nc;
+    a.total_rows = rows;
+    if (rows > 0) e = kvq::launch_evict(r.m, r.bits, r.sym, a, s);
+  }
+  // 2) append the surviving new rows to the tail rings
+  for (int i0 = 0; i0 < n_caches && e == hipSuccess && t_new > 0; i0 += kvq::kMaxEvictCaches) {
+    kvq::TailCopyArgs a{};
+    a.D = r.D;
+    int64_t rows = 0;
+    int nc = 0;
+    for (int i = i0; i < n_caches && i < i0 + kvq::kMaxEvictCaches; ++i) {
+      const int64_t keep = t_new - plan[i].keep_from;
+      if (keep <= 0) continue;
+      const kvq_cache* c = caches[i];
+      kvq::TailCopyCache& tc = a.c[nc++];
+      tc.src = static_cast<const uint16_t*>(new_rows_dev[i]) + plan[i].keep_from * r.D;
+      tc.ring = static_cast<uint16_t*>(c->tail_dev);
+      tc.cap = c->tail_cap;
+      tc.first_slot = (c->tail_head + c->tail_len + plan[i].keep_from) % c->tail_cap;
+      tc.rows = keep;
+      tc.row_begin = rows;
+      rows += keep;
+    }
+    a.n_caches = nc;
+    a.total_rows = rows;
+    if (rows > 0) e = kvq::launch_tail_copy(a, s);
+  }
+  if (e != hipSuccess) {
+    delete[] plan;
+    return from_hip(e, "append_evict_chunk");
+  }
+  for (int i = 0; i < n_caches; ++i) {
+    kvq_cache* c = caches[i];
+    const int64_t ev = plan[i].k * C;
+    c->packed_len += ev;
+    c->tail_head = (c->tail_head + ev) % c->tail_cap;
+    c->tail_len = c->tail_len + t_new - ev;
+    if (evicted_host) evicted_host[i] = plan[i].k;
+  }
+  delete[] plan;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// kvq_kernels.h — argument blocks and launchers of the gfx950 kernels (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+struct EncodeArgs {
+  Tables tab;
+  const uint16_t* x;        // bf16 rows
+  int64_t ld;               // elements between rows
+  int64_t n;                // vectors
+  uint8_t* rec;             // records
+  // outlier side list (outlier kernels only)
+  uint32_t* ol_off;
+  uint8_t* ol_idx;
+  uint16_t* ol_val;
+  int64_t ol_cap;
+  uint64_t* ws_status;      // one status word per tile
+  uint32_t* ws_ticket;      // tile ticket counter
+  uint32_t* ws_error;       // set when a look-back wait gave up
+  // PCA projection (PCA kernels only)
+  const uint16_t* basis;    // bf16 [D][r]
+  const float* mean;        // f32 [D] or nullptr
+};
+
+struct DecodeArgs {
+  Tables tab;
+  const uint8_t* rec;
+  int64_t n;
+  const uint32_t* ol_off;   // nullptr = no side list
+  const uint8_t* ol_idx;
+  const uint16_t* ol_val;
+  int64_t ol_cap;
+  void* y;
+  int64_t ld;
+  const uint16_t* basis;    // PCA only
+  const float* mean;
+};
+
+struct ScoreArgs {
+  Tables tab;
+  const uint16_t* q;
+  int64_t q_sb, q_sh;
+  const uint8_t* rec;
+  int64_t rec_sb, rec_sh;   // in records
+  int64_t T;
+  float* s;
+  int64_t s_sb, s_sh;
+  int32_t B, Hq, Hkv, pad;
+  const uint16_t* basis;    // PCA only
+  const float* mean;
+};
+
+// One cache of an append/evict launch: rows [0, rows) of the concatenation (tail ring, new rows)
+// are encoded into dst.
+struct EvictCache {
+  const uint16_t* tail;     // ring base
+  const uint16_t* fresh;    // new rows
+  uint8_t* dst;             // first record to write
+  int64_t tail_cap, tail_head, tail_len;
+  int64_t rows;             // multiple of 128
+  int64_t row_begin;        // prefix over caches
+};
+
+constexpr int kMaxEvictCaches = 32;
+
+struct EvictArgs {
+  Tables tab;
+  int32_t n_caches, pad;
+  int64_t total_rows;
+  int64_t D;
+  EvictCache c[kMaxEvictCaches];
+};
+
+struct TailCopyCache {
+  const uint16_t* src;      // first new row to keep
+  uint16_t* ring;
+  int64_t cap, first_slot;  // ring slot of src row 0
+  int64_t rows;
+  int64_t row_begin;
+};
+
+struct TailCopyArgs {
+  int32_t n_caches, pad;
+  int64_t total_rows;
+  int64_t D;
+  TailCopyCache c[kMaxEvictCaches];
+};
+
+hipError_t launch_encode(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
+hipError_t launch_encode_outliers(int m, int bits, bool sym, const EncodeArgs& a,
+                                  int64_t n_tiles, hipStream_t st);
+int64_t encode_outlier_tile_vectors(int m);
+hipError_t launch_encode_pca(int D, int r, int bits, bool sym, bool outliers,
+                             const EncodeArgs& a, int64_t n_tiles, hipStream_t st);
+hipError_t launch_decode(int D, int m, int bits, bool outliers, bool bf16_out,
+                         const DecodeArgs& a, hipStream_t st);
+hipError_t launch_score(int D, int m, int bits, int group, const ScoreArgs& a, hipStream_t st);
+hipError_t launch_evict(int m, int bits, bool sym, const EvictArgs& a, hipStream_t st);
+hipError_t launch_tail_copy(const TailCopyArgs& a, hipStream_t st);
+hipError_t launch_clear_u32(uint32_t* p, int64_t n_words, hipStream_t st);
+
+}  // namespace kvq

@@ -1,0 +1,46 @@
+// kvq_misc.hip — small helper kernels: tail-ring append and word clearing.
+#include "kvq_device.h"
+#include "kvq_kernels.h"
+
+namespace kvq {
+
+// Copy new rows into the dense tail rings of several caches (16 bytes per lane).
+__global__ __launch_bounds__(256) void k_tail_copy(TailCopyArgs a) {
+  const int64_t per_row = a.D / 8;  // uint4 per row
+  const int64_t total = a.total_rows * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t g = i / per_row, q = i % per_row;
+    int k = 0;
+    while (k + 1 < a.n_caches && g >= a.c[k + 1].row_begin) ++k;
+    const TailCopyCache& tc = a.c[k];
+    const int64_t r = g - tc.row_begin;
+    const int64_t slot = (tc.first_slot + r) % tc.cap;
+    const uint4 v = reinterpret_cast<const uint4*>(tc.src + r * a.D)[q];
+    reinterpret_cast<uint4*>(tc.ring + slot * a.D)[q] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_clear_u32(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
+hipError_t launch_tail_copy(const TailCopyArgs& a, hipStream_t st) {
+  const int64_t total = a.total_rows * (a.D / 8);
+  if (total <= 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(k_tail_copy, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_u32(uint32_t* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_clear_u32, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,247 @@
+"""ctypes binding of libkvq.so. Argument marshalling only: PyTorch supplies device memory and
+the current HIP stream; every step of the codec runs in the library's kernels.
+
+Functions mirror include/kvq.h: encode, decode, score_packed, cache_init, append_evict_chunk.
+The library must have been built (kv_cache_compression_vector_amd/build.py); importing a
+missing library raises — there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK = 0
+STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_E_NULL", 2: "KVQ_E_DIM", 3: "KVQ_E_BITS",
+                4: "KVQ_E_CENTROIDS", 5: "KVQ_E_STRIDE", 6: "KVQ_E_OUTLIER",
+                7: "KVQ_E_CAPACITY", 8: "KVQ_E_CACHE", 9: "KVQ_E_DEVICE", 10: "KVQ_E_ARG"}
+EVICT_CHUNK = 128
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+
+
+class _Codec(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_uint32), ("bits", ctypes.c_uint32),
+                ("proj_rank", ctypes.c_uint32), ("flags", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64), ("outlier_T", ctypes.c_float),
+                ("reserved0", ctypes.c_uint32), ("centroids_host", ctypes.c_void_p),
+                ("basis_dev", ctypes.c_void_p), ("mean_dev", ctypes.c_void_p)]
+
+
+class _Outliers(ctypes.Structure):
+    _fields_ = [("offsets_dev", ctypes.c_void_p), ("idx_dev", ctypes.c_void_p),
+                ("val_dev", ctypes.c_void_p), ("capacity", ctypes.c_int64),
+                ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint64), ("codec_key", ctypes.c_uint64),
+                ("packed_dev", ctypes.c_void_p), ("packed_len", ctypes.c_int64),
+                ("packed_cap", ctypes.c_int64), ("tail_dev", ctypes.c_void_p),
+                ("tail_head", ctypes.c_int64), ("tail_len", ctypes.c_int64),
+                ("tail_cap", ctypes.c_int64), ("window", ctypes.c_int32),
+                ("margin", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python kv_cache_compression_vector_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        PC = ctypes.POINTER(_Codec)
+        L.kvq_record_bytes.argtypes = [PC]
+        L.kvq_record_bytes.restype = ctypes.c_size_t
+        L.kvq_encode_workspace_bytes.argtypes = [PC, I64]
+        L.kvq_encode_workspace_bytes.restype = ctypes.c_size_t
+        L.kvq_codec_tables.argtypes = [PC, P, P, P]
+        L.kvq_encode.argtypes = [PC, P, I64, I64, P, ctypes.POINTER(_Outliers),
+                                 ctypes.POINTER(ctypes.c_int64), P]
+        L.kvq_decode.argtypes = [PC, P, I64, ctypes.POINTER(_Outliers), P, ctypes.c_int, I64, P]
+        L.kvq_score_packed.argtypes = [PC, P, I32, I32, I64, I64, P, I32, I64, I64, I64, P,
+                                       I64, I64, P]
+        L.kvq_cache_init.argtypes = [PC, ctypes.POINTER(_Cache), P, I64, P, I64, I32, I32]
+        L.kvq_append_evict_chunk.argtypes = [PC, ctypes.POINTER(ctypes.POINTER(_Cache)), I32,
+                                             ctypes.POINTER(ctypes.c_void_p), I64, P,
+                                             ctypes.POINTER(ctypes.c_int64)]
+        L.kvq_last_error.restype = ctypes.c_char_p
+        L.kvq_abi_version.restype = ctypes.c_int32
+        for name in ("kvq_codec_tables", "kvq_encode", "kvq_decode", "kvq_score_packed",
+                     "kvq_cache_init", "kvq_append_evict_chunk"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != KVQ_OK:
+        raise KvqError(status, lib().kvq_last_error().decode())
+
+
+def _stream(t: torch.Tensor | None = None):
+    dev = t.device if t is not None and t.is_cuda else None
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class Codec:
+    """Codec descriptor. centroids: host f32 array (or None = Gaussian Lloyd-Max).
+    basis: device bf16 [D, r] (PCA only); mean: device f32 [D] (PCA only, optional)."""
+
+    def __init__(self, head_dim: int, bits: int, seed: int = 42, proj_rank: int = 0,
+                 outlier_T: float = 0.0, centroids=None, basis: torch.Tensor | None = None,
+                 mean: torch.Tensor | None = None, flags: int = 0):
+        self.head_dim, self.bits, self.seed = head_dim, bits, seed
+        self.proj_rank, self.outlier_T = proj_rank, float(outlier_T)
+        self.m = proj_rank if proj_rank else head_dim
+        self._centroids = None if centroids is None else np.ascontiguousarray(centroids, np.float32)
+        self.basis, self.mean = basis, mean
+        self._c = _Codec(head_dim, bits, proj_rank, flags, seed, self.outlier_T, 0,
+                         None if self._centroids is None else self._centroids.ctypes.data,
+                         None if basis is None else basis.data_ptr(),
+                         None if mean is None else mean.data_ptr())
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._c)
+
+    def record_bytes(self) -> int:
+        n = lib().kvq_record_bytes(self.ref)
+        if n == 0:
+            raise KvqError(lib().kvq_last_error() and 10 or 10, lib().kvq_last_error().decode())
+        return n
+
+    def tables(self):
+        L = 1 << self.bits
+        c = np.zeros(L, np.float32)
+        t = np.zeros(L - 1, np.float32)
+        s = np.zeros(self.m, np.int8)
+        _check(lib().kvq_codec_tables(self.ref, c.ctypes.data, t.ctypes.data, s.ctypes.data))
+        return c, t, s
+
+
+class Outliers:
+    """Device CSR outlier list: offsets [n+1] u32, idx [cap] u8, val [cap] bf16 bits."""
+
+    def __init__(self, codec: Codec, n: int, capacity: int, device):
+        self.offsets = torch.zeros(n + 1, dtype=torch.int32, device=device)
+        self.idx = torch.zeros(max(capacity, 1), dtype=torch.uint8, device=device)
+        self.val = torch.zeros(max(capacity, 1), dtype=torch.int16, device=device)
+        self.capacity = capacity
+        wsb = lib().kvq_encode_workspace_bytes(codec.ref, n)
+        self.workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=device)
+        self._s = _Outliers(self.offsets.data_ptr(), self.idx.data_ptr(), self.val.data_ptr(),
+                            capacity, self.workspace.data_ptr(), wsb)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+def encode(codec: Codec, x: torch.Tensor, records: torch.Tensor | None = None,
+           outliers: Outliers | None = None, want_total: bool = False):
+    """x: bf16 [n, >=D] (row stride multiple of 8). Returns records (uint8 [n, rec_bytes]) and,
+    with want_total, the outlier total (synchronises)."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    n = x.shape[0]
+    rb = codec.record_bytes()
+    if records is None:
+        records = torch.empty(n, rb, dtype=torch.uint8, device=x.device)
+    total = ctypes.c_int64(-1)
+    _check(lib().kvq_encode(codec.ref, _ptr(x), n, x.stride(0), _ptr(records),
+                            outliers.ref if outliers is not None else None,
+                            ctypes.byref(total) if want_total else None, _stream(x)))
+    return (records, total.value) if want_total else records
+
+
+def decode(codec: Codec, records: torch.Tensor, n: int | None = None,
+           outliers: Outliers | None = None, out: torch.Tensor | None = None,
+           dtype=torch.float32) -> torch.Tensor:
+    n = records.shape[0] if n is None else n
+    if out is None:
+        out = torch.empty(n, codec.head_dim, dtype=dtype, device=records.device)
+    ydt = 1 if out.dtype == torch.bfloat16 else 0
+    _check(lib().kvq_decode(codec.ref, _ptr(records), n,
+                            outliers.ref if outliers is not None else None, _ptr(out), ydt,
+                            out.stride(0), _stream(records)))
+    return out
+
+
+def score_packed(codec: Codec, q: torch.Tensor, records: torch.Tensor, Hkv: int, T: int,
+                 rec_sb: int, rec_sh: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """q: bf16 [B, Hq, D] (last dim contiguous); records: record (b, kv, t) at index
+    b*rec_sb + kv*rec_sh + t. Returns f32 scores [B, Hq, T]."""
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    _check(lib().kvq_score_packed(codec.ref, _ptr(q), B, Hq, q.stride(0), q.stride(1),
+                                  _ptr(records), Hkv, T, rec_sb, rec_sh, _ptr(out),
+                                  out.stride(0), out.stride(1), _stream(q)))
+    return out
+
+
+class Cache:
+    """Two-region cache over caller (torch) buffers; lengths live on the host."""
+
+    def __init__(self, codec: Codec, packed_cap: int, tail_cap: int, window: int,
+                 margin: int = 16, device="cuda"):
+        self.codec = codec
+        self.packed = torch.zeros(max(packed_cap, 1), codec.record_bytes(), dtype=torch.uint8,
+                                  device=device)
+        self.tail = torch.zeros(tail_cap, codec.head_dim, dtype=torch.bfloat16, device=device)
+        self._s = _Cache()
+        _check(lib().kvq_cache_init(codec.ref, ctypes.byref(self._s), _ptr(self.packed),
+                                    packed_cap, _ptr(self.tail), tail_cap, window, margin))
+
+    @property
+    def packed_len(self):
+        return self._s.packed_len
+
+    @property
+    def tail_len(self):
+        return self._s.tail_len
+
+    @property
+    def tail_head(self):
+        return self._s.tail_head
+
+    def tail_rows(self) -> torch.Tensor:
+        """Dense rows in order, oldest first (a copy)."""
+        cap, h, n = self.tail.shape[0], self._s.tail_head, self._s.tail_len
+        idx = (torch.arange(n, device=self.tail.device) + h) % cap
+        return self.tail[idx]
+
+
+def append_evict_chunk(codec: Codec, caches: list[Cache], new_rows: list[torch.Tensor] | None,
+                       t_new: int):
+    n = len(caches)
+    arr = (ctypes.POINTER(_Cache) * n)(*[ctypes.pointer(c._s) for c in caches])
+    rows = None
+    if t_new > 0:
+        assert new_rows is not None and len(new_rows) == n
+        for r in new_rows:
+            assert r.dtype == torch.bfloat16 and r.is_contiguous() and r.shape[0] >= t_new
+        rows = (ctypes.c_void_p * n)(*[r.data_ptr() for r in new_rows])
+    ev = (ctypes.c_int64 * n)()
+    dev = caches[0].tail if n else None
+    _check(lib().kvq_append_evict_chunk(codec.ref, arr, n, rows, t_new, _stream(dev), ev))
+    return list(ev)

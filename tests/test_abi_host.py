@@ -1,0 +1,158 @@
+"""Host-side checks of the C-ABI library (no GPU needed): exported symbols, tables and signs
+equal to the oracle's bit for bit, record sizes, and typed refusals of invalid arguments
+before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_compression_vector_amd import kvq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvq.lib()
+    names = _declared_functions()
+    assert "kvq_encode" in names and "kvq_append_evict_chunk" in names
+    for name in names:
+        assert hasattr(L, name), name
+    assert L.kvq_abi_version() == 1
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("D", [64, 128, 512])
+def test_tables_and_signs_equal_oracle_bit_for_bit(D, bits):
+    c, t, s = kvq.Codec(D, bits, seed=1234567 + D).tables()
+    oc = oracle.gaussian_table(bits)[1]
+    np.testing.assert_array_equal(c.view(np.uint32), oc.view(np.uint32))
+    np.testing.assert_array_equal(t.view(np.uint32), oracle.thresholds(oc).view(np.uint32))
+    np.testing.assert_array_equal(s, oracle.signs(1234567 + D, D))
+
+
+def test_custom_table_passes_through():
+    custom = np.array([-1.7, -0.4, 0.5, 1.9], np.float32)
+    c, t, _ = kvq.Codec(128, 2, centroids=custom).tables()
+    np.testing.assert_array_equal(c, custom)
+    np.testing.assert_array_equal(t, oracle.thresholds(custom))
+
+
+@pytest.mark.parametrize("m,bits,expect", [(512, 4, 260), (128, 3, 52), (128, 2, 36), (64, 3, 28)])
+def test_record_bytes(m, bits, expect):
+    if m == 64 and bits == 3:
+        cd = kvq.Codec(128, 3, proj_rank=64, basis=None)
+        cd._c.basis_dev = 16  # any non-NULL value: record size needs no device memory
+    else:
+        cd = kvq.Codec(m, bits)
+    assert cd.record_bytes() == expect == oracle.record_bytes(m, bits)
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return kvq.STATUS_NAMES[st], kvq.lib().kvq_last_error().decode()
+
+
+FAKE = 1 << 40  # a 16-byte-aligned non-NULL address; never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(head_dim=96), "KVQ_E_DIM", "head_dim=96"),
+    (dict(head_dim=1024), "KVQ_E_DIM", "head_dim=1024"),
+    (dict(bits=0), "KVQ_E_BITS", "bits=0"),
+    (dict(bits=5), "KVQ_E_BITS", "bits=5"),
+    (dict(flags=1), "KVQ_E_ARG", "flags=1"),
+    (dict(proj_rank=128), "KVQ_E_DIM", "proj_rank=128"),
+    (dict(proj_rank=48), "KVQ_E_DIM", "proj_rank=48"),
+    (dict(head_dim=512, outlier_T=2.0), "KVQ_E_OUTLIER", "m=512"),
+    (dict(outlier_T=-1.0), "KVQ_E_OUTLIER", "outlier_T"),
+    (dict(centroids=np.array([0.0, -1.0, 1.0, 2.0], np.float32), bits=2), "KVQ_E_CENTROIDS", "ascending"),
+    (dict(centroids=np.array([0.0, np.nan, 1.0, 2.0], np.float32), bits=2), "KVQ_E_CENTROIDS", "finite"),
+])
+def test_codec_refusals(kw, status, needle):
+    base = dict(head_dim=128, bits=3)
+    base.update(kw)
+    cd = kvq.Codec(**base)
+    name, msg = _status(kvq.lib().kvq_encode, cd.ref, ctypes.c_void_p(FAKE), 4, base["head_dim"],
+                        ctypes.c_void_p(FAKE), None, None, None)
+    assert name == status and needle in msg, msg
+    assert kvq.lib().kvq_record_bytes(cd.ref) == 0
+
+
+def test_encode_argument_refusals():
+    L = kvq.lib()
+    cd = kvq.Codec(128, 3)
+    P = ctypes.c_void_p
+    assert _status(L.kvq_encode, cd.ref, P(FAKE), 4, 100, P(FAKE), None, None, None)[0] == "KVQ_E_STRIDE"
+    assert _status(L.kvq_encode, cd.ref, P(FAKE), 4, 132, P(FAKE), None, None, None)[0] == "KVQ_E_STRIDE"
+    assert _status(L.kvq_encode, cd.ref, P(FAKE + 2), 4, 128, P(FAKE), None, None, None)[0] == "KVQ_E_STRIDE"
+    assert _status(L.kvq_encode, cd.ref, None, 4, 128, P(FAKE), None, None, None)[0] == "KVQ_E_NULL"
+    assert _status(L.kvq_encode, cd.ref, P(FAKE), -1, 128, P(FAKE), None, None, None)[0] == "KVQ_E_ARG"
+    assert _status(L.kvq_encode, None, P(FAKE), 4, 128, P(FAKE), None, None, None)[0] == "KVQ_E_NULL"
+    # outliers requested without a list, and a list given without outliers
+    cdo = kvq.Codec(128, 2, outlier_T=2.0)
+    assert _status(L.kvq_encode, cdo.ref, P(FAKE), 4, 128, P(FAKE), None, None, None)[0] == "KVQ_E_OUTLIER"
+    ol = kvq._Outliers(FAKE, FAKE, FAKE, 10, FAKE, 0)
+    name, msg = _status(L.kvq_encode, cdo.ref, P(FAKE), 4, 128, P(FAKE), ctypes.byref(ol), None, None)
+    assert name == "KVQ_E_CAPACITY" and "workspace" in msg
+    assert _status(L.kvq_encode, cd.ref, P(FAKE), 4, 128, P(FAKE), ctypes.byref(ol), None, None)[0] == "KVQ_E_OUTLIER"
+
+
+def test_score_argument_refusals():
+    L = kvq.lib()
+    cd = kvq.Codec(128, 3)
+    P = ctypes.c_void_p
+    name, msg = _status(L.kvq_score_packed, cd.ref, P(FAKE), 2, 6, 768, 128, P(FAKE), 4, 10, 40, 10,
+                        P(FAKE), 60, 10, None)
+    assert name == "KVQ_E_ARG" and "multiple" in msg
+    name, msg = _status(L.kvq_score_packed, cd.ref, P(FAKE), 2, 12, 1536, 128, P(FAKE), 4, 10, 40, 10,
+                        P(FAKE), 120, 10, None)
+    assert name == "KVQ_E_ARG" and "Hq/Hkv=3" in msg
+    assert _status(L.kvq_score_packed, cd.ref, P(FAKE), 2, 8, 1028, 128, P(FAKE), 2, 10, 20, 10,
+                   P(FAKE), 80, 10, None)[0] == "KVQ_E_STRIDE"
+    cdo = kvq.Codec(128, 2, outlier_T=2.0)
+    assert _status(L.kvq_score_packed, cdo.ref, P(FAKE), 2, 8, 1024, 128, P(FAKE), 2, 10, 20, 10,
+                   P(FAKE), 80, 10, None)[0] == "KVQ_E_OUTLIER"
+
+
+def test_cache_refusals():
+    L = kvq.lib()
+    cd = kvq.Codec(512, 4)
+    c = kvq._Cache()
+    P = ctypes.c_void_p
+    assert _status(L.kvq_cache_init, cd.ref, ctypes.byref(c), P(FAKE), 10, P(FAKE), 0, 8, 16)[0] == "KVQ_E_ARG"
+    assert _status(L.kvq_cache_init, cd.ref, ctypes.byref(c), P(FAKE), 10, P(FAKE), 64, 8, 16)[0] == "KVQ_OK"
+    assert L.kvq_cache_init(cd.ref, ctypes.byref(c), P(FAKE), 256, P(FAKE), 2000, 1024, 16) == 0
+    assert c.magic != 0 and c.tail_len == 0 and c.packed_len == 0
+    arr = (ctypes.POINTER(kvq._Cache) * 1)(ctypes.pointer(c))
+    # foreign codec
+    other = kvq.Codec(512, 4, seed=7)
+    name, msg = _status(L.kvq_append_evict_chunk, other.ref, arr, 1, None, 0, None, None)
+    assert name == "KVQ_E_CACHE" and "another codec" in msg
+    # struct not built by kvq_cache_init
+    bogus = kvq._Cache()
+    arr2 = (ctypes.POINTER(kvq._Cache) * 1)(ctypes.pointer(bogus))
+    assert _status(L.kvq_append_evict_chunk, cd.ref, arr2, 1, None, 0, None, None)[0] == "KVQ_E_CACHE"
+    # capacity: 3000 new rows do not fit a 2000-row tail when nothing can be evicted yet
+    rows = (ctypes.c_void_p * 1)(FAKE)
+    name, msg = _status(L.kvq_append_evict_chunk, cd.ref, arr, 1, rows, 3000, None, None)
+    assert name == "KVQ_E_CAPACITY" and "tail" in msg
+    assert c.tail_len == 0 and c.packed_len == 0  # unchanged after a refusal
+    # outlier and projection codecs are refused for caches
+    assert _status(L.kvq_cache_init, kvq.Codec(128, 2, outlier_T=2.0).ref, ctypes.byref(c), P(FAKE), 10,
+                   P(FAKE), 64, 8, 16)[0] == "KVQ_E_ARG"
+
+
+def test_zero_sized_calls_are_no_ops():
+    L = kvq.lib()
+    cd = kvq.Codec(128, 3)
+    assert L.kvq_encode(cd.ref, None, 0, 128, None, None, None, None) == 0
+    assert L.kvq_decode(cd.ref, None, 0, None, None, 0, 128, None) == 0

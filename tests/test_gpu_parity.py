@@ -1,0 +1,226 @@
+"""GPU parity of the HIP codec against the CPU oracle, through the C ABI.
+
+Bars: codes bit-exact except coordinates within 1e-5 of a decision boundary (those mismatches
+<= 1e-4 of coordinates); norms within 1e-5 relative; decode (f32, same records) within
+1e-3*||x||; scores within 1e-3 of max(|s|, sum of |terms|) on the same records.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_vector_amd import kvq, synth
+from tests.gpu_helpers import (bf16_host, compare_codes, compare_decoded, oracle_codec_like, say,
+                               unpack_records)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _rows(n, D, seed, scale=1.0, ld=None):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    ld = ld or D
+    x = torch.zeros(n, ld, dtype=torch.bfloat16, device=DEV)
+    x[:, :D] = (scale * torch.randn(n, D, generator=g, device=DEV)).to(torch.bfloat16)
+    return x
+
+
+def _encode_both(codec, x, D):
+    say(f"encode D={D} b={codec.bits} n={x.shape[0]} ld={x.stride(0)} seed={codec.seed}")
+    rec = kvq.encode(codec, x)
+    torch.cuda.synchronize()
+    ref = oracle.encode(oracle_codec_like(codec), bf16_host(x[:, :D]))
+    return rec.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_encode_decode_parity_hadamard(D, bits):
+    n = 1000 + 37 * bits + D // 64  # not a multiple of any tile
+    x = _rows(n, D, seed=D * 10 + bits, ld=D + 8 * (bits % 2))
+    codec = kvq.Codec(D, bits, seed=42 + bits)
+    rec, ref = _encode_both(codec, x, D)
+    mism, flagged = compare_codes(rec, ref, D, bits, f"D={D} b={bits}")
+    say(f"  code mismatches {mism}, flagged {flagged}")
+    # decode of the GPU records: GPU vs oracle, f32 and bf16
+    recd = torch.from_numpy(rec).to(DEV)
+    y32 = kvq.decode(codec, recd, dtype=torch.float32)
+    y16 = kvq.decode(codec, recd, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    yref = oracle.decode(oracle_codec_like(codec), rec)
+    _, norms = unpack_records(rec, D, bits)
+    compare_decoded(y32.cpu().numpy(), yref, norms, f"decode f32 D={D} b={bits}")
+    compare_decoded(y16.float().cpu().numpy(), yref, norms, f"decode bf16 D={D} b={bits}",
+                    extra_ulp_bf16=True)
+
+
+@pytest.mark.parametrize("D,bits", [(128, 2), (128, 3), (512, 4)])
+def test_custom_asymmetric_table(D, bits):
+    L = 1 << bits
+    c = oracle.gaussian_table(bits)[1].astype(np.float64)
+    c = (c * (1.0 + 0.05 * np.sin(np.arange(L))) + 0.03).astype(np.float32)  # still ascending
+    assert np.all(np.diff(c) > 0) and not np.array_equal(c, -c[::-1])
+    codec = kvq.Codec(D, bits, seed=9, centroids=c)
+    x = _rows(700, D, seed=5)
+    rec, ref = _encode_both(codec, x, D)
+    compare_codes(rec, ref, D, bits, "custom table")
+    y = kvq.decode(codec, torch.from_numpy(rec).to(DEV))
+    yref = oracle.decode(oracle_codec_like(codec), rec)
+    compare_decoded(y.cpu().numpy(), yref, unpack_records(rec, D, bits)[1], "custom decode")
+
+
+def test_edge_vectors_zero_single_and_scaled():
+    D, bits = 128, 3
+    codec = kvq.Codec(D, bits, seed=3)
+    x = _rows(67, D, seed=11)
+    x[5] = 0
+    x[6, :] = 0
+    x[6, 17] = 1.0   # one nonzero coordinate
+    x[7] = x[8] * 64  # power-of-two scale
+    rec, ref = _encode_both(codec, x, D)
+    compare_codes(rec, ref, D, bits, "edge")
+    codes, norms = unpack_records(rec, D, bits)
+    assert norms[5] == 0 and np.all(codes[5] == 3)
+    # n = 1 and n = 0
+    one = kvq.encode(codec, x[:1].contiguous())
+    np.testing.assert_array_equal(one.cpu().numpy()[0], rec[0])
+    empty = kvq.encode(codec, x[:0])
+    assert empty.shape[0] == 0
+
+
+def test_scale_invariance_on_gpu():
+    D, bits = 256, 4
+    codec = kvq.Codec(D, bits, seed=13)
+    x = _rows(512, D, seed=17)
+    a = kvq.encode(codec, x).cpu().numpy()
+    b = kvq.encode(codec, (x.float() * 4).to(torch.bfloat16)).cpu().numpy()
+    ca, na = unpack_records(a, D, bits)
+    cb, nb = unpack_records(b, D, bits)
+    np.testing.assert_array_equal(ca, cb)
+    np.testing.assert_array_equal(nb, na * 4)
+
+
+@pytest.mark.parametrize("D,bits,G", [(128, 3, 4), (64, 2, 1), (256, 4, 2), (512, 4, 8), (128, 1, 4)])
+def test_score_packed_parity(D, bits, G):
+    B, Hkv, T = 2, 2, 300
+    Hq = Hkv * G
+    codec = kvq.Codec(D, bits, seed=21)
+    k = _rows(B * Hkv * T, D, seed=31)
+    rec = kvq.encode(codec, k)
+    q = _rows(B * Hq, D, seed=41).view(B, Hq, D)
+    say(f"score D={D} b={bits} G={G} B={B} Hkv={Hkv} T={T}")
+    s = kvq.score_packed(codec, q, rec, Hkv, T, rec_sb=Hkv * T, rec_sh=T)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    rec_h = rec.cpu().numpy().reshape(B, Hkv, T, -1)
+    q_h = bf16_host(q)
+    oc = oracle_codec_like(codec)
+    qq = np.repeat(q_h[:, :, None, :], T, axis=2)                       # [B, Hq, T, D]
+    rr = rec_h[:, np.arange(Hq) // G]                                   # [B, Hq, T, rb]
+    ref = oracle.score(oc, qq.reshape(-1, D), rr.reshape(-1, rr.shape[-1])).reshape(B, Hq, T)
+    # normwise scale: (n/D) sum_i |q'_i z^_i|
+    sgn = oracle.signs(codec.seed, D).astype(np.float64)
+    qv = (q_h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    qp = oracle.fwht_rows(qv * sgn)                                    # [B, Hq, D]
+    codes, norms = unpack_records(rr.reshape(-1, rr.shape[-1]), D, bits)
+    zh = oc.centroids.astype(np.float64)[codes].reshape(B, Hq, T, D)
+    scale = norms.reshape(B, Hq, T) / D * np.abs(qp[:, :, None, :] * zh).sum(-1)
+    err = np.abs(s - ref)
+    bound = 1e-3 * np.maximum(np.abs(ref), scale)
+    assert np.all(err <= bound), f"score error {err.max():.3g} (bound min {bound.min():.3g})"
+
+
+@pytest.mark.parametrize("D,bits,T_", [(128, 2, 2.0), (64, 3, 1.5), (256, 2, 2.5), (128, 4, 2.0)])
+def test_outlier_parity(D, bits, T_):
+    n = 3000 + 13
+    x = _rows(n, D, seed=D + bits)
+    x[:, 3] *= 16  # heavy channel
+    codec = kvq.Codec(D, bits, seed=5, outlier_T=T_)
+    ol = kvq.Outliers(codec, n, capacity=n * D // 4, device=DEV)
+    say(f"outliers D={D} b={bits} T={T_} n={n}")
+    rec, total = kvq.encode(codec, x, outliers=ol, want_total=True)
+    ref = oracle.encode(oracle_codec_like(codec), bf16_host(x))
+    recn = rec.cpu().numpy()
+    compare_codes(recn, ref, D, bits, "outlier codes")
+    off = ol.offsets.cpu().numpy().view(np.uint32)
+    idx = ol.idx.cpu().numpy()
+    val = ol.val.cpu().numpy().view(np.uint16)
+    roff = ref["offsets"]
+    near_t = (ref["flags"] & oracle.FLAG_NEAR_T) != 0
+    per_vec_ok = np.diff(off.astype(np.int64)) == np.diff(roff.astype(np.int64))
+    # counts may differ only for vectors with a coordinate within 1e-5 of T
+    bad = ~per_vec_ok & ~near_t.any(1)
+    assert not bad.any(), f"outlier counts differ at unflagged vectors {np.nonzero(bad)[0][:5]}"
+    assert total == off[-1] and abs(int(off[-1]) - ref["total"]) <= near_t.sum()
+    rate = ref["total"] / (n * D)
+    say(f"  outliers {total} (oracle {ref['total']}), rate {rate:.4f}")
+    for v in np.nonzero(per_vec_ok)[0][:400]:
+        gi = idx[off[v]:off[v + 1]]
+        ri = ref["idx"][roff[v]:roff[v + 1]]
+        np.testing.assert_array_equal(gi, ri)
+        gv = val[off[v]:off[v + 1]].astype(np.int32)
+        rv = ref["val"][roff[v]:roff[v + 1]].astype(np.int32)
+        assert np.all(np.abs(gv - rv) <= 1), "outlier values beyond 1 bf16 ulp"
+    # decode with the side list: GPU vs oracle on the GPU's own records and list
+    y = kvq.decode(codec, rec, outliers=ol)
+    yref = oracle.decode(oracle_codec_like(codec), recn, off, idx[:total], val[:total])
+    compare_decoded(y.cpu().numpy(), yref, unpack_records(recn, D, bits)[1], "outlier decode")
+
+
+def test_outlier_capacity_overflow_reports_and_truncates():
+    D, bits, n = 128, 2, 2000
+    codec = kvq.Codec(D, bits, seed=5, outlier_T=1.0)
+    x = _rows(n, D, seed=99)
+    ol = kvq.Outliers(codec, n, capacity=100, device=DEV)
+    with pytest.raises(kvq.KvqError) as ei:
+        kvq.encode(codec, x, outliers=ol, want_total=True)
+    assert ei.value.name == "KVQ_E_CAPACITY"
+    off = ol.offsets.cpu().numpy().view(np.uint32)
+    ref = oracle.encode(oracle_codec_like(codec), bf16_host(x), ol_cap=100)
+    assert abs(int(off[-1]) - ref["total"]) <= ((ref["flags"] & 2) != 0).sum()
+    y = kvq.decode(codec, kvq.encode(codec, x, outliers=ol), outliers=ol)  # decode ignores the tail
+    assert torch.isfinite(y).all()
+
+
+def test_append_evict_matches_oracle_model():
+    D, bits, window, margin = 128, 3, 200, 16
+    codec = kvq.Codec(D, bits, seed=77)
+    n_caches = 3
+    caches = [kvq.Cache(codec, packed_cap=4096, tail_cap=1500, window=window, margin=margin,
+                        device=DEV) for _ in range(n_caches)]
+    models = [oracle.CacheModel(oracle_codec_like(codec), window, margin) for _ in range(n_caches)]
+    appended = [np.zeros((0, D), np.uint16) for _ in range(n_caches)]
+    seed = 1
+    for t_new in [700, 1, 1, 129, 0, 1, 300, 5, 0, 1]:
+        rows = [_rows(max(t_new, 1), D, seed=seed + k) for k in range(n_caches)]
+        seed += 10
+        say(f"append t_new={t_new}")
+        ev = kvq.append_evict_chunk(codec, caches, rows if t_new else None, t_new)
+        for k in range(n_caches):
+            host = bf16_host(rows[k][:t_new]) if t_new else np.zeros((0, D), np.uint16)
+            appended[k] = np.concatenate([appended[k], host])
+            assert ev[k] == models[k].append_evict(host)
+        torch.cuda.synchronize()
+        for k in range(n_caches):
+            c, mdl = caches[k], models[k]
+            assert c.tail_len == len(mdl.tail) and c.packed_len == len(mdl.packed)
+            np.testing.assert_array_equal(bf16_host(c.tail_rows()), np.stack(mdl.tail))
+            if c.packed_len:
+                got = c.packed[: c.packed_len].cpu().numpy()
+                ref = oracle.encode(oracle_codec_like(codec), appended[k][: c.packed_len])
+                compare_codes(got, ref, D, bits, f"evict cache {k}")
+
+
+def test_config1_full_roundtrip():
+    """8 KV heads x 2048 tokens x head_dim 128, channels 7 and 93 x8; K b=3, V b=2."""
+    K, V = synth.kv_pair_outlier_channels(device=DEV)
+    for name, X, bits in (("K", K, 3), ("V", V, 2)):
+        x = X.reshape(-1, 128)
+        codec = kvq.Codec(128, bits, seed=42)
+        rec, ref = _encode_both(codec, x, 128)
+        mism, flagged = compare_codes(rec, ref, 128, bits, f"config1 {name}")
+        y = kvq.decode(codec, torch.from_numpy(rec).to(DEV))
+        yref = oracle.decode(oracle_codec_like(codec), rec)
+        worst = compare_decoded(y.cpu().numpy(), yref, unpack_records(rec, 128, bits)[1], "config1")
+        say(f"config1 {name}: mismatches {mism} flagged {flagged} worst decode err/||x|| {worst:.2e}")
