@@ -69,16 +69,25 @@ typedef struct kvq_codec {
   uint32_t head_dim;          /* D in {64, 128, 256, 512}                                    */
   uint32_t bits;              /* b in 1..4                                                   */
   uint32_t proj_rank;         /* 0: rotate all D coordinates (m = D).
-                                 r in {32, 64, 128, 256}, r < D: PCA projection to r
-                                 coordinates, then rotation over r (m = r)                   */
+                                 r in {32, 64, 128}, r < D, D*r <= 32768: PCA projection to r
+                                 coordinates (MFMA), then rotation over r (m = r). Projection
+                                 codecs carry no outlier list.                               */
   uint32_t flags;             /* reserved, must be 0                                         */
   uint64_t seed;              /* seed of the +-1 sign diagonal (SplitMix64 stream)           */
   float outlier_T;            /* 0: no side list. > 0: coordinates with |z| > T are listed
                                  (requires m <= 256). Units: rotated, normalised (z).        */
   uint32_t reserved0;         /* must be 0                                                   */
   const float* centroids_host;   /* f32[2^b] strictly ascending, or NULL = Gaussian Lloyd-Max */
-  const uint16_t* basis_dev;     /* PCA only: bf16 [D][r] row-major, column j = basis vector j */
-  const float* mean_dev;         /* PCA only: f32 [D] mean mu, or NULL = zero mean            */
+  const uint16_t* basis_dev;     /* PCA only: bf16 [basis_count][D][r] row-major; column j of
+                                    basis k is its j-th basis vector                          */
+  const float* mean_dev;         /* PCA only: f32 [basis_count][D] means mu, or NULL = zero   */
+  uint32_t basis_count;          /* PCA only: number of bases (0 or 1 = one basis for all rows) */
+  uint32_t basis_block_rows;     /* PCA with basis_count > 1: rows are grouped in blocks of this
+                                    many rows (a multiple of 64); block k uses basis
+                                    basis_index_dev[k]. For the packed score the row of record
+                                    (b, kv, t) is b*rec_sb + kv*rec_sh + t.                     */
+  const int32_t* basis_index_dev;   /* PCA with basis_count > 1: int32 per block, < basis_count;
+                                       the caller guarantees it covers every block touched      */
 } kvq_codec;
 
 /* Outlier side list, CSR by vector. Entry e of vector v is at offsets[v] + e; within a vector

@@ -105,7 +105,10 @@ static hipError_t launch_decode_m(int bits, bool ol, bool bf16, const DecodeArgs
 
 hipError_t launch_decode(int D, int m, int bits, bool ol, bool bf16, const DecodeArgs& a,
                          hipStream_t st) {
-  if (D != m) return hipErrorInvalidValue;  // projection decode: separate kernel
+  if (D != m) {
+    if (ol) return hipErrorInvalidValue;  // projection codecs carry no outlier list
+    return launch_decode_pca(D, m, bits, bf16, a, st);
+  }
   switch (m) {
     case 64: return launch_decode_m<64>(bits, ol, bf16, a, st);
     case 128: return launch_decode_m<128>(bits, ol, bf16, a, st);

@@ -26,6 +26,24 @@ struct Tables {
   int32_t pad[2];
 };
 
+// PCA bases: basis k is bf16 [D][r] at basis + k*D*r, its mean f32 [D] at mean + k*D.
+// Rows are grouped in blocks of block_rows; block i uses basis index[i] (count > 1).
+struct Basis {
+  const uint16_t* basis;
+  const float* mean;        // may be null (zero mean)
+  const int32_t* index;     // may be null when count <= 1
+  int32_t count;
+  int32_t block_rows;
+};
+
+// Basis of the block holding `row`; an out-of-range index is clamped into [0, count).
+__device__ __forceinline__ int basis_of_row(const Basis& b, int64_t row) {
+  if (b.count <= 1) return 0;
+  int k = b.index[row / b.block_rows];
+  k = k < 0 ? 0 : k;
+  return k >= b.count ? b.count - 1 : k;
+}
+
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

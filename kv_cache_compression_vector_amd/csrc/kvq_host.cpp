@@ -112,6 +112,7 @@ struct Resolved {
   int D, m, bits, L;
   bool pca, sym, outliers;
   kvq::Tables tab;
+  kvq::Basis basis;
 };
 
 bool is_pow2_in(uint32_t v, uint32_t lo, uint32_t hi) {
@@ -129,16 +130,33 @@ kvq_status resolve_codec(const kvq_codec* cd, Resolved& r) {
   r.bits = (int)cd->bits;
   r.L = 1 << r.bits;
   r.pca = cd->proj_rank != 0;
+  std::memset(&r.basis, 0, sizeof(r.basis));
   if (r.pca) {
-    if (!is_pow2_in(cd->proj_rank, 32, 256) || cd->proj_rank >= cd->head_dim)
-      return fail(KVQ_E_DIM, "proj_rank=%u not supported (32..256, power of two, < head_dim=%u)",
+    if (!kvq::pca_shape_supported((int)cd->head_dim, (int)cd->proj_rank))
+      return fail(KVQ_E_DIM, "proj_rank=%u with head_dim=%u not supported (r in {32,64,128}, r < D, D*r <= 32768)",
                   cd->proj_rank, cd->head_dim);
     if (!cd->basis_dev) return fail(KVQ_E_NULL, "proj_rank=%u needs basis_dev", cd->proj_rank);
+    if (cd->basis_count > 1) {
+      if (!cd->basis_index_dev)
+        return fail(KVQ_E_NULL, "basis_count=%u needs basis_index_dev", cd->basis_count);
+      if (cd->basis_block_rows == 0 || cd->basis_block_rows % 64)
+        return fail(KVQ_E_ARG, "basis_block_rows=%u must be a positive multiple of 64", cd->basis_block_rows);
+    }
+    r.basis.basis = cd->basis_dev;
+    r.basis.mean = cd->mean_dev;
+    r.basis.index = cd->basis_count > 1 ? cd->basis_index_dev : nullptr;
+    r.basis.count = cd->basis_count > 1 ? (int32_t)cd->basis_count : 1;
+    r.basis.block_rows = cd->basis_count > 1 ? (int32_t)cd->basis_block_rows : 0;
+  } else if (cd->basis_count > 1) {
+    return fail(KVQ_E_ARG, "basis_count=%u without proj_rank", cd->basis_count);
   }
   r.m = r.pca ? (int)cd->proj_rank : r.D;
   if (!(cd->outlier_T >= 0.0f) || std::isinf(cd->outlier_T))
     return fail(KVQ_E_OUTLIER, "outlier_T=%g must be finite and >= 0", (double)cd->outlier_T);
   r.outliers = cd->outlier_T > 0.0f;
+  if (r.outliers && r.pca)
+    return fail(KVQ_E_OUTLIER, "projection codecs carry no outlier list (proj_rank=%u, outlier_T=%g)",
+                cd->proj_rank, (double)cd->outlier_T);
   if (r.outliers && r.m > 256)
     return fail(KVQ_E_OUTLIER, "outlier lists need coded length <= 256 (u8 index), got m=%d", r.m);
   std::memset(&r.tab, 0, sizeof(r.tab));
@@ -256,13 +274,10 @@ kvq_status kvq_encode(const kvq_codec* codec, const void* x_dev, int64_t n, int6
   a.ld = ld_x;
   a.n = n;
   a.rec = static_cast<uint8_t*>(records_dev);
-  if (r.pca) {
-    a.basis = codec->basis_dev;
-    a.mean = codec->mean_dev;
-  }
+  a.pca = r.basis;
   if (!r.outliers) {
     if (n == 0) return ok();
-    if (r.pca) return from_hip(kvq::launch_encode_pca(r.D, r.m, r.bits, r.sym, false, a, 0, s), "encode_pca");
+    if (r.pca) return from_hip(kvq::launch_encode_pca(r.D, r.m, r.bits, r.sym, a, s), "encode_pca");
     return from_hip(kvq::launch_encode(r.m, r.bits, r.sym, a, s), "encode");
   }
   // outlier path: tiles + decoupled look-back over a caller workspace
@@ -280,8 +295,6 @@ kvq_status kvq_encode(const kvq_codec* codec, const void* x_dev, int64_t n, int6
   if (e != hipSuccess) return from_hip(e, "encode workspace clear");
   if (n == 0) {
     e = hipMemcpyAsync(ol->offsets_dev, ws, sizeof(uint32_t), hipMemcpyDeviceToDevice, s);
-  } else if (r.pca) {
-    e = kvq::launch_encode_pca(r.D, r.m, r.bits, r.sym, true, a, n_tiles, s);
   } else {
     e = kvq::launch_encode_outliers(r.m, r.bits, r.sym, a, n_tiles, s);
   }
@@ -329,8 +342,7 @@ kvq_status kvq_decode(const kvq_codec* codec, const void* records_dev, int64_t n
   }
   a.y = y_dev;
   a.ld = ld_y;
-  a.basis = codec->basis_dev;
-  a.mean = codec->mean_dev;
+  a.pca = r.basis;
   return from_hip(kvq::launch_decode(r.D, r.m, r.bits, ol != nullptr, y_dtype == KVQ_BF16, a,
                                      static_cast<hipStream_t>(stream)),
                   "decode");
@@ -348,8 +360,7 @@ kvq_status kvq_score_packed(const kvq_codec* codec, const void* q_dev, int32_t B
   if (B == 0 || Hq == 0 || T == 0) return ok();
   if (Hkv == 0 || Hq % Hkv) return fail(KVQ_E_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   const int group = Hq / Hkv;
-  if (group != 1 && group != 2 && group != 4 && group != 8)
-    return fail(KVQ_E_ARG, "Hq/Hkv=%d not supported (1, 2, 4, 8)", group);
+  if (group < 1 || group > 8) return fail(KVQ_E_ARG, "Hq/Hkv=%d not supported (1..8)", group);
   if (B * Hkv > 65535) return fail(KVQ_E_ARG, "B*Hkv=%d exceeds 65535", B * Hkv);
   if (!q_dev || !records_dev || !scores_dev) return fail(KVQ_E_NULL, "q_dev, records_dev or scores_dev is NULL");
   if (!aligned(q_dev, 16) || q_sb % 8 || q_sh % 8)
@@ -373,8 +384,12 @@ kvq_status kvq_score_packed(const kvq_codec* codec, const void* q_dev, int32_t B
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
-  a.basis = codec->basis_dev;
-  a.mean = codec->mean_dev;
+  a.pca = r.basis;
+  if (r.pca && r.basis.count > 1 &&
+      (r.basis.block_rows % 256 || rec_sb % 256 || rec_sh % 256))
+    return fail(KVQ_E_STRIDE,
+                "score with several bases needs basis_block_rows, rec_sb, rec_sh multiples of 256 "
+                "(got %d, %lld, %lld)", r.basis.block_rows, (long long)rec_sb, (long long)rec_sh);
   return from_hip(kvq::launch_score(r.D, r.m, r.bits, group, a, static_cast<hipStream_t>(stream)),
                   "score_packed");
 }

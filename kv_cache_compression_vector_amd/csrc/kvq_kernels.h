@@ -23,8 +23,7 @@ struct EncodeArgs {
   uint32_t* ws_ticket;      // tile ticket counter
   uint32_t* ws_error;       // set when a look-back wait gave up
   // PCA projection (PCA kernels only)
-  const uint16_t* basis;    // bf16 [D][r]
-  const float* mean;        // f32 [D] or nullptr
+  Basis pca;                // PCA kernels only
 };
 
 struct DecodeArgs {
@@ -37,8 +36,7 @@ struct DecodeArgs {
   int64_t ol_cap;
   void* y;
   int64_t ld;
-  const uint16_t* basis;    // PCA only
-  const float* mean;
+  Basis pca;                // PCA kernels only
 };
 
 struct ScoreArgs {
@@ -51,8 +49,7 @@ struct ScoreArgs {
   float* s;
   int64_t s_sb, s_sh;
   int32_t B, Hq, Hkv, pad;
-  const uint16_t* basis;    // PCA only
-  const float* mean;
+  Basis pca;                // PCA kernels only
 };
 
 // One cache of an append/evict launch: rows [0, rows) of the concatenation (tail ring, new rows)
@@ -95,8 +92,10 @@ hipError_t launch_encode(int m, int bits, bool sym, const EncodeArgs& a, hipStre
 hipError_t launch_encode_outliers(int m, int bits, bool sym, const EncodeArgs& a,
                                   int64_t n_tiles, hipStream_t st);
 int64_t encode_outlier_tile_vectors(int m);
-hipError_t launch_encode_pca(int D, int r, int bits, bool sym, bool outliers,
-                             const EncodeArgs& a, int64_t n_tiles, hipStream_t st);
+bool pca_shape_supported(int D, int r);
+hipError_t launch_encode_pca(int D, int r, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
+hipError_t launch_decode_pca(int D, int r, int bits, bool bf16_out, const DecodeArgs& a,
+                             hipStream_t st);
 hipError_t launch_decode(int D, int m, int bits, bool outliers, bool bf16_out,
                          const DecodeArgs& a, hipStream_t st);
 hipError_t launch_score(int D, int m, int bits, int group, const ScoreArgs& a, hipStream_t st);

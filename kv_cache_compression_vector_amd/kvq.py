@@ -35,7 +35,9 @@ class _Codec(ctypes.Structure):
                 ("proj_rank", ctypes.c_uint32), ("flags", ctypes.c_uint32),
                 ("seed", ctypes.c_uint64), ("outlier_T", ctypes.c_float),
                 ("reserved0", ctypes.c_uint32), ("centroids_host", ctypes.c_void_p),
-                ("basis_dev", ctypes.c_void_p), ("mean_dev", ctypes.c_void_p)]
+                ("basis_dev", ctypes.c_void_p), ("mean_dev", ctypes.c_void_p),
+                ("basis_count", ctypes.c_uint32), ("basis_block_rows", ctypes.c_uint32),
+                ("basis_index_dev", ctypes.c_void_p)]
 
 
 class _Outliers(ctypes.Structure):
@@ -105,20 +107,31 @@ def _ptr(t: torch.Tensor | None):
 
 class Codec:
     """Codec descriptor. centroids: host f32 array (or None = Gaussian Lloyd-Max).
-    basis: device bf16 [D, r] (PCA only); mean: device f32 [D] (PCA only, optional)."""
+    PCA: basis device bf16 [D, r] or [k, D, r]; mean device f32 [D] or [k, D] (optional);
+    with k > 1 bases, basis_index (device int32, one per block of basis_block_rows rows)."""
 
     def __init__(self, head_dim: int, bits: int, seed: int = 42, proj_rank: int = 0,
                  outlier_T: float = 0.0, centroids=None, basis: torch.Tensor | None = None,
-                 mean: torch.Tensor | None = None, flags: int = 0):
+                 mean: torch.Tensor | None = None, flags: int = 0,
+                 basis_index: torch.Tensor | None = None, basis_block_rows: int = 0):
         self.head_dim, self.bits, self.seed = head_dim, bits, seed
         self.proj_rank, self.outlier_T = proj_rank, float(outlier_T)
         self.m = proj_rank if proj_rank else head_dim
         self._centroids = None if centroids is None else np.ascontiguousarray(centroids, np.float32)
-        self.basis, self.mean = basis, mean
+        self.basis, self.mean, self.basis_index = basis, mean, basis_index
+        count = 0 if basis is None else (basis.shape[0] if basis.dim() == 3 else 1)
+        if basis is not None:
+            assert basis.dtype == torch.bfloat16 and basis.is_contiguous()
+        if mean is not None:
+            assert mean.dtype == torch.float32 and mean.is_contiguous()
+        if basis_index is not None:
+            assert basis_index.dtype == torch.int32 and basis_index.is_contiguous()
         self._c = _Codec(head_dim, bits, proj_rank, flags, seed, self.outlier_T, 0,
                          None if self._centroids is None else self._centroids.ctypes.data,
                          None if basis is None else basis.data_ptr(),
-                         None if mean is None else mean.data_ptr())
+                         None if mean is None else mean.data_ptr(),
+                         count, basis_block_rows,
+                         None if basis_index is None else basis_index.data_ptr())
 
     @property
     def ref(self):
@@ -126,8 +139,8 @@ class Codec:
 
     def record_bytes(self) -> int:
         n = lib().kvq_record_bytes(self.ref)
-        if n == 0:
-            raise KvqError(lib().kvq_last_error() and 10 or 10, lib().kvq_last_error().decode())
+        if n == 0:  # invalid codec: report the typed status of its validation
+            _check(lib().kvq_codec_tables(self.ref, None, None, None))
         return n
 
     def tables(self):
