@@ -2,12 +2,70 @@
 //
 // x^ = (n/M) s (.) H_M z^, z^_i = centroid[code_i], outlier entries replacing their coordinate
 // before the inverse rotation [kakeyaturbo PR #15, commit "M5": LUT, outlier scatter, y = z^ n,
-// x = H y sign / wht_len]. Same lane layout as the encoder: 8 coordinates per lane, M/8 lanes
-// per vector, the Hadamard network run in place (H is its own inverse up to 1/M).
+// x = H y sign / wht_len]. The Hadamard network runs in place (H is its own inverse up to
+// 1/M). Without a side list a vector lives in one lane's registers (kvq_lanevec.h); with a
+// side list the 8-coordinates-per-lane layout lets each lane test the entries of its vector.
 #include "kvq_device.h"
 #include "kvq_kernels.h"
+#include "kvq_lanevec.h"
 
 namespace kvq {
+
+template <int M, int BITS, bool BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LV<M>::WAVES)))
+void k_decode_lv(DecodeArgs a) {
+  using L = LV<M>;
+  using St = Stage<L::K>;
+  constexpr int NWC = (M / 32) * BITS, NWT = NWC + 1;
+  __shared__ __attribute__((aligned(16))) uint32_t s_sign[LV<M>::Q > 1 ? M / 2 : 4];
+  __shared__ float lut[16];
+  __shared__ uint4 s_tile[BF16 ? 4 * St::WORDS : 4];
+  build_sign_table<M>(a.tab, s_sign);
+  if (threadIdx.x < 16) lut[threadIdx.x] = a.tab.c[threadIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane % L::Q, vw = lane / L::Q;
+  uint4* tile = s_tile + (BF16 ? wave * St::WORDS : 0);
+  const int64_t n_iter = (a.n + L::VPW - 1) / L::VPW;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < n_iter; it += (int64_t)gridDim.x * 4) {
+    const int64_t vec = it * L::VPW + vw;
+    // lanes past the end decode the last record (their rows are not stored): the wave stays
+    // whole for the staged store and the quad exchanges
+    const int64_t src = vec < a.n ? vec : a.n - 1;
+    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(a.rec) + src * NWT;
+    float zh[L::K];
+    unpack_lookup_lv<M, BITS>(r32, q, lut, zh);
+    const float scale = __uint_as_float(r32[NWC]) * a.tab.inv_m;
+    fwht_regs<L::K>(zh);
+    fwht_cross<L::Q, L::K>(zh, q);
+    const uint32_t* sm = part_signs<M>(a.tab, s_sign, q);
+    if constexpr (BF16) {
+#pragma unroll
+      for (int c = 0; c < L::K / 8; ++c) {
+        const uint4 m = *reinterpret_cast<const uint4*>(sm + 4 * c);
+        uint4 o;
+        o.x = pack_bf16x2(zh[8 * c + 0] * scale, zh[8 * c + 1] * scale) ^ m.x;
+        o.y = pack_bf16x2(zh[8 * c + 2] * scale, zh[8 * c + 3] * scale) ^ m.y;
+        o.z = pack_bf16x2(zh[8 * c + 4] * scale, zh[8 * c + 5] * scale) ^ m.z;
+        o.w = pack_bf16x2(zh[8 * c + 6] * scale, zh[8 * c + 7] * scale) ^ m.w;
+        tile[lane * St::S + c] = o;
+      }
+      stage_rows_out<M>(static_cast<uint16_t*>(a.y), a.ld, it * L::VPW, a.n, tile);
+    } else if (vec < a.n) {
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<float*>(a.y) + vec * a.ld + q * L::K);
+#pragma unroll
+      for (int c = 0; c < L::K / 4; ++c) {
+        const uint32_t m0 = sm[2 * c], m1 = sm[2 * c + 1];
+        uint4 o;
+        o.x = __float_as_uint(zh[4 * c + 0] * scale) ^ (m0 << 16);
+        o.y = __float_as_uint(zh[4 * c + 1] * scale) ^ (m0 & 0x80000000u);
+        o.z = __float_as_uint(zh[4 * c + 2] * scale) ^ (m1 << 16);
+        o.w = __float_as_uint(zh[4 * c + 3] * scale) ^ (m1 & 0x80000000u);
+        st_stream(dst + c, o);
+      }
+    }
+  }
+}
 
 // Codes of the 8 coordinates of chunk c, looked up in the centroid table in LDS.
 template <int M, int BITS>
@@ -75,8 +133,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 
 template <int M, int BITS>
 static hipError_t launch_decode_t(bool ol, bool bf16, const DecodeArgs& a, hipStream_t st) {
-  constexpr int VPW = 64 / (M / 8);
-  const int64_t n_iter = (a.n + VPW - 1) / VPW;
+  const int vpw = ol ? 64 / (M / 8) : LV<M>::VPW;
+  const int64_t n_iter = (a.n + vpw - 1) / vpw;
   int64_t blocks = (n_iter + 3) / 4;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) return hipSuccess;
@@ -85,8 +143,8 @@ static hipError_t launch_decode_t(bool ol, bool bf16, const DecodeArgs& a, hipSt
     if (bf16) hipLaunchKernelGGL((k_decode<M, BITS, true, true>), g, b, 0, st, a);
     else hipLaunchKernelGGL((k_decode<M, BITS, true, false>), g, b, 0, st, a);
   } else {
-    if (bf16) hipLaunchKernelGGL((k_decode<M, BITS, false, true>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((k_decode<M, BITS, false, false>), g, b, 0, st, a);
+    if (bf16) hipLaunchKernelGGL((k_decode_lv<M, BITS, true>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((k_decode_lv<M, BITS, false>), g, b, 0, st, a);
   }
   return hipGetLastError();
 }

@@ -24,6 +24,9 @@ struct Tables {
   float T;                // outlier threshold (0 = off)
   float inv_m;            // 1/M
   int32_t pad[2];
+  // bf16-pair sign masks: entry w flips coordinate 2w (bit 15) and 2w + 1 (bit 31); read with
+  // wave-uniform indices, so they come in through scalar loads.
+  uint32_t sign_pairs[256];
 };
 
 // PCA bases: basis k is bf16 [D][r] at basis + k*D*r, its mean f32 [D] at mean + k*D.

@@ -2,31 +2,46 @@
 //
 // Per vector [kakeyaturbo PR #15, commits "M4 Phase A" / "M4 Phase B"; arc PR #98 "What
 // landed"]: n = ||v||, u = H_M (s (.) v), z = u/n, code_i = #{k : z_i > t_k}, b bit-planes + the
-// f32 norm. One wavefront holds 64/(M/8) vectors, 8 coordinates per lane; the rotation is a
-// butterfly network inside the lane and across the vector's lanes; the quantiser's compare
-// masks are wave ballots, which are exactly the record's bit-planes.
+// f32 norm. The plain and eviction kernels hold a vector in the registers of one lane (two or
+// four lanes for head_dim 256 / 512; kvq_lanevec.h). The outlier kernel keeps the wave-ballot
+// layout of kvq_quant.h (8 coordinates per lane), where a vector's outliers are found by lane
+// order.
 #include "kvq_device.h"
 #include "kvq_kernels.h"
+#include "kvq_lanevec.h"
 #include "kvq_quant.h"
 
 namespace kvq {
 
 template <int M, int BITS, bool SYM>
-__global__ __launch_bounds__(256) void k_encode(EncodeArgs a) {
-  constexpr int LPV = M / 8, VPW = 64 / LPV;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LV<M>::WAVES)))
+void k_encode(EncodeArgs a) {
+  using L = LV<M>;
+  using St = Stage<L::K>;
+  constexpr int NWT = (M / 32) * BITS + 1;
+  __shared__ __attribute__((aligned(16))) uint32_t s_sign[LV<M>::Q > 1 ? M / 2 : 4];
+  __shared__ uint4 s_tile[4 * St::WORDS];
+  build_sign_table<M>(a.tab, s_sign);
+  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane / LPV, c = lane % LPV;
-  uint32_t sm[4];
-  chunk_sign_masks<M>(a.tab, c, sm);
-  const int64_t n_iter = (a.n + VPW - 1) / VPW;
+  const int q = lane % L::Q, vw = lane / L::Q;
+  uint4* tile = s_tile + wave * St::WORDS;
+  const int64_t n_iter = (a.n + L::VPW - 1) / L::VPW;
   for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < n_iter; it += (int64_t)gridDim.x * 4) {
-    const int64_t vec = it * VPW + sub;
+    const int64_t vec = it * L::VPW + vw;
     const bool valid = vec < a.n;
-    float v[8];
-    const float ss = load_signed_chunk(a.x + vec * a.ld, c, sm, valid, v);
-    const float n = sqrtf(vector_sum<LPV>(ss));
-    fwht_vector<LPV>(v, c);
-    quantize_store<M, BITS, SYM>(v, n, valid, vec, sub, c, a.tab, a.rec);
+    const int64_t vec0 = it * L::VPW;
+    stage_rows_in<M>([&](int j) {  // rows past the end repeat the last row (results unused)
+      const int64_t r = vec0 + j < a.n ? vec0 + j : a.n - 1;
+      return a.x + r * a.ld;
+    }, tile);
+    float v[L::K];
+    const float ss = load_part<L::K>(tile + lane * St::S, part_signs<M>(a.tab, s_sign, q), v);
+    const float n = sqrtf(part_sum<L::Q>(ss));
+    fwht_regs<L::K, 8>(v);
+    fwht_cross<L::Q, L::K>(v, q);
+    quantize_store_lv<M, BITS, SYM>(v, n, valid, q, a.tab,
+                                    reinterpret_cast<uint32_t*>(a.rec) + vec * NWT);
   }
 }
 
@@ -229,35 +244,45 @@ hipError_t launch_encode_outliers(int m, int bits, bool sym, const EncodeArgs& a
 // Eviction: encode whole chunks of the oldest dense rows of several caches in one launch
 // [arc PR #98, "Eviction is chunked, on purpose"]. Row r of cache k is row r of the
 // concatenation (tail ring from its head, then the new rows). Chunks are 128 rows and a wave
-// never straddles two caches (64/(M/8) divides 128).
+// (64 / Q vectors) never straddles two caches.
 template <int M, int BITS, bool SYM>
-__global__ __launch_bounds__(256) void k_evict(EvictArgs a) {
-  constexpr int LPV = M / 8, VPW = 64 / LPV;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LV<M>::WAVES)))
+void k_evict(EvictArgs a) {
+  using L = LV<M>;
+  using St = Stage<L::K>;
+  constexpr int NWT = (M / 32) * BITS + 1;
+  __shared__ __attribute__((aligned(16))) uint32_t s_sign[LV<M>::Q > 1 ? M / 2 : 4];
+  __shared__ uint4 s_tile[4 * St::WORDS];
+  build_sign_table<M>(a.tab, s_sign);
+  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane / LPV, c = lane % LPV;
-  uint32_t sm[4];
-  chunk_sign_masks<M>(a.tab, c, sm);
-  const int64_t n_iter = a.total_rows / VPW;
+  const int q = lane % L::Q, vw = lane / L::Q;
+  uint4* tile = s_tile + wave * St::WORDS;
+  const int64_t n_iter = a.total_rows / L::VPW;
   for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < n_iter; it += (int64_t)gridDim.x * 4) {
-    const int64_t g0 = it * VPW;
+    const int64_t g0 = it * L::VPW;
     int k = 0;
     while (k + 1 < a.n_caches && g0 >= a.c[k + 1].row_begin) ++k;
     const EvictCache& ec = a.c[k];
-    const int64_t r = g0 - ec.row_begin + sub;
-    const uint16_t* row = r < ec.tail_len
-                              ? ec.tail + ((ec.tail_head + r) % ec.tail_cap) * a.D
-                              : ec.fresh + (r - ec.tail_len) * a.D;
-    float v[8];
-    const float ss = load_signed_chunk(row, c, sm, true, v);
-    const float n = sqrtf(vector_sum<LPV>(ss));
-    fwht_vector<LPV>(v, c);
-    quantize_store<M, BITS, SYM>(v, n, true, r, sub, c, a.tab, ec.dst);
+    const int64_t r0 = g0 - ec.row_begin, r = r0 + vw;
+    stage_rows_in<M>([&](int j) {
+      const int64_t rr = r0 + j;
+      return rr < ec.tail_len ? ec.tail + ((ec.tail_head + rr) % ec.tail_cap) * a.D
+                              : ec.fresh + (rr - ec.tail_len) * a.D;
+    }, tile);
+    float v[L::K];
+    const float ss = load_part<L::K>(tile + lane * St::S, part_signs<M>(a.tab, s_sign, q), v);
+    const float n = sqrtf(part_sum<L::Q>(ss));
+    fwht_regs<L::K, 8>(v);
+    fwht_cross<L::Q, L::K>(v, q);
+    quantize_store_lv<M, BITS, SYM>(v, n, true, q, a.tab,
+                                    reinterpret_cast<uint32_t*>(ec.dst) + r * NWT);
   }
 }
 
 template <int M, int BITS, bool SYM>
 static hipError_t launch_evict_t(const EvictArgs& a, hipStream_t st) {
-  constexpr int VPW = 64 / (M / 8);
+  constexpr int VPW = LV<M>::VPW;
   const int64_t n_iter = a.total_rows / VPW;
   int64_t blocks = (n_iter + 3) / 4;
   if (blocks > 65536) blocks = 65536;
@@ -296,7 +321,7 @@ hipError_t launch_evict(int m, int bits, bool sym, const EvictArgs& a, hipStream
 
 template <int M, int BITS, bool SYM>
 static hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t st) {
-  constexpr int VPW = 64 / (M / 8);
+  constexpr int VPW = LV<M>::VPW;
   const int64_t n_iter = (a.n + VPW - 1) / VPW;
   int64_t blocks = (n_iter + 3) / 4;
   if (blocks > 65536) blocks = 65536;

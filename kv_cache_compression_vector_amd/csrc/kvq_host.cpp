@@ -176,7 +176,10 @@ kvq_status resolve_codec(const kvq_codec* cd, Resolved& r) {
     if (c[r.L - 1 - k] != -c[k]) r.sym = false;
   uint64_t st = cd->seed;
   for (int i = 0; i < r.m; ++i)
-    if (splitmix64_next(st) >> 63) r.tab.sign_words[i >> 5] |= 1u << (i & 31);
+    if (splitmix64_next(st) >> 63) {
+      r.tab.sign_words[i >> 5] |= 1u << (i & 31);
+      r.tab.sign_pairs[i >> 1] |= (i & 1) ? 0x80000000u : 0x8000u;
+    }
   r.tab.T = cd->outlier_T;
   r.tab.inv_m = 1.0f / (float)r.m;
   return ok();

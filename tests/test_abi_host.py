@@ -113,9 +113,9 @@ def test_score_argument_refusals():
     name, msg = _status(L.kvq_score_packed, cd.ref, P(FAKE), 2, 6, 768, 128, P(FAKE), 4, 10, 40, 10,
                         P(FAKE), 60, 10, None)
     assert name == "KVQ_E_ARG" and "multiple" in msg
-    name, msg = _status(L.kvq_score_packed, cd.ref, P(FAKE), 2, 12, 1536, 128, P(FAKE), 4, 10, 40, 10,
-                        P(FAKE), 120, 10, None)
-    assert name == "KVQ_E_ARG" and "Hq/Hkv=3" in msg
+    name, msg = _status(L.kvq_score_packed, cd.ref, P(FAKE), 2, 36, 4608, 128, P(FAKE), 4, 10, 40, 10,
+                        P(FAKE), 360, 10, None)
+    assert name == "KVQ_E_ARG" and "Hq/Hkv=9" in msg
     assert _status(L.kvq_score_packed, cd.ref, P(FAKE), 2, 8, 1028, 128, P(FAKE), 2, 10, 20, 10,
                    P(FAKE), 80, 10, None)[0] == "KVQ_E_STRIDE"
     cdo = kvq.Codec(128, 2, outlier_T=2.0)
