@@ -83,7 +83,7 @@ typedef struct kvq_codec {
   const float* mean_dev;         /* PCA only: f32 [basis_count][D] means mu, or NULL = zero   */
   uint32_t basis_count;          /* PCA only: number of bases (0 or 1 = one basis for all rows) */
   uint32_t basis_block_rows;     /* PCA with basis_count > 1: rows are grouped in blocks of this
-                                    many rows (a multiple of 64); block k uses basis
+                                    many rows (a multiple of 256); block k uses basis
                                     basis_index_dev[k]. For the packed score the row of record
                                     (b, kv, t) is b*rec_sb + kv*rec_sh + t.                     */
   const int32_t* basis_index_dev;   /* PCA with basis_count > 1: int32 per block, < basis_count;

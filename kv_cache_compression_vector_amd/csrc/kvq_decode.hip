@@ -34,7 +34,7 @@ void k_decode_lv(DecodeArgs a) {
     const int64_t src = vec < a.n ? vec : a.n - 1;
     const uint32_t* r32 = reinterpret_cast<const uint32_t*>(a.rec) + src * NWT;
     float zh[L::K];
-    unpack_lookup_lv<M, BITS>(r32, q, lut, zh);
+    unpack_lookup_lv<M, BITS>(r32, q, LdsLut{lut}, zh);
     const float scale = __uint_as_float(r32[NWC]) * a.tab.inv_m;
     fwht_regs<L::K>(zh);
     fwht_cross<L::Q, L::K>(zh, q);

@@ -139,8 +139,8 @@ kvq_status resolve_codec(const kvq_codec* cd, Resolved& r) {
     if (cd->basis_count > 1) {
       if (!cd->basis_index_dev)
         return fail(KVQ_E_NULL, "basis_count=%u needs basis_index_dev", cd->basis_count);
-      if (cd->basis_block_rows == 0 || cd->basis_block_rows % 64)
-        return fail(KVQ_E_ARG, "basis_block_rows=%u must be a positive multiple of 64", cd->basis_block_rows);
+      if (cd->basis_block_rows == 0 || cd->basis_block_rows % 256)
+        return fail(KVQ_E_ARG, "basis_block_rows=%u must be a positive multiple of 256", cd->basis_block_rows);
     }
     r.basis.basis = cd->basis_dev;
     r.basis.mean = cd->mean_dev;

@@ -421,11 +421,29 @@ __device__ __forceinline__ void quantize_store_lv(float (&u)[LV<M>::K], float n,
   }
 }
 
-// Codes of this lane part's K coordinates looked up in the LDS centroid table.
+// Centroid tables for the unpacking below: in LDS, or held by lanes 0..15 of one register and
+// fetched with a cross-lane permute (no LDS space needed).
+struct LdsLut {
+  const float* p;
+  __device__ __forceinline__ float operator()(uint32_t code) const { return p[code]; }
+};
+struct LaneLut {
+  int v;  // bits of centroid (lane % 16)
+  __device__ __forceinline__ explicit LaneLut(const Tables& tab) : v(0) {
+    const int l = __lane_id() & 15;
+#pragma unroll
+    for (int k = 0; k < kMaxLevels; ++k) v = l == k ? __float_as_int(tab.c[k]) : v;
+  }
+  __device__ __forceinline__ float operator()(uint32_t code) const {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((int)(code << 2), v));
+  }
+};
+
+// Codes of this lane part's K coordinates looked up in the centroid table lut.
 //  Q == 1: words = the whole record's code words. Q > 1: words g as laid out above.
-template <int M, int BITS>
+template <int M, int BITS, class Lut>
 __device__ __forceinline__ void unpack_lookup_lv(const uint32_t* __restrict__ r32, int q,
-                                                 const float* __restrict__ lut,
+                                                 const Lut& lut,
                                                  float (&zh)[LV<M>::K]) {
   constexpr int Q = LV<M>::Q, K = LV<M>::K, NWC = (M / 32) * BITS;
   if constexpr (Q == 1) {
@@ -437,7 +455,7 @@ __device__ __forceinline__ void unpack_lookup_lv(const uint32_t* __restrict__ r3
       uint32_t code = 0;
 #pragma unroll
       for (int p = 0; p < BITS; ++p) code |= ((w[(pos >> 5) * BITS + p] >> (pos & 31)) & 1u) << p;
-      zh[k] = lut[code];
+      zh[k] = lut(code);
     }
   } else {
     const int sh = 16 * (q & 1);
@@ -452,7 +470,7 @@ __device__ __forceinline__ void unpack_lookup_lv(const uint32_t* __restrict__ r3
         uint32_t code = 0;
 #pragma unroll
         for (int p = 0; p < BITS; ++p) code |= ((w[p] >> t) & 1u) << p;
-        zh[8 * t + s] = lut[code];
+        zh[8 * t + s] = lut(code);
       }
     }
   }

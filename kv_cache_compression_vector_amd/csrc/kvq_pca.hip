@@ -4,221 +4,340 @@
 // The projection follows the pages' per-token pipeline project -> rotate -> scale ->
 // Lloyd-Max [kakeyaturbo PR #15, commits "M4 Phase A" ((X - mu) @ basis^T) and "M5" (unproject
 // on the matrix engine)]. It is a genuine dense contraction, so it runs on
-// v_mfma_f32_16x16x32_bf16: x and B are bf16, so every product is exact and accumulates in f32.
-// The decode splits v^ into two bf16 halves (hi + lo) so the unprojection keeps ~2^-17 relative
-// precision. Rows are processed in tiles of 64; the basis of a tile stays in LDS until a tile
-// needs another basis.
+// v_mfma_f32_16x16x32_bf16: x and B are bf16, every product is exact and sums in f32; B^T mu
+// enters as the accumulator's initial value. The decode multiplies B by v^ split into two bf16
+// halves (hi + lo), keeping ~2^-17 relative precision, with mu as the initial value.
+//
+// A block of W waves (4, or 2 for the largest bases) takes 64 W consecutive rows, all under one
+// basis (basis blocks are multiples of 256 rows). Each wave owns 64 rows and one LDS region
+// that holds, in turn, its swizzled input chunk, the MFMA output and the staged output rows,
+// so global traffic moves in 256-byte row segments, 1 KB per instruction. After the
+// projection each lane owns one vector (r <= 128 coordinates in registers) for the rotation
+// and quantiser of kvq_lanevec.h. LDS at (D, r) = (128, 64): basis 16 KB + 4 x 16 KB, so two
+// blocks share a CU.
+//
+// MFMA 16x16x32 operand layout (lane l): A[row l%16][k 8(l/16)..+7], B[k 8(l/16)..+7][col l%16],
+// result D[row 4(l/16)+i][col l%16], i = 0..3.
 #include "kvq_device.h"
 #include "kvq_kernels.h"
-#include "kvq_quant.h"
+#include "kvq_lanevec.h"
 
 namespace kvq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPcaTile = 64;
+// Per-shape constants. Input (encode) and output (decode) rows move through LDS in column
+// chunks of 256 bytes: 128 bf16 (or 64 f32) columns, the whole row when it is shorter.
+template <int D, int R>
+struct PcaShape {
+  static constexpr int DC = D < 128 ? D : 128;            // bf16 columns per staged chunk
+  static constexpr int CCH = DC / 8;                      // 16-byte chunks per staged row
+  static constexpr int RCH = CCH > R / 4 ? CCH : R / 4;   // region row stride (f32 y, hi|lo v^)
+  static constexpr int BASIS_BYTES = D * R * 2;
+  static constexpr int REGION_BYTES = 64 * RCH * 16;
+  static constexpr int W = BASIS_BYTES + 4 * REGION_BYTES <= 128 * 1024 ? 4 : 2;  // waves
+  static constexpr int ROWS = 64 * W;                     // rows per block tile
+};
+
+// Mean used when a codec gives none (read only).
+__device__ const float kZeroMean[512] = {};
 
 __device__ __forceinline__ floatx4 mfma_bf16(const uint4& a, const uint4& b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 16-byte chunk c of row r in a tile whose rows are CH chunks apart, XOR-swizzled so that 16
+// lanes reading one chunk column (or one row each) hit distinct banks.
+template <int CH>
+__device__ __forceinline__ int swz(int r, int c) {
+  constexpr int mask = (CH < 16 ? CH : 16) - 1;
+  return r * CH + (c ^ (r & mask));
+}
+
+// The lane index as a value the compiler cannot see through: addresses derived from it inside a
+// tile loop are recomputed each tile instead of being hoisted out of the loop (and spilled).
+__device__ __forceinline__ int opaque_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 // ------------------------------------------------------------------------------------------
-// Encode.
-//   LDS: bT[r][D] = transposed basis (B operand: 8 consecutive k = input dims per lane),
-//        mp[r] = B^T mu, y[64][r] = projected tile.
-//   MFMA 16x16x32: lane l holds A[row l%16][k 8(l/16)..+7], B[k 8(l/16)..+7][col l%16] and
-//   returns D[row 4(l/16)+i][col l%16], i = 0..3.
+// Encode. The random signs are folded into the staged basis (column j of B times s_j, exact
+// in bf16), so the MFMA yields s (.) B^T x directly. The product is formed transposed,
+// (B^T)(x^T), so that lane l receives 4 consecutive projected coordinates of one row.
 template <int D, int R, int BITS, bool SYM>
-__global__ __launch_bounds__(256) void k_encode_pca(EncodeArgs a) {
-  constexpr int KS = D / 32, NT = R / 16, LPV = R / 8, VPW = 64 / LPV;
-  constexpr int BTS = D + 8;  // padded row (bf16 elements): 16-byte aligned rows, fewer conflicts
-  constexpr int YS = R + 4;   // padded f32 row
-  __shared__ __attribute__((aligned(16))) uint16_t bT[R * BTS];
-  __shared__ float mp[R];
-  __shared__ __attribute__((aligned(16))) float y[kPcaTile * YS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane / LPV, c = lane % LPV;
-  const uint32_t sbyte = (a.tab.sign_words[(c >> 2) & 15] >> (8 * (c & 3))) & 0xFFu;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void k_encode_pca(EncodeArgs a, int64_t tiles_per_block) {
+  using P = PcaShape<D, R>;
+  constexpr int W = P::W, DC = P::DC, CCH = P::CCH, RCH = P::RCH;
+  constexpr int BCH = D / 8;   // B^T row (one basis column, D bf16) in chunks
+  constexpr int NT = R / 16, NWT = (R / 32) * BITS + 1;
+  __shared__ uint4 s_bT[R * BCH];
+  __shared__ uint4 s_reg[W * 64 * RCH];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  uint4* reg = s_reg + wave * 64 * RCH;
+  float4 mp[NT];  // -(s (.) B^T mu) at this lane's output columns 16 t + 4 (l / 16) .. +3
   int cur = -1;
-  const int64_t n_tiles = (a.n + kPcaTile - 1) / kPcaTile;
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int64_t row0 = tile * kPcaTile;
-    const int bi = basis_of_row(a.pca, row0);
+  const int64_t n_tiles = (a.n + P::ROWS - 1) / P::ROWS;
+  const int64_t t0 = blockIdx.x * tiles_per_block;
+  const int64_t t1 = t0 + tiles_per_block < n_tiles ? t0 + tiles_per_block : n_tiles;
+  for (int64_t tile = t0; tile < t1; ++tile) {
+    const int64_t row0 = tile * P::ROWS;
+    const int bi = basis_of_row(a.pca, row0);  // block tiles never straddle basis blocks
     if (bi != cur) {
       __syncthreads();
       const uint16_t* Bk = a.pca.basis + (int64_t)bi * D * R;
-      for (int e = tid; e < D * R; e += 256) {  // B[d][j] -> bT[j][d]
+      uint16_t* bt16 = reinterpret_cast<uint16_t*>(s_bT);
+      for (int e = tid; e < D * R; e += 64 * W) {
         const int d = e / R, j = e % R;
-        bT[j * BTS + d] = Bk[e];
+        const uint32_t flip = (a.tab.sign_pairs[j >> 1] >> (16 * (j & 1))) & 0x8000u;
+        bt16[swz<BCH>(j, d / 8) * 8 + d % 8] = (uint16_t)(Bk[e] ^ flip);
       }
       __syncthreads();
+      // -(s (.) B^T mu) through the (idle) regions: one column per thread, then each lane
+      // takes the 4 NT columns its accumulators start from
       if (tid < R) {
         float s = 0.0f;
         if (a.pca.mean) {
           const float* mu = a.pca.mean + (int64_t)bi * D;
-          for (int d = 0; d < D; ++d) s = fmaf(__uint_as_float((uint32_t)bT[tid * BTS + d] << 16), mu[d], s);
+          for (int c = 0; c < BCH; ++c) {
+            const uint4 w = s_bT[swz<BCH>(tid, c)];
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              s = fmaf(bf16lo_to_f32(u[e]), mu[8 * c + 2 * e], s);
+              s = fmaf(bf16hi_to_f32(u[e]), mu[8 * c + 2 * e + 1], s);
+            }
+          }
         }
-        mp[tid] = s;
+        reinterpret_cast<float*>(s_reg)[tid] = -s;
       }
-      cur = bi;
       __syncthreads();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) mp[t] = reinterpret_cast<const float4*>(s_reg)[4 * t + ((tid & 63) >> 4)];
+      __syncthreads();
+      cur = bi;
     }
-    // projection of rows row0 + 16*wave .. +15
-    {
-      const int64_t row = row0 + 16 * wave + (lane & 15);
-      const bool ok = row < a.n;
-      floatx4 acc[NT];
+    const int64_t rw0 = row0 + 64 * wave;
+    const int ln = opaque_lane();
+    floatx4 acc[4][NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int k0 = ks * 32 + 8 * (lane >> 4);
-        uint4 av = make_uint4(0, 0, 0, 0);
-        if (ok) av = *reinterpret_cast<const uint4*>(a.x + row * a.ld + k0);
+      for (int rt = 0; rt < 4; ++rt) acc[rt][t] = floatx4{mp[t].x, mp[t].y, mp[t].z, mp[t].w};
+#pragma unroll
+    for (int dc = 0; dc < D / DC; ++dc) {
+      // coalesced, swizzled input chunk: 64 rows x DC bf16 (rows past the end repeat the last);
+      // all loads are issued before the first LDS write: one memory round trip per chunk
+      uint4 in[CCH];
+#pragma unroll
+      for (int k = 0; k < CCH; ++k) {
+        const int id = k * 64 + ln, p = id / CCH, c = id % CCH;
+        const int64_t row = rw0 + p < a.n ? rw0 + p : a.n - 1;
+        in[k] = ld_stream(reinterpret_cast<const uint4*>(a.x + row * a.ld + dc * DC) + c);
+      }
+#pragma unroll
+      for (int k = 0; k < CCH; ++k) {
+        const int id = k * 64 + ln, p = id / CCH, c = id % CCH;
+        reg[swz<RCH>(p, c)] = in[k];
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int ks = 0; ks < DC / 32; ++ks) {
+        const int ck = 4 * ks + (ln >> 4);
+        uint4 xf[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) xf[rt] = reg[swz<RCH>(16 * rt + (ln & 15), ck)];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const uint4 bv = *reinterpret_cast<const uint4*>(&bT[(t * 16 + (lane & 15)) * BTS + k0]);
-          acc[t] = mfma_bf16(av, bv, acc[t]);
+          const uint4 bf = s_bT[swz<BCH>(16 * t + (ln & 15), dc * CCH + ck)];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) acc[rt][t] = mfma_bf16(bf, xf[rt], acc[rt][t]);
         }
       }
+      __builtin_amdgcn_wave_barrier();
+    }
+    // projected rows (f32) into the region: acc[rt][t] = y[16 rt + l % 16][16 t + 4 (l / 16) ..+3]
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
+        reg[swz<RCH>(16 * rt + (ln & 15), 4 * t + (ln >> 4))] =
+            make_uint4(__float_as_uint(acc[rt][t][0]), __float_as_uint(acc[rt][t][1]),
+                       __float_as_uint(acc[rt][t][2]), __float_as_uint(acc[rt][t][3]));
+    __builtin_amdgcn_wave_barrier();
+    // one vector per lane: norm, rotation, quantiser
+    const int64_t vec = rw0 + ln;
+    float v[R];
+    float ss = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          y[(16 * wave + 4 * (lane >> 4) + i) * YS + t * 16 + (lane & 15)] = acc[t][i];
+    for (int c = 0; c < R / 4; ++c) {
+      const uint4 f = reg[swz<RCH>(ln, c)];
+      v[4 * c + 0] = __uint_as_float(f.x);
+      v[4 * c + 1] = __uint_as_float(f.y);
+      v[4 * c + 2] = __uint_as_float(f.z);
+      v[4 * c + 3] = __uint_as_float(f.w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = fmaf(v[4 * c + e], v[4 * c + e], ss);
     }
-    __syncthreads();
-    // Hadamard codec over the r projected coordinates, VPW vectors per wave step
-#pragma unroll
-    for (int st = 0; st < 16 / VPW; ++st) {
-      const int local = 16 * wave + st * VPW + sub;
-      const int64_t vec = row0 + local;
-      const bool valid = vec < a.n;
-      float v[8];
-      float ss = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = y[local * YS + 8 * c + j] - mp[8 * c + j];
-        v[j] = __uint_as_float(__float_as_uint(p) ^ (((sbyte >> j) & 1u) << 31));
-        ss = fmaf(p, p, ss);
-      }
-      const float n = sqrtf(vector_sum<LPV>(ss));
-      fwht_vector<LPV>(v, c);
-      quantize_store<R, BITS, SYM>(v, n, valid, vec, sub, c, a.tab, a.rec);
-    }
+    __builtin_amdgcn_wave_barrier();
+    const float n = sqrtf(ss);
+    fwht_regs<R>(v);
+    quantize_store_lv<R, BITS, SYM>(v, n, vec < a.n, 0, a.tab,
+                                    reinterpret_cast<uint32_t*>(a.rec) + vec * NWT);
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode.
-//   LDS: Bs[D][r] = basis as stored (B operand of the unprojection: k = j contiguous),
-//        mu[D], vh/vl[64][r] = bf16 hi / lo halves of v^.
+// Decode: out^T[d][row] = sum_j B[d][j] v^[row][j] + mu[d]. The A operand is B as stored (row d,
+// k = j contiguous) with the signs folded into its columns, the B operand the rows of
+// scale * H z^, so lane l receives 4 consecutive d of one row.
 template <int D, int R, int BITS, bool BF16>
-__global__ __launch_bounds__(256) void k_decode_pca(DecodeArgs a) {
-  constexpr int KS = R / 32, NT = D / 16, LPV = R / 8, VPW = 64 / LPV;
-  constexpr int NWC = (R / 32) * BITS, NWT = NWC + 1;
-  constexpr int BS = R + 8;   // padded bf16 row
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[D * BS];
-  __shared__ float mu[D];
-  __shared__ __attribute__((aligned(16))) uint16_t vh[kPcaTile * BS];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[kPcaTile * BS];
-  __shared__ float lut[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane / LPV, c = lane % LPV;
-  if (tid < 16) lut[tid] = a.tab.c[tid];
-  const uint32_t sbyte = (a.tab.sign_words[(c >> 2) & 15] >> (8 * (c & 3))) & 0xFFu;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void k_decode_pca(DecodeArgs a, int64_t tiles_per_block) {
+  using P = PcaShape<D, R>;
+  constexpr int W = P::W, CCH = P::CCH, RCH = P::RCH;
+  constexpr int HCH = R / 8;                      // basis row (R bf16) in chunks = v^ half row
+  constexpr int OCOLS = BF16 ? P::DC : P::DC / 2; // output columns per staged chunk (256 B)
+  constexpr int ES = BF16 ? 2 : 4;                // output element bytes
+  constexpr int KS = R / 32, NWC = (R / 32) * BITS, NWT = NWC + 1;
+  __shared__ uint4 s_B[D * HCH];
+  __shared__ uint4 s_reg[W * 64 * RCH];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const LaneLut lut(a.tab);
+  uint4* reg = s_reg + wave * 64 * RCH;
+  const float* mu = kZeroMean;
   int cur = -1;
-  const int64_t n_tiles = (a.n + kPcaTile - 1) / kPcaTile;
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int64_t row0 = tile * kPcaTile;
+  const int64_t n_tiles = (a.n + P::ROWS - 1) / P::ROWS;
+  const int64_t t0 = blockIdx.x * tiles_per_block;
+  const int64_t t1 = t0 + tiles_per_block < n_tiles ? t0 + tiles_per_block : n_tiles;
+  for (int64_t tile = t0; tile < t1; ++tile) {
+    const int64_t row0 = tile * P::ROWS;
     const int bi = basis_of_row(a.pca, row0);
     if (bi != cur) {
       __syncthreads();
-      const uint16_t* Bk = a.pca.basis + (int64_t)bi * D * R;
-      for (int e = tid; e < D * R; e += 256) Bs[(e / R) * BS + (e % R)] = Bk[e];
-      for (int d = tid; d < D; d += 256) mu[d] = a.pca.mean ? a.pca.mean[(int64_t)bi * D + d] : 0.0f;
+      const uint4* Bk = reinterpret_cast<const uint4*>(a.pca.basis + (int64_t)bi * D * R);
+      for (int e = tid; e < D * HCH; e += 64 * W) {
+        const uint4 w = Bk[e];
+        const int j0 = 8 * (e % HCH);  // the chunk's first basis column; signs folded in
+        s_B[swz<HCH>(e / HCH, e % HCH)] =
+            make_uint4(w.x ^ a.tab.sign_pairs[j0 / 2], w.y ^ a.tab.sign_pairs[j0 / 2 + 1],
+                       w.z ^ a.tab.sign_pairs[j0 / 2 + 2], w.w ^ a.tab.sign_pairs[j0 / 2 + 3]);
+      }
+      if (a.pca.mean) mu = a.pca.mean + (int64_t)bi * D;
       cur = bi;
+      __syncthreads();
     }
-    __syncthreads();
+    const int64_t rw0 = row0 + 64 * wave;
+    const int ln = opaque_lane();
+    const int64_t vec = rw0 + ln;
+    const int64_t src = vec < a.n ? vec : a.n - 1;  // lanes past the end decode the last record
+    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(a.rec) + src * NWT;
+    float zh[R];
+    unpack_lookup_lv<R, BITS>(r32, 0, lut, zh);
+    const float scale = __uint_as_float(r32[NWC]) * a.tab.inv_m;
+    fwht_regs<R>(zh);
+    // scale * (H z^) as bf16 hi | lo halves of the lane's region row (the signs s are in s_B)
 #pragma unroll
-    for (int st = 0; st < 16 / VPW; ++st) {
-      const int local = 16 * wave + st * VPW + sub;
-      const int64_t vec = row0 + local;
-      float zh[8];
-      float nrm = 0.0f;
-      if (vec < a.n) {
-        const uint32_t* r32 = reinterpret_cast<const uint32_t*>(a.rec) + vec * NWT;
+    for (int c = 0; c < HCH; ++c) {
+      uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int pos = j * LPV + c;
-          uint32_t code = 0;
-#pragma unroll
-          for (int p = 0; p < BITS; ++p) code |= ((r32[(pos >> 5) * BITS + p] >> (pos & 31)) & 1u) << p;
-          zh[j] = lut[code];
-        }
-        nrm = __uint_as_float(r32[NWC]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) zh[j] = 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = zh[8 * c + 2 * e] * scale;
+        const float x1 = zh[8 * c + 2 * e + 1] * scale;
+        hi[e] = pack_bf16x2(x0, x1);
+        lo[e] = pack_bf16x2(x0 - __uint_as_float(hi[e] << 16), x1 - __uint_as_float(hi[e] & 0xFFFF0000u));
       }
-      fwht_vector<LPV>(zh, c);
-      const float scale = nrm * a.tab.inv_m;
-      uint32_t hi[8], lo[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = __uint_as_float(__float_as_uint(zh[j] * scale) ^ (((sbyte >> j) & 1u) << 31));
-        hi[j] = f32_to_bf16_rne(v);
-        lo[j] = f32_to_bf16_rne(v - __uint_as_float(hi[j] << 16));
-      }
-      uint4 h4 = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-      uint4 l4 = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
-      *reinterpret_cast<uint4*>(&vh[local * BS + 8 * c]) = h4;
-      *reinterpret_cast<uint4*>(&vl[local * BS + 8 * c]) = l4;
+      reg[swz<RCH>(ln, c)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      reg[swz<RCH>(ln, HCH + c)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
-    __syncthreads();
-    {
-      const int arow = 16 * wave + (lane & 15);
+    __builtin_amdgcn_wave_barrier();
+    uint4 bh[4][KS], bl[4][KS];  // B-operand fragments: row tile nt, k step ks
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int k0 = ks * 32 + 8 * (lane >> 4);
-          const uint4 bv = *reinterpret_cast<const uint4*>(&Bs[(t * 16 + (lane & 15)) * BS + k0]);
-          acc = mfma_bf16(*reinterpret_cast<const uint4*>(&vh[arow * BS + k0]), bv, acc);
-          acc = mfma_bf16(*reinterpret_cast<const uint4*>(&vl[arow * BS + k0]), bv, acc);
-        }
-        const int col = t * 16 + (lane & 15);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int row = 16 * nt + (ln & 15), ck = 4 * ks + (ln >> 4);
+        bh[nt][ks] = reg[swz<RCH>(row, ck)];
+        bl[nt][ks] = reg[swz<RCH>(row, HCH + ck)];
+      }
+    __builtin_amdgcn_wave_barrier();
+    uint32_t* reg32 = reinterpret_cast<uint32_t*>(reg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t vec = row0 + 16 * wave + 4 * (lane >> 4) + i;
-          if (vec < a.n) {
-            const float val = acc[i] + mu[col];
-            if constexpr (BF16)
-              static_cast<uint16_t*>(a.y)[vec * a.ld + col] = (uint16_t)f32_to_bf16_rne(val);
-            else
-              static_cast<float*>(a.y)[vec * a.ld + col] = val;
+    for (int oc = 0; oc < D / OCOLS; ++oc) {
+#pragma unroll
+      for (int mt = 0; mt < OCOLS / 16; ++mt) {
+        const int dl = 16 * mt + 4 * (ln >> 4);  // column within the staged chunk
+        const float4 m4 = *reinterpret_cast<const float4*>(mu + oc * OCOLS + dl);
+        const floatx4 init = floatx4{m4.x, m4.y, m4.z, m4.w};
+        uint4 af[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          af[ks] = s_B[swz<HCH>(oc * OCOLS + 16 * mt + (ln & 15), 4 * ks + (ln >> 4))];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          floatx4 acc = init;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            acc = mfma_bf16(af[ks], bh[nt][ks], acc);
+            acc = mfma_bf16(af[ks], bl[nt][ks], acc);
+          }
+          const int row = 16 * nt + (ln & 15);  // acc = out[row][d0 .. d0 + 3]
+          if constexpr (BF16) {
+            uint32_t* slot = reg32 + swz<RCH>(row, dl / 8) * 4 + 2 * ((dl / 4) & 1);
+            slot[0] = pack_bf16x2(acc[0], acc[1]);
+            slot[1] = pack_bf16x2(acc[2], acc[3]);
+          } else {
+            reg[swz<RCH>(row, dl / 4)] = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                                                    __float_as_uint(acc[2]), __float_as_uint(acc[3]));
           }
         }
       }
+      __builtin_amdgcn_wave_barrier();
+      uint4 out[CCH];
+#pragma unroll
+      for (int k = 0; k < CCH; ++k) {
+        const int id = k * 64 + ln, p = id / CCH, c = id % CCH;
+        out[k] = reg[swz<RCH>(p, c)];
+      }
+#pragma unroll
+      for (int k = 0; k < CCH; ++k) {
+        const int id = k * 64 + ln, p = id / CCH, c = id % CCH;
+        if (rw0 + p < a.n)
+          st_stream(static_cast<uint8_t*>(a.y) + ((rw0 + p) * a.ld + oc * OCOLS) * ES + 16 * c, out[k]);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// Launchers. Supported (D, r): r in {32, 64, 128}, r < D, D*r <= 32768.
+// Launchers. Supported (D, r): r in {32, 64, 128}, r <= D/2, D*r <= 32768.
 
-static int64_t pca_blocks(int64_t n) {
-  int64_t tiles = (n + kPcaTile - 1) / kPcaTile;
-  if (tiles > 8192) tiles = 8192;
-  return tiles < 1 ? 1 : tiles;
+// Blocks take consecutive tiles (consecutive tiles share a basis), as many as keeps the grid
+// within what the chip holds at once.
+struct PcaGrid {
+  unsigned blocks;
+  int64_t per_block;
+};
+
+template <int D, int R>
+static PcaGrid pca_grid(int64_t n) {
+  using P = PcaShape<D, R>;
+  const int64_t tiles = (n + P::ROWS - 1) / P::ROWS;
+  const int64_t resident = 256 * (160 * 1024 / (P::BASIS_BYTES + P::W * P::REGION_BYTES));
+  const int64_t per = (tiles + resident - 1) / resident;
+  return PcaGrid{(unsigned)((tiles + per - 1) / per), per};
 }
 
 template <int D, int R, int BITS, bool SYM>
 static hipError_t enc_t(const EncodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_encode_pca<D, R, BITS, SYM>), dim3((unsigned)pca_blocks(a.n)), dim3(256), 0, st, a);
+  const PcaGrid g = pca_grid<D, R>(a.n);
+  hipLaunchKernelGGL((k_encode_pca<D, R, BITS, SYM>), dim3(g.blocks), dim3(64 * PcaShape<D, R>::W), 0, st,
+                     a, g.per_block);
   return hipGetLastError();
 }
 
@@ -239,9 +358,10 @@ static hipError_t enc_dr(int bits, bool sym, const EncodeArgs& a, hipStream_t st
 
 template <int D, int R, int BITS>
 static hipError_t dec_t(bool bf16, const DecodeArgs& a, hipStream_t st) {
-  const dim3 g((unsigned)pca_blocks(a.n)), b(256);
-  if (bf16) hipLaunchKernelGGL((k_decode_pca<D, R, BITS, true>), g, b, 0, st, a);
-  else hipLaunchKernelGGL((k_decode_pca<D, R, BITS, false>), g, b, 0, st, a);
+  const PcaGrid pg = pca_grid<D, R>(a.n);
+  const dim3 g(pg.blocks), b(64 * PcaShape<D, R>::W);
+  if (bf16) hipLaunchKernelGGL((k_decode_pca<D, R, BITS, true>), g, b, 0, st, a, pg.per_block);
+  else hipLaunchKernelGGL((k_decode_pca<D, R, BITS, false>), g, b, 0, st, a, pg.per_block);
   return hipGetLastError();
 }
 
