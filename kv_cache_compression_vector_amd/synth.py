@@ -86,6 +86,26 @@ def student_t_heavy(layers=28, heads=8, tokens=8192, head_dim=128, df=3, frac=0.
     return out
 
 
+def v4_flash_layers(layers=43, tokens=65536, head_dim=512, seed=1003, device="cpu"):
+    """DeepSeek-V4-Flash-shaped K rows (one KV head per layer): yields one bf16
+    [tokens, head_dim] iid N(0,1) tensor per layer from a single seeded stream."""
+    g = _gen(seed, device)
+    for _ in range(layers):
+        yield torch.randn(tokens, head_dim, generator=g, device=device).to(torch.bfloat16)
+
+
+def long_context_keys(batch=8, kv_heads=8, tokens=131072, head_dim=128, heads_q=32,
+                      seed=1005, device="cpu"):
+    """Keys [batch, kv_heads, tokens, head_dim] and decode-step queries [batch, heads_q,
+    head_dim], both iid N(0,1) rounded to bf16 (keys drawn one batch row at a time)."""
+    g = _gen(seed, device)
+    k = torch.empty(batch, kv_heads, tokens, head_dim, dtype=torch.bfloat16, device=device)
+    for b in range(batch):
+        k[b] = torch.randn(kv_heads, tokens, head_dim, generator=g, device=device).to(torch.bfloat16)
+    q = torch.randn(batch, heads_q, head_dim, generator=g, device=device).to(torch.bfloat16)
+    return k, q
+
+
 def pca_basis_from_calibration(calib_bf16: torch.Tensor, rank: int):
     """Frozen PCA fit on a calibration slice [tokens, D] (bf16): the mean (f32 [D]) and the
     top-`rank` eigenvectors of the centred covariance, in descending eigenvalue order, each
