@@ -5,62 +5,170 @@
 // decoding every key [arc PR #98 / #94 kernel commit: attention reads packed K directly]. With
 // a projection, x^ = mu + B v^ gives q.x^ = q.mu + (n/r) sum_i q''_i z^_i, q'' = H_r(s (.) B^T q).
 // The query heads that share a KV head (GQA) are scored together so each record is read once.
+//
+// Work split: the products run on MFMA (v_mfma_f32_16x16x32_bf16) as S^T = Q' Z^T for tiles of
+// 16 heads (G <= 8 used) x 16 tokens x 32 coordinates. A = the rotated queries, split into bf16
+// hi + lo once per block; B = the dequantised keys: each lane expands 8 coordinates of one token
+// through a 2^(2b)-entry LDS table indexed by the bit pairs of two coordinates, whose entries are
+// the two centroids' bf16 hi pair and lo pair, i.e. MFMA operand words. hi*hi + hi*lo + lo*hi
+// keep ~2^-16 relative accuracy per product with f32 accumulation. A block takes a run of tokens
+// of one (batch, KV head), so the query preparation is paid once per run.
 #include "kvq_device.h"
 #include "kvq_kernels.h"
 
 namespace kvq {
 
 constexpr int kScoreThreads = 256;
+constexpr int kScoreSegment = 256;  // tokens per basis check (basis blocks are multiples of 256)
+constexpr int kScoreHeads = 8;      // query heads per KV head handled (MFMA rows 8..15 idle)
 
-// Rotated queries of the G (<= GMAX) heads of one (batch, kv head) into LDS, plane-position
-// order: qs[pos * GMAX + h], pos = (i mod 8) * (M/8) + i/8; heads h >= G are zero.
-// PCA: also qmu[h] = q . mu.
-template <int D, int M, int GMAX, bool PCA>
-__device__ __forceinline__ void rotate_queries(const ScoreArgs& a, int b, int kv, int G, int64_t row0,
-                                               float* qs, float* qf, float* uq, float* qmu) {
-  constexpr int LPV = M / 8;
-  constexpr int HPB = kScoreThreads / LPV;  // heads per pass
-  const int tid = threadIdx.x, c = tid % LPV;
-  const uint32_t sbyte = (a.tab.sign_words[(c >> 2) & 15] >> (8 * (c & 3))) & 0xFFu;
-  if constexpr (PCA) {
-    for (int e = tid; e < GMAX * D; e += kScoreThreads) {
-      const int h = e / D, d = e % D;
-      qf[e] = h < G ? __uint_as_float((uint32_t)a.q[b * a.q_sb + (int64_t)(kv * G + h) * a.q_sh + d] << 16)
-                    : 0.0f;
-    }
-    __syncthreads();
-    const int bi = basis_of_row(a.pca, row0);
-    const uint16_t* Bk = a.pca.basis + (int64_t)bi * D * M;
-    for (int e = tid; e < GMAX * M; e += kScoreThreads) {
-      const int h = e / M, j = e % M;
-      float u = 0.0f;
-      for (int d = 0; d < D; ++d) u = fmaf(__uint_as_float((uint32_t)Bk[d * M + j] << 16), qf[h * D + d], u);
-      uq[e] = u;
-    }
-    if (tid < GMAX) {
-      float s = 0.0f;
-      if (a.pca.mean) {
-        const float* mu = a.pca.mean + (int64_t)bi * D;
-        for (int d = 0; d < D; ++d) s = fmaf(mu[d], qf[tid * D + d], s);
-      }
-      qmu[tid] = s;
-    }
-    __syncthreads();
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4_t mfma16(const uint4& a, const uint4& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// bf16 hi + lo of an f32 (both round to nearest even): hi + lo = x to ~2^-17 relative.
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_rne(x);
+  lo = f32_to_bf16_rne(x - __uint_as_float(hi << 16));
+}
+
+// Pair-table index of the coordinates at bits sh + pr, sh + pr + 1 of the b plane words w:
+// bit 2p + i of the index = plane p of coordinate i. For b = 2, 3 the planes' bit pairs are
+// gathered into one word (byte p = plane p) and brought together by one 24-bit multiply:
+// with y = a + b 2^8 + c 2^16 (a, b, c < 4), y * (2^16 + 2^10 + 2^4) holds a + 4 b + 16 c in bits
+// 16..21 and nothing else reaches those bits or carries into them.
+template <int BITS>
+__device__ __forceinline__ uint32_t pair_index(const uint32_t* w, int sh, int pr) {
+  if constexpr (BITS == 1) {
+    return __builtin_amdgcn_ubfe(w[0], sh + pr, 2);
+  } else if constexpr (BITS == 2 || BITS == 3) {
+    uint32_t y = __builtin_amdgcn_ubfe(w[0], sh, 8) | (__builtin_amdgcn_ubfe(w[1], sh, 8) << 8);
+    if constexpr (BITS == 3) y |= __builtin_amdgcn_ubfe(w[2], sh, 8) << 16;
+    const uint32_t mask = (BITS == 3 ? 0x030303u : 0x0303u) << pr;
+    const uint32_t prod = __umul24(y & mask, BITS == 3 ? 0x10410u : 0x10400u);
+    return __builtin_amdgcn_ubfe(prod, 16 + pr, 2 * BITS);
+  } else {
+    uint32_t idx = 0;
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) idx |= __builtin_amdgcn_ubfe(w[p], sh + pr, 2) << (2 * p);
+    return idx;
   }
-  for (int h0 = 0; h0 < GMAX; h0 += HPB) {
+}
+
+// Rotated queries of heads [0, 8) of one (batch, kv head) into qs[h * M + pos] (plane-position
+// order pos = (i mod 8) * (M/8) + i/8; heads >= G are zero) and qmu[h] = q_h . mu (PCA).
+// Every thread of the block calls this; it synchronises.
+template <int D, int M, bool PCA>
+__device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int kv, int G, int bi,
+                                                float* qs, float* qmu, uint4* sBT, float* uq) {
+  constexpr int H = kScoreHeads;
+  constexpr int LPV = M / 8;
+  constexpr int HPB = kScoreThreads / LPV;  // heads per rotation pass
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint16_t* qb = a.q + b * a.q_sb + (int64_t)kv * G * a.q_sh;
+  if constexpr (PCA) {
+    // every global load of the prologue first (one memory round trip): the basis (16-byte
+    // pieces), wave 0 the query fragments, wave 1 the query and mean slices of q . mu
+    constexpr int BCH = D / 8, MASK = (BCH < 16 ? BCH : 16) - 1;
+    constexpr int NB = D * M / 8 / kScoreThreads;
+    const uint4* Bk = reinterpret_cast<const uint4*>(a.pca.basis + (int64_t)bi * D * M);
+    uint4 bl[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) bl[i] = Bk[tid + kScoreThreads * i];
+    const int h = lane & 15;
+    uint4 qf[D / 32];
+    if (tid < 64) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        qf[ks] = h < G ? *reinterpret_cast<const uint4*>(qb + (int64_t)h * a.q_sh + 32 * ks + 8 * (lane >> 4))
+                       : make_uint4(0, 0, 0, 0);
+    }
+    // q . mu: 8 lanes per head, D/8 consecutive coordinates each
+    const int hm = (tid - 64) / 8, lm = (tid - 64) % 8;
+    const bool mu_lane = tid >= 64 && tid < 64 + 8 * H && a.pca.mean && hm < G;
+    uint4 qm4[D / 64];
+    float4 mu4[D / 32];
+    if (mu_lane) {
+      const float* mu = a.pca.mean + (int64_t)bi * D + lm * (D / 8);
+      const uint16_t* qh = qb + (int64_t)hm * a.q_sh + lm * (D / 8);
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) qm4[i] = *reinterpret_cast<const uint4*>(qh + 8 * i);
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) mu4[i] = *reinterpret_cast<const float4*>(mu + 4 * i);
+    }
+    // basis transposed into LDS: sBT row j = basis column j (D bf16), chunk-swizzled
+    uint16_t* bt16 = reinterpret_cast<uint16_t*>(sBT);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int e = tid + kScoreThreads * i;
+      const int d = e / (M / 8), j0 = 8 * (e % (M / 8));
+      const uint32_t u[4] = {bl[i].x, bl[i].y, bl[i].z, bl[i].w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = j0 + k;
+        bt16[(j * BCH + ((d / 8) ^ (j & MASK))) * 8 + d % 8] = (uint16_t)(u[k / 2] >> (16 * (k & 1)));
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // uq^T = B^T q^T on MFMA: A = basis^T rows (16 columns j), B = query rows (16 heads)
+#pragma unroll
+      for (int nt = 0; nt < M / 16; ++nt) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+        const int j = 16 * nt + (lane & 15);
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const int ck = 4 * ks + (lane >> 4);
+          acc = mfma16(sBT[j * BCH + (ck ^ (j & MASK))], qf[ks], acc);
+        }
+        // acc[i] = uq[head lane % 16][j = 16 nt + 4 (lane / 16) + i]
+        if (h < H) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) uq[h * M + 16 * nt + 4 * (lane >> 4) + i] = acc[i];
+        }
+      }
+    } else if (tid < 64 + 8 * H) {
+      float s = 0.0f;
+      if (mu_lane) {
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+          const uint32_t w[4] = {qm4[i].x, qm4[i].y, qm4[i].z, qm4[i].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float4 m = mu4[2 * i + k / 2];
+            s = fmaf(bf16lo_to_f32(w[k]), (k & 1) ? m.z : m.x, s);
+            s = fmaf(bf16hi_to_f32(w[k]), (k & 1) ? m.w : m.y, s);
+          }
+        }
+      }
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      s += __shfl_xor(s, 4, 64);
+      if (lm == 0) qmu[hm] = s;
+    }
+    __syncthreads();
+  } else {
+    if (tid < H) qmu[tid] = 0.0f;
+  }
+  // s (.) v, then the M-point Hadamard transform, LPV lanes per head with 8 coordinates each
+  const int c = tid % LPV;
+  const uint32_t sbyte = (a.tab.sign_words[(c >> 2) & 15] >> (8 * (c & 3))) & 0xFFu;
+  for (int h0 = 0; h0 < H; h0 += HPB) {
     const int h = h0 + tid / LPV;
-    const bool active = h < G;
     float v[8];
     if constexpr (PCA) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float x = h < GMAX ? uq[h * M + 8 * c + j] : 0.0f;
+        const float x = h < H ? uq[h * M + 8 * c + j] : 0.0f;
         v[j] = __uint_as_float(__float_as_uint(x) ^ (((sbyte >> j) & 1u) << 31));
       }
     } else {
       uint4 raw = make_uint4(0, 0, 0, 0);
-      if (active)
-        raw = *reinterpret_cast<const uint4*>(a.q + b * a.q_sb + (int64_t)(kv * G + h) * a.q_sh + 8 * c);
+      if (h < G) raw = *reinterpret_cast<const uint4*>(qb + (int64_t)h * a.q_sh + 8 * c);
       const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -69,75 +177,185 @@ __device__ __forceinline__ void rotate_queries(const ScoreArgs& a, int b, int kv
       }
     }
     fwht_vector<LPV>(v, c);
-    if (h < GMAX) {
+    if (h < H) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qs[(j * LPV + c) * GMAX + h] = active ? v[j] : 0.0f;
+      for (int j = 0; j < 8; ++j) qs[h * M + j * LPV + c] = v[j];
     }
   }
-}
-
-template <int D, int M, int BITS, int GMAX, bool PCA>
-__global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a) {
-  constexpr int NWC = (M / 32) * BITS, NWT = NWC + 1;
-  __shared__ float qs[M * GMAX];
-  __shared__ float qf[PCA ? GMAX * D : 1];
-  __shared__ float uq[PCA ? GMAX * M : 1];
-  __shared__ float qmu[GMAX];
-  __shared__ float lut[16];
-  const int pair = blockIdx.y;
-  const int b = pair / a.Hkv, kv = pair % a.Hkv;
-  const int G = a.Hq / a.Hkv;
-  if (threadIdx.x < 16) lut[threadIdx.x] = a.tab.c[threadIdx.x];
-  if (!PCA && threadIdx.x < GMAX) qmu[threadIdx.x] = 0.0f;
-  const int64_t row0 = b * a.rec_sb + kv * a.rec_sh + (int64_t)blockIdx.x * kScoreThreads;
-  rotate_queries<D, M, GMAX, PCA>(a, b, kv, G, row0, qs, qf, uq, qmu);
   __syncthreads();
-  const int64_t t = (int64_t)blockIdx.x * kScoreThreads + threadIdx.x;
-  if (t >= a.T) return;
-  const uint32_t* r32 =
-      reinterpret_cast<const uint32_t*>(a.rec) + (b * a.rec_sb + kv * a.rec_sh + t) * NWT;
-  float acc[GMAX];
-#pragma unroll
-  for (int h = 0; h < GMAX; ++h) acc[h] = 0.0f;
-#pragma unroll
-  for (int g = 0; g < M / 32; ++g) {
-    uint32_t W[BITS];
-#pragma unroll
-    for (int p = 0; p < BITS; ++p) W[p] = r32[g * BITS + p];
-#pragma unroll 4
-    for (int jb = 0; jb < 32; ++jb) {
-      uint32_t code = 0;
-#pragma unroll
-      for (int p = 0; p < BITS; ++p) code |= ((W[p] >> jb) & 1u) << p;
-      const float cv = lut[code];
-      const float* qrow = qs + (32 * g + jb) * GMAX;
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h) acc[h] = fmaf(qrow[h], cv, acc[h]);
-    }
-  }
-  const float scale = __uint_as_float(r32[NWC]) * a.tab.inv_m;
-  float* srow = a.s + b * a.s_sb + t;
-#pragma unroll
-  for (int h = 0; h < GMAX; ++h)
-    if (h < G) srow[(int64_t)(kv * G + h) * a.s_sh] = fmaf(acc[h], scale, qmu[h]);
 }
 
 template <int D, int M, int BITS, bool PCA>
-static hipError_t launch_score_t(int group, const ScoreArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((a.T + kScoreThreads - 1) / kScoreThreads), (unsigned)(a.B * a.Hkv));
-  const dim3 blk(kScoreThreads);
-  if (group <= 4) hipLaunchKernelGGL((k_score<D, M, BITS, 4, PCA>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((k_score<D, M, BITS, 8, PCA>), grid, blk, 0, st, a);
+__global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t chunk,
+                                                         int64_t chunks_per_pair) {
+  constexpr int H = kScoreHeads;
+  constexpr int KS = M / 32;              // MFMA k-steps (one 32-coordinate word group each)
+  constexpr int NWC = KS * BITS, NWT = NWC + 1;
+  constexpr int NPAIR = 1 << (2 * BITS);  // pair-table entries
+  // tiles in flight per wave: as many 16-token record tiles as fit ~64 registers (1 .. 7)
+  constexpr int P = (64 / NWT - 1) < 1 ? 1 : ((64 / NWT - 1) > 7 ? 7 : (64 / NWT - 1));
+  constexpr int R = P + 1;
+  __shared__ __attribute__((aligned(16))) float qs[H * M];
+  __shared__ float qmu[H];
+  __shared__ uint32_t lut_hi[NPAIR], lut_lo[NPAIR];
+  __shared__ uint4 sBT[PCA ? D * M / 8 : 1];
+  __shared__ float uq[PCA ? H * M : 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tok = lane & 15, oct = lane >> 4;
+  const int64_t pair = blockIdx.x / chunks_per_pair;
+  const int b = (int)(pair / a.Hkv), kv = (int)(pair % a.Hkv);
+  const int G = a.Hq / a.Hkv;
+  const int64_t t_begin = (blockIdx.x % chunks_per_pair) * chunk;
+  const int64_t t_end = t_begin + chunk < a.T ? t_begin + chunk : a.T;
+  const int64_t rowbase = b * a.rec_sb + kv * a.rec_sh;
+  // pair table: entry e holds the centroids of code_a (bits 2p of e) and code_b (bits 2p+1)
+  for (int e = tid; e < NPAIR; e += kScoreThreads) {
+    uint32_t ca = 0, cb = 0;
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) {
+      ca |= ((e >> (2 * p)) & 1u) << p;
+      cb |= ((e >> (2 * p + 1)) & 1u) << p;
+    }
+    float va = 0.0f, vb = 0.0f;
+#pragma unroll
+    for (int k = 0; k < (1 << BITS); ++k) {
+      va = (uint32_t)k == ca ? a.tab.c[k] : va;
+      vb = (uint32_t)k == cb ? a.tab.c[k] : vb;
+    }
+    uint32_t ha, la, hb, lb;
+    split_bf16(va, ha, la);
+    split_bf16(vb, hb, lb);
+    lut_hi[e] = ha | (hb << 16);
+    lut_lo[e] = la | (lb << 16);
+  }
+  uint4 qa_hi[KS], qa_lo[KS];  // A operand: head tok, coordinates 32 ks + 8 oct .. + 7
+  float qm[4];
+  int cur = -1;
+  // Tiles of 16 tokens: tile j of this wave covers tokens t_begin + 64 j + 16 wave + [0, 16);
+  // four tiles per wave make a 256-token segment (one basis). R = P + 1 record slots form a
+  // ring: while tile j computes, tiles j + 1 .. j + P are in flight.
+  const int64_t n_tiles = ((t_end - t_begin + kScoreSegment - 1) / kScoreSegment) * 4;
+  auto load_tile = [&](int64_t j, uint32_t (&w)[NWT]) {
+    const int64_t t = t_begin + 64 * j + 16 * wave + tok;
+    const int64_t se = t_begin + kScoreSegment * (j / 4 + 1);
+    const int64_t te = se < t_end ? se : t_end;
+    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(a.rec) +
+                          (rowbase + (t < te ? t : te - 1)) * NWT;
+#pragma unroll
+    for (int k = 0; k < NWT; ++k) w[k] = r32[k];
+  };
+  uint32_t ring[R][NWT];
+#pragma unroll
+  for (int r = 0; r < P; ++r)
+    if (r < n_tiles) load_tile(r, ring[r]);
+  for (int64_t j0 = 0; j0 < n_tiles; j0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t j = j0 + r;
+      if (j >= n_tiles) break;  // uniform
+      if (j % 4 == 0) {
+        const int bi = PCA ? basis_of_row(a.pca, rowbase + t_begin + 64 * j) : 0;
+        if (bi != cur) {  // block-uniform
+          __syncthreads();
+          prepare_queries<D, M, PCA>(a, b, kv, G, bi, qs, qmu, sBT, uq);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            uint32_t hi[8], lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = tok < H ? qs[tok * M + 32 * ks + 8 * oct + e] : 0.0f;
+              split_bf16(x, hi[e], lo[e]);
+            }
+            qa_hi[ks] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                   hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+            qa_lo[ks] = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                                   lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) qm[k] = 4 * oct + k < H ? qmu[4 * oct + k] : 0.0f;
+          cur = bi;
+        }
+      }
+      if (j + P < n_tiles) load_tile(j + P, ring[(r + P) % R]);
+      const uint32_t (&w)[NWT] = ring[r];
+      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint32_t zh[4], zl[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          const uint32_t idx = pair_index<BITS>(w + ks * BITS, 8 * oct, 2 * pr);
+          zh[pr] = lut_hi[idx];
+          zl[pr] = lut_lo[idx];
+        }
+        const uint4 bh = make_uint4(zh[0], zh[1], zh[2], zh[3]);
+        const uint4 blo = make_uint4(zl[0], zl[1], zl[2], zl[3]);
+        acc = mfma16(qa_hi[ks], bh, acc);
+        acc = mfma16(qa_hi[ks], blo, acc);
+        acc = mfma16(qa_lo[ks], bh, acc);
+      }
+      // acc[k] = sum for head 4 oct + k, token t
+      const int64_t t = t_begin + 64 * j + 16 * wave + tok;
+      const int64_t se = t_begin + kScoreSegment * (j / 4 + 1);
+      const float scale = __uint_as_float(w[NWC]) * a.tab.inv_m;
+      float* srow = a.s + b * a.s_sb + t;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int h = 4 * oct + k;
+        if (t < se && t < t_end && h < G) srow[(int64_t)(kv * G + h) * a.s_sh] = fmaf(acc[k], scale, qm[k]);
+      }
+    }
+  }
+}
+
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Launch: one round of resident blocks. Each (batch, KV head) pair is split into as many token
+// chunks (multiples of the 256-token segment) as the chip holds blocks per pair, so every
+// block pays the query preparation once over the longest possible run of tokens.
+template <int D, int M, int BITS, bool PCA>
+static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t st) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_score<D, M, BITS, PCA>, kScoreThreads, 0) !=
+            hipSuccess || nb <= 0)
+      nb = 1;
+    per_cu = nb;
+  }
+  const int64_t pairs = (int64_t)a.B * a.Hkv;
+  const int64_t segs = (a.T + kScoreSegment - 1) / kScoreSegment;
+  int64_t cpp = ((int64_t)per_cu * device_cus()) / pairs;
+  if (cpp > segs) cpp = segs;
+  if (cpp < 1) cpp = 1;
+  const int64_t chunk = ((segs + cpp - 1) / cpp) * kScoreSegment;
+  const int64_t chunks = (a.T + chunk - 1) / chunk;
+  const int64_t blocks = chunks * pairs;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_score<D, M, BITS, PCA>), dim3((unsigned)blocks), dim3(kScoreThreads), 0, st,
+                     a, chunk, chunks);
   return hipGetLastError();
 }
 
 template <int D, int M, bool PCA>
-static hipError_t launch_score_dm(int bits, int group, const ScoreArgs& a, hipStream_t st) {
+static hipError_t launch_score_dm(int bits, const ScoreArgs& a, hipStream_t st) {
   switch (bits) {
-    case 1: return launch_score_t<D, M, 1, PCA>(group, a, st);
-    case 2: return launch_score_t<D, M, 2, PCA>(group, a, st);
-    case 3: return launch_score_t<D, M, 3, PCA>(group, a, st);
-    case 4: return launch_score_t<D, M, 4, PCA>(group, a, st);
+    case 1: return launch_score_t<D, M, 1, PCA>(a, st);
+    case 2: return launch_score_t<D, M, 2, PCA>(a, st);
+    case 3: return launch_score_t<D, M, 3, PCA>(a, st);
+    case 4: return launch_score_t<D, M, 4, PCA>(a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -147,15 +365,15 @@ hipError_t launch_score(int D, int m, int bits, int group, const ScoreArgs& a, h
   if (group < 1 || group > 8) return hipErrorInvalidValue;
   if (D == m) {
     switch (m) {
-      case 64: return launch_score_dm<64, 64, false>(bits, group, a, st);
-      case 128: return launch_score_dm<128, 128, false>(bits, group, a, st);
-      case 256: return launch_score_dm<256, 256, false>(bits, group, a, st);
-      case 512: return launch_score_dm<512, 512, false>(bits, group, a, st);
+      case 64: return launch_score_dm<64, 64, false>(bits, a, st);
+      case 128: return launch_score_dm<128, 128, false>(bits, a, st);
+      case 256: return launch_score_dm<256, 256, false>(bits, a, st);
+      case 512: return launch_score_dm<512, 512, false>(bits, a, st);
     }
     return hipErrorInvalidValue;
   }
 #define KVQ_CASE(d, r) \
-  if (D == d && m == r) return launch_score_dm<d, r, true>(bits, group, a, st);
+  if (D == d && m == r) return launch_score_dm<d, r, true>(bits, a, st);
   KVQ_CASE(64, 32) KVQ_CASE(128, 32) KVQ_CASE(128, 64) KVQ_CASE(256, 32) KVQ_CASE(256, 64)
   KVQ_CASE(256, 128) KVQ_CASE(512, 32) KVQ_CASE(512, 64)
 #undef KVQ_CASE
