@@ -14,8 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 OBJ = os.path.join(HERE, "_obj")
-SOURCES = ["kvq_host.cpp", "kvq_encode.hip", "kvq_decode.hip", "kvq_score.hip", "kvq_pca.hip",
-           "kvq_misc.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_encode.hip", "kvq_encode_mx.hip", "kvq_decode.hip", "kvq_score.hip",
+           "kvq_pca.hip", "kvq_misc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed f32 VALU instructions are disabled for all device code: the plain f32 forms are used.
@@ -23,11 +23,16 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-gpu-rdc"]
 
 
+# Per-source extras. The rotation kernels keep MFMA results in architectural VGPRs (the
+# quantiser reads every one of them; accumulator registers would cost a move each).
+EXTRA = {"kvq_encode_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c"] + (["-x", "hip"] if src.endswith(".cpp") else []) + \
-          [path, "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c"] + \
+          (["-x", "hip"] if src.endswith(".cpp") else []) + [path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

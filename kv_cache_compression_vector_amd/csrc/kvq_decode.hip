@@ -27,15 +27,35 @@ void k_decode_lv(DecodeArgs a) {
   const int q = lane % L::Q, vw = lane / L::Q;
   uint4* tile = s_tile + (BF16 ? wave * St::WORDS : 0);
   const int64_t n_iter = (a.n + L::VPW - 1) / L::VPW;
-  for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < n_iter; it += (int64_t)gridDim.x * 4) {
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  // lanes past the end decode the last record (their rows are not stored): the wave stays
+  // whole for the staged store and the quad exchanges
+  auto rec_of = [&](int64_t it) {
     const int64_t vec = it * L::VPW + vw;
-    // lanes past the end decode the last record (their rows are not stored): the wave stays
-    // whole for the staged store and the quad exchanges
-    const int64_t src = vec < a.n ? vec : a.n - 1;
-    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(a.rec) + src * NWT;
+    return reinterpret_cast<const uint32_t*>(a.rec) + (vec < a.n ? vec : a.n - 1) * NWT;
+  };
+  // one lane per vector: the next iteration's record is loaded while this one computes
+  uint32_t wn[L::Q == 1 ? NWT : 1];
+  const int64_t it0 = (int64_t)blockIdx.x * 4 + wave;
+  if constexpr (L::Q == 1) {
+    if (it0 < n_iter) load_words<NWT>(rec_of(it0), wn);
+  }
+  for (int64_t it = it0; it < n_iter; it += stride) {
+    const int64_t vec = it * L::VPW + vw;
     float zh[L::K];
-    unpack_lookup_lv<M, BITS>(r32, q, LdsLut{lut}, zh);
-    const float scale = __uint_as_float(r32[NWC]) * a.tab.inv_m;
+    float scale;
+    if constexpr (L::Q == 1) {
+      uint32_t w[NWC];
+#pragma unroll
+      for (int i = 0; i < NWC; ++i) w[i] = wn[i];
+      scale = __uint_as_float(wn[NWC]) * a.tab.inv_m;
+      if (it + stride < n_iter) load_words<NWT>(rec_of(it + stride), wn);
+      unpack_lookup_words<M, BITS>(w, LdsLut{lut}, zh);
+    } else {
+      const uint32_t* r32 = rec_of(it);
+      unpack_lookup_lv<M, BITS>(r32, q, LdsLut{lut}, zh);
+      scale = __uint_as_float(r32[NWC]) * a.tab.inv_m;
+    }
     fwht_regs<L::K>(zh);
     fwht_cross<L::Q, L::K>(zh, q);
     const uint32_t* sm = part_signs<M>(a.tab, s_sign, q);

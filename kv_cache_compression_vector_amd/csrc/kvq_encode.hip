@@ -346,6 +346,7 @@ static hipError_t launch_encode_m(int bits, bool sym, const EncodeArgs& a, hipSt
 }
 
 hipError_t launch_encode(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
+  if (encode_mx_supported(m)) return launch_encode_mx(m, bits, sym, a, st);
   switch (m) {
     case 32: return launch_encode_m<32>(bits, sym, a, st);
     case 64: return launch_encode_m<64>(bits, sym, a, st);

@@ -1,0 +1,224 @@
+// kvq_encode_mx.hip — Hadamard-path encode with the rotation on the matrix cores (m <= 128).
+//
+// u = H_m (s (.) x) [kakeyaturbo PR #15, "M4 Phase A": rotate = H.D.x; "M4 Phase B": the rotation
+// as a dense product on the tensor cores] is formed as U = X Bm with Bm = diag(s) H_m (entries
+// +-1, exact in bf16; x is bf16, so every product is exact and sums in f32). The in-register
+// butterfly would cost log2(m) adds per coordinate on the vector ALUs, which bind first on this
+// chip; the product costs them nothing.
+//
+// Output columns are permuted: lane column c of n-tile nt receives coordinate
+// j = pi^-1(NT c + nt), pi the record's plane position, so each lane holds NT consecutive plane
+// positions of each of its rows. The quantiser (kvq_lanevec.h) then builds NT-bit fields per
+// plane in registers, and LPW = 32/NT lanes OR their fields into a record word over DPP.
+//
+// Per wave: 16-row tiles staged through a swizzled LDS region with 1 KB-contiguous loads, the
+// next tile's loads in flight while the current one computes. A block of 8 waves shares the
+// staged rotation, so two blocks (16 waves) fit a CU: enough bytes in flight to stream HBM.
+// Norms come from bf16 dot products of the staged rows.
+#include "kvq_device.h"
+#include "kvq_kernels.h"
+#include "kvq_lanevec.h"
+#include "kvq_mfma.h"
+
+namespace kvq {
+
+template <int M>
+struct MX {
+  static constexpr int NT = M / 16;    // n-tiles = coordinates per lane per row
+  static constexpr int KS = M / 32;    // k-steps
+  static constexpr int LPW = 32 / NT;  // lanes per record word
+  static constexpr int ROWS = 16;      // rows per wave tile
+  static constexpr int RT = ROWS / 16; // MFMA row tiles per wave tile
+  static constexpr int RCH = M / 8;    // staged row, 16-byte chunks
+  static constexpr int WAVES = 8;     // waves per block, sharing the staged rotation
+  static constexpr int LDS = M * M * 2 + WAVES * ROWS * RCH * 16;
+};
+
+// B fragment (ks, nt) of lane l: k = 32 ks + 8 (l / 16) + e, column j = pi^-1(NT (l % 16) + nt);
+// entry e = s_k (-1)^popcount(k & j) as bf16.
+template <int M>
+__device__ __forceinline__ uint4 rotation_fragment(const Tables& tab, int ks, int nt, int l) {
+  constexpr int NT = MX<M>::NT;
+  const int j = coord_at(NT * (l & 15) + nt, M);
+  uint32_t w[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int k = 32 * ks + 8 * (l >> 4) + 2 * h + q;
+      const uint32_t s = (tab.sign_pairs[k >> 1] >> (16 * (k & 1))) & 0x8000u;  // s_k = -1
+      const uint32_t par = (uint32_t)(__builtin_popcount(k & j) & 1) << 15;
+      v |= (0x3F80u | (s ^ par)) << (16 * q);
+    }
+    w[h] = v;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int M, int BITS, bool SYM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+void k_encode_mx(EncodeArgs a, int64_t tiles_per_block) {
+  using X = MX<M>;
+  constexpr int NT = X::NT, KS = X::KS, LPW = X::LPW, RT = X::RT, RCH = X::RCH;
+  constexpr int ROWS = X::ROWS, NWC = (M / 32) * BITS, NWT = NWC + 1;
+  constexpr int TILE = X::WAVES * ROWS;
+  __shared__ uint4 sB[KS * NT * 64];
+  __shared__ uint4 s_reg[X::WAVES * ROWS * RCH];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int f = tid; f < KS * NT * 64; f += 64 * X::WAVES)
+    sB[f] = rotation_fragment<M>(a.tab, f / (NT * 64), (f / 64) % NT, f % 64);
+  __syncthreads();
+  uint4* reg = s_reg + wave * ROWS * RCH;
+  const int64_t n_tiles = (a.n + TILE - 1) / TILE;
+  const int64_t t0 = blockIdx.x * tiles_per_block;
+  const int64_t t1 = t0 + tiles_per_block < n_tiles ? t0 + tiles_per_block : n_tiles;
+  constexpr int PER = ROWS * RCH / 64;  // 16-byte input pieces per lane and tile
+  // rows of a tile, 1 KB-contiguous per instruction (rows past the end repeat the last row)
+  auto load_tile = [&](int64_t tile, uint4 (&in)[PER]) {
+    const int64_t rw = tile * TILE + ROWS * wave;
+    const int l = opaque_lane();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int id = k * 64 + l, p = id / RCH, ch = id % RCH;
+      const int64_t row = rw + p < a.n ? rw + p : a.n - 1;
+      in[k] = ld_stream(reinterpret_cast<const uint4*>(a.x + row * a.ld) + ch);
+    }
+  };
+  uint4 nxt[PER];
+  if (t0 < t1) load_tile(t0, nxt);
+  for (int64_t tile = t0; tile < t1; ++tile) {
+    const int64_t rw0 = tile * TILE + ROWS * wave;
+    const int ln = opaque_lane();
+    const int c = ln & 15, grp = ln >> 4;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int id = k * 64 + ln, p = id / RCH, ch = id % RCH;
+      reg[swz<RCH>(p, ch)] = nxt[k];
+    }
+    if (tile + 1 < t1) load_tile(tile + 1, nxt);  // in flight while this tile computes
+    __builtin_amdgcn_wave_barrier();
+    uint4 A[RT][KS];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) A[rt][ks] = reg[swz<RCH>(16 * rt + c, 4 * ks + grp)];
+    __builtin_amdgcn_wave_barrier();
+    // norms: row 16 rt + c from this lane's chunks, summed over the 4 lane groups, then moved to
+    // the accumulator layout (rows 16 rt + 4 grp + i)
+    float nC[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t w[4] = {A[rt][ks].x, A[rt][ks].y, A[rt][ks].z, A[rt][ks].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]),
+                                               __builtin_bit_cast(bf16x2_t, w[e]), ss, false);
+      }
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      const float nr = sqrtf(ss);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nC[rt][i] = __shfl(nr, 4 * grp + i, 64);
+    }
+    // rotation
+    floatx4 acc[RT][NT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 bfrag = sB[(ks * NT + nt) * 64 + ln];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = mfma_bf16(A[rt][ks], bfrag, acc[rt][nt]);
+      }
+    // quantise this lane's NT plane positions per row, join LPW lanes per word, and collect
+    // the tile's records in the (now free) LDS region
+    const int e = c % LPW, g = c / LPW;
+    uint32_t* rec_lds = reinterpret_cast<uint32_t*>(reg);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * grp + i;
+        const float n = nC[rt][i];
+        const Quant<BITS, SYM> q(a.tab, n);
+        QuantAcc<BITS, SYM> qa;
+#pragma unroll
+        for (int nt = NT - 1; nt >= 0; --nt) qa.push(acc[rt][nt][i], q);
+        uint32_t pl[BITS];
+        qa.planes(q, (1u << NT) - 1u, pl);
+        uint32_t mine = 0;
+#pragma unroll
+        for (int p = 0; p < BITS; ++p) {
+          const uint32_t wd = group_or<LPW>(pl[p] << (NT * e));
+          mine = (e == p) ? wd : mine;
+        }
+        if (e < BITS) rec_lds[r * NWT + g * BITS + e] = mine;
+        if (c == 0) rec_lds[r * NWT + NWC] = __float_as_uint(n);
+      }
+    __builtin_amdgcn_wave_barrier();
+    // the tile's records are contiguous (and 16-byte aligned) in memory: coalesced stores
+    {
+      constexpr int CH = ROWS * NWT / 4;  // 16-byte pieces
+      const int64_t valid_rows = a.n - rw0 < ROWS ? a.n - rw0 : ROWS;
+      const int64_t valid_ch = (valid_rows * NWT) / 4;  // whole pieces of valid records
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(a.rec) + rw0 * NWT);
+      const uint4* src = reinterpret_cast<const uint4*>(rec_lds);
+#pragma unroll
+      for (int k = 0; k < (CH + 63) / 64; ++k) {
+        const int id = k * 64 + ln;
+        if (id < CH && id < valid_ch) st_stream(dst + id, src[id]);
+      }
+      // a partial last piece (only when the tile ends inside it): its words one by one
+      const int64_t tail_w = valid_rows * NWT - valid_ch * 4;
+      if (ln < tail_w)
+        reinterpret_cast<uint32_t*>(a.rec)[(rw0 * NWT) + valid_ch * 4 + ln] = rec_lds[valid_ch * 4 + ln];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int M, int BITS, bool SYM>
+static hipError_t launch_mx_t(const EncodeArgs& a, hipStream_t st) {
+  constexpr int TILE = MX<M>::WAVES * MX<M>::ROWS;
+  const int64_t tiles = (a.n + TILE - 1) / TILE;
+  const int64_t resident = 256 * (160 * 1024 / MX<M>::LDS);
+  const int64_t per = (tiles + resident - 1) / resident;
+  const int64_t blocks = (tiles + per - 1) / per;
+  hipLaunchKernelGGL((k_encode_mx<M, BITS, SYM>), dim3((unsigned)blocks), dim3(64 * MX<M>::WAVES), 0,
+                     st, a, per);
+  return hipGetLastError();
+}
+
+template <int M>
+static hipError_t launch_mx_m(int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
+  switch (bits * 2 + (sym ? 1 : 0)) {
+    case 2: return launch_mx_t<M, 1, false>(a, st);
+    case 3: return launch_mx_t<M, 1, true>(a, st);
+    case 4: return launch_mx_t<M, 2, false>(a, st);
+    case 5: return launch_mx_t<M, 2, true>(a, st);
+    case 6: return launch_mx_t<M, 3, false>(a, st);
+    case 7: return launch_mx_t<M, 3, true>(a, st);
+    case 8: return launch_mx_t<M, 4, false>(a, st);
+    case 9: return launch_mx_t<M, 4, true>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool encode_mx_supported(int m) { return m == 64 || m == 128; }
+
+hipError_t launch_encode_mx(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  if (m == 64) return launch_mx_m<64>(bits, sym, a, st);
+  if (m == 128) return launch_mx_m<128>(bits, sym, a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

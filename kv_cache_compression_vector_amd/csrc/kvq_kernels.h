@@ -89,6 +89,9 @@ struct TailCopyArgs {
 };
 
 hipError_t launch_encode(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
+// Rotation on the matrix cores (coded length 64 or 128, no outlier list).
+bool encode_mx_supported(int m);
+hipError_t launch_encode_mx(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
 hipError_t launch_encode_outliers(int m, int bits, bool sym, const EncodeArgs& a,
                                   int64_t n_tiles, hipStream_t st);
 int64_t encode_outlier_tile_vectors(int m);

@@ -439,6 +439,20 @@ struct LaneLut {
   }
 };
 
+// Q == 1 with the record's code words already in registers (lets a caller load them early).
+template <int M, int BITS, class Lut>
+__device__ __forceinline__ void unpack_lookup_words(const uint32_t (&w)[(M / 32) * BITS],
+                                                    const Lut& lut, float (&zh)[M]) {
+#pragma unroll
+  for (int k = 0; k < M; ++k) {
+    const int pos = plane_pos(k, M);
+    uint32_t code = 0;
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) code |= ((w[(pos >> 5) * BITS + p] >> (pos & 31)) & 1u) << p;
+    zh[k] = lut(code);
+  }
+}
+
 // Codes of this lane part's K coordinates looked up in the centroid table lut.
 //  Q == 1: words = the whole record's code words. Q > 1: words g as laid out above.
 template <int M, int BITS, class Lut>

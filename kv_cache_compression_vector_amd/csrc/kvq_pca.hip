@@ -21,11 +21,10 @@
 #include "kvq_device.h"
 #include "kvq_kernels.h"
 #include "kvq_lanevec.h"
+#include "kvq_mfma.h"
 
 namespace kvq {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // Per-shape constants. Input (encode) and output (decode) rows move through LDS in column
 // chunks of 256 bytes: 128 bf16 (or 64 f32) columns, the whole row when it is shorter.
@@ -43,26 +42,6 @@ struct PcaShape {
 // Mean used when a codec gives none (read only).
 __device__ const float kZeroMean[512] = {};
 
-__device__ __forceinline__ floatx4 mfma_bf16(const uint4& a, const uint4& b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// 16-byte chunk c of row r in a tile whose rows are CH chunks apart, XOR-swizzled so that 16
-// lanes reading one chunk column (or one row each) hit distinct banks.
-template <int CH>
-__device__ __forceinline__ int swz(int r, int c) {
-  constexpr int mask = (CH < 16 ? CH : 16) - 1;
-  return r * CH + (c ^ (r & mask));
-}
-
-// The lane index as a value the compiler cannot see through: addresses derived from it inside a
-// tile loop are recomputed each tile instead of being hoisted out of the loop (and spilled).
-__device__ __forceinline__ int opaque_lane() {
-  int l = __lane_id();
-  asm volatile("" : "+v"(l));
-  return l;
-}
 
 // ------------------------------------------------------------------------------------------
 // Encode. The random signs are folded into the staged basis (column j of B times s_j, exact
@@ -214,6 +193,13 @@ void k_decode_pca(DecodeArgs a, int64_t tiles_per_block) {
   const int64_t n_tiles = (a.n + P::ROWS - 1) / P::ROWS;
   const int64_t t0 = blockIdx.x * tiles_per_block;
   const int64_t t1 = t0 + tiles_per_block < n_tiles ? t0 + tiles_per_block : n_tiles;
+  // lanes past the end decode the last record (their rows are not stored)
+  auto rec_of = [&](int64_t tile) {
+    const int64_t vec = tile * P::ROWS + 64 * wave + opaque_lane();
+    return reinterpret_cast<const uint32_t*>(a.rec) + (vec < a.n ? vec : a.n - 1) * NWT;
+  };
+  uint32_t wn[NWT];
+  if (t0 < t1) load_words<NWT>(rec_of(t0), wn);
   for (int64_t tile = t0; tile < t1; ++tile) {
     const int64_t row0 = tile * P::ROWS;
     const int bi = basis_of_row(a.pca, row0);
@@ -233,12 +219,13 @@ void k_decode_pca(DecodeArgs a, int64_t tiles_per_block) {
     }
     const int64_t rw0 = row0 + 64 * wave;
     const int ln = opaque_lane();
-    const int64_t vec = rw0 + ln;
-    const int64_t src = vec < a.n ? vec : a.n - 1;  // lanes past the end decode the last record
-    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(a.rec) + src * NWT;
+    uint32_t w[NWC];
+#pragma unroll
+    for (int i = 0; i < NWC; ++i) w[i] = wn[i];
+    const float scale = __uint_as_float(wn[NWC]) * a.tab.inv_m;
+    if (tile + 1 < t1) load_words<NWT>(rec_of(tile + 1), wn);  // in flight during this tile
     float zh[R];
-    unpack_lookup_lv<R, BITS>(r32, 0, lut, zh);
-    const float scale = __uint_as_float(r32[NWC]) * a.tab.inv_m;
+    unpack_lookup_words<R, BITS>(w, lut, zh);
     fwht_regs<R>(zh);
     // scale * (H z^) as bf16 hi | lo halves of the lane's region row (the signs s are in s_B)
 #pragma unroll
