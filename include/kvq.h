@@ -127,7 +127,8 @@ typedef struct kvq_cache {
 /* Bytes of one record for this codec: m*b/8 + 4. Returns 0 for an invalid codec. */
 size_t kvq_record_bytes(const kvq_codec* codec);
 
-/* Workspace bytes kvq_encode needs for n vectors when codec->outlier_T > 0 (0 otherwise). */
+/* Workspace bytes kvq_encode needs for n vectors when codec->outlier_T > 0 (0 otherwise): the
+ * block sums of the scan that turns per-vector outlier counts into CSR offsets. */
 size_t kvq_encode_workspace_bytes(const kvq_codec* codec, int64_t n);
 
 /* Host copies of the tables the kernels use, for inspection and tests: centroids f32[2^b],
@@ -140,6 +141,8 @@ kvq_status kvq_codec_tables(const kvq_codec* codec, float* centroids_host, float
  * records_dev: n records. ol: required iff codec->outlier_T > 0, else must be NULL.
  * ol_total_host: optional; when non-NULL the call synchronises the stream, stores the total
  * outlier count and returns KVQ_E_CAPACITY if it exceeds ol->capacity.
+ * With an outlier list the work is three kernels on the stream: records + per-vector counts
+ * (into offsets_dev), an exclusive scan of the counts in place, then the entries.
  * [kakeyaturbo PR #15, commits "M4 Phase A", "M4 Phase B"; arc PR #98, "What landed"] */
 kvq_status kvq_encode(const kvq_codec* codec, const void* x_dev, int64_t n, int64_t ld_x,
                       void* records_dev, const kvq_outliers* ol, int64_t* ol_total_host,

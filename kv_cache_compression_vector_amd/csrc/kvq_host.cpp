@@ -225,9 +225,7 @@ size_t kvq_encode_workspace_bytes(const kvq_codec* codec, int64_t n) {
   Resolved r;
   if (resolve_codec(codec, r) != KVQ_OK || n < 0) return 0;
   if (!r.outliers) return 0;
-  const int64_t tile = kvq::encode_outlier_tile_vectors(r.m);
-  const int64_t tiles = (n + tile - 1) / tile;
-  return (size_t)(16 + 8 * tiles);
+  return (size_t)(16 + 4 * kvq::scan_partials(n));
 }
 
 kvq_status kvq_codec_tables(const kvq_codec* codec, float* centroids_host,
@@ -283,33 +281,25 @@ kvq_status kvq_encode(const kvq_codec* codec, const void* x_dev, int64_t n, int6
     if (r.pca) return from_hip(kvq::launch_encode_pca(r.D, r.m, r.bits, r.sym, a, s), "encode_pca");
     return from_hip(kvq::launch_encode(r.m, r.bits, r.sym, a, s), "encode");
   }
-  // outlier path: tiles + decoupled look-back over a caller workspace
-  const int64_t tile = kvq::encode_outlier_tile_vectors(r.m);
-  const int64_t n_tiles = (n + tile - 1) / tile;
+  // outlier path: encode + counts, scan of the counts into offsets, entries
   uint32_t* ws = static_cast<uint32_t*>(ol->workspace_dev);
-  a.ws_ticket = ws;
-  a.ws_error = ws + 1;
-  a.ws_status = reinterpret_cast<uint64_t*>(ws + 4);
   a.ol_off = ol->offsets_dev;
   a.ol_idx = ol->idx_dev;
   a.ol_val = ol->val_dev;
   a.ol_cap = ol->capacity;
-  hipError_t e = kvq::launch_clear_u32(ws, 4 + 2 * n_tiles, s);
-  if (e != hipSuccess) return from_hip(e, "encode workspace clear");
+  hipError_t e;
   if (n == 0) {
-    e = hipMemcpyAsync(ol->offsets_dev, ws, sizeof(uint32_t), hipMemcpyDeviceToDevice, s);
+    e = kvq::launch_clear_u32(ol->offsets_dev, 1, s);  // offsets[0] = 0
   } else {
-    e = kvq::launch_encode_outliers(r.m, r.bits, r.sym, a, n_tiles, s);
+    e = kvq::launch_encode_outliers3(r.m, r.bits, r.sym, a, ws + 4, s);
   }
   if (e != hipSuccess) return from_hip(e, "encode_outliers");
   if (ol_total_host) {
-    uint32_t tot = 0, err = 0;
+    uint32_t tot = 0;
     e = hipMemcpyAsync(&tot, ol->offsets_dev + n, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipMemcpyAsync(&err, ws + 1, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return from_hip(e, "encode outlier total");
     *ol_total_host = tot;
-    if (err) return fail(KVQ_E_DEVICE, "outlier prefix scan gave up waiting (error word %u)", err);
     if ((int64_t)tot > ol->capacity)
       return fail(KVQ_E_CAPACITY, "outlier count %u exceeds capacity %lld", tot, (long long)ol->capacity);
   }

@@ -19,9 +19,6 @@ struct EncodeArgs {
   uint8_t* ol_idx;
   uint16_t* ol_val;
   int64_t ol_cap;
-  uint64_t* ws_status;      // one status word per tile
-  uint32_t* ws_ticket;      // tile ticket counter
-  uint32_t* ws_error;       // set when a look-back wait gave up
   // PCA projection (PCA kernels only)
   Basis pca;                // PCA kernels only
 };
@@ -91,10 +88,12 @@ struct TailCopyArgs {
 hipError_t launch_encode(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
 // Rotation on the matrix cores (coded length 64 or 128, no outlier list).
 bool encode_mx_supported(int m);
+// Outlier lists in three passes (count + records, offsets scan, entries); `part` holds
+// scan_partials(n) u32 of workspace.
+int64_t scan_partials(int64_t n);
+hipError_t launch_encode_outliers3(int m, int bits, bool sym, const EncodeArgs& a, uint32_t* part,
+                                   hipStream_t st);
 hipError_t launch_encode_mx(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
-hipError_t launch_encode_outliers(int m, int bits, bool sym, const EncodeArgs& a,
-                                  int64_t n_tiles, hipStream_t st);
-int64_t encode_outlier_tile_vectors(int m);
 bool pca_shape_supported(int D, int r);
 hipError_t launch_encode_pca(int D, int r, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
 hipError_t launch_decode_pca(int D, int r, int bits, bool bf16_out, const DecodeArgs& a,
