@@ -192,12 +192,15 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
   constexpr int KS = M / 32;              // MFMA k-steps (one 32-coordinate word group each)
   constexpr int NWC = KS * BITS, NWT = NWC + 1;
   constexpr int NPAIR = 1 << (2 * BITS);  // pair-table entries
+  // copies of the pair table, lane l reading copy l % COPIES: the lookups of a half-wave then
+  // never share an LDS bank
+  constexpr int COPIES = BITS <= 3 ? 32 : 4;
   // tiles in flight per wave: as many 16-token record tiles as fit ~64 registers (1 .. 7)
   constexpr int P = (64 / NWT - 1) < 1 ? 1 : ((64 / NWT - 1) > 7 ? 7 : (64 / NWT - 1));
   constexpr int R = P + 1;
   __shared__ __attribute__((aligned(16))) float qs[H * M];
   __shared__ float qmu[H];
-  __shared__ uint32_t lut_hi[NPAIR], lut_lo[NPAIR];
+  __shared__ uint32_t lut[2 * NPAIR * COPIES];  // [hi | lo][entry][copy]
   __shared__ uint4 sBT[PCA ? D * M / 8 : 1];
   __shared__ float uq[PCA ? H * M : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -208,25 +211,31 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
   const int64_t t_begin = (blockIdx.x % chunks_per_pair) * chunk;
   const int64_t t_end = t_begin + chunk < a.T ? t_begin + chunk : a.T;
   const int64_t rowbase = b * a.rec_sb + kv * a.rec_sh;
-  // pair table: entry e holds the centroids of code_a (bits 2p of e) and code_b (bits 2p+1)
-  for (int e = tid; e < NPAIR; e += kScoreThreads) {
-    uint32_t ca = 0, cb = 0;
+  // pair table: entry e holds the centroids of code_a (bits 2p of e) and code_b (bits 2p+1) as
+  // their bf16 hi pair and lo pair; a thread forms one entry and writes its share of the copies
+  {
+    constexpr int ACT = kScoreThreads < NPAIR * COPIES ? kScoreThreads : NPAIR * COPIES;
+    static_assert(ACT % NPAIR == 0 && (NPAIR * COPIES) % ACT == 0, "pair table split");
+    constexpr int CSTEP = ACT / NPAIR;
+    for (int e = tid % NPAIR, c = tid / NPAIR; tid < ACT && c < COPIES; c += CSTEP) {
+      uint32_t ca = 0, cb = 0;
 #pragma unroll
-    for (int p = 0; p < BITS; ++p) {
-      ca |= ((e >> (2 * p)) & 1u) << p;
-      cb |= ((e >> (2 * p + 1)) & 1u) << p;
-    }
-    float va = 0.0f, vb = 0.0f;
+      for (int p = 0; p < BITS; ++p) {
+        ca |= ((e >> (2 * p)) & 1u) << p;
+        cb |= ((e >> (2 * p + 1)) & 1u) << p;
+      }
+      float va = 0.0f, vb = 0.0f;
 #pragma unroll
-    for (int k = 0; k < (1 << BITS); ++k) {
-      va = (uint32_t)k == ca ? a.tab.c[k] : va;
-      vb = (uint32_t)k == cb ? a.tab.c[k] : vb;
+      for (int k = 0; k < (1 << BITS); ++k) {
+        va = (uint32_t)k == ca ? a.tab.c[k] : va;
+        vb = (uint32_t)k == cb ? a.tab.c[k] : vb;
+      }
+      uint32_t ha, la, hb, lb;
+      split_bf16(va, ha, la);
+      split_bf16(vb, hb, lb);
+      lut[e * COPIES + c] = ha | (hb << 16);
+      lut[(NPAIR + e) * COPIES + c] = la | (lb << 16);
     }
-    uint32_t ha, la, hb, lb;
-    split_bf16(va, ha, la);
-    split_bf16(vb, hb, lb);
-    lut_hi[e] = ha | (hb << 16);
-    lut_lo[e] = la | (lb << 16);
   }
   uint4 qa_hi[KS], qa_lo[KS];  // A operand: head tok, coordinates 32 ks + 8 oct .. + 7
   float qm[4];
@@ -285,8 +294,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
           const uint32_t idx = pair_index<BITS>(w + ks * BITS, 8 * oct, 2 * pr);
-          zh[pr] = lut_hi[idx];
-          zl[pr] = lut_lo[idx];
+          zh[pr] = lut[idx * COPIES + (lane & (COPIES - 1))];
+          zl[pr] = lut[(NPAIR + idx) * COPIES + (lane & (COPIES - 1))];
         }
         const uint4 bh = make_uint4(zh[0], zh[1], zh[2], zh[3]);
         const uint4 blo = make_uint4(zl[0], zl[1], zl[2], zl[3]);

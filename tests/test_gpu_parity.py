@@ -89,6 +89,26 @@ def test_edge_vectors_zero_single_and_scaled():
     assert empty.shape[0] == 0
 
 
+@pytest.mark.parametrize("D,bits", [(128, 2), (64, 3), (128, 1)])
+@pytest.mark.parametrize("n", [1, 17, 255, 257, 4099])
+def test_decode_strided_output_and_ragged_n(D, bits, n):
+    """Decode into rows wider than D (ld = D + 24): the columns past D stay untouched; vector
+    counts below, at and past the block tile (256) and a ragged large count."""
+    codec = kvq.Codec(D, bits, seed=21)
+    x = _rows(n, D, seed=n + D + bits)
+    rec = kvq.encode(codec, x)
+    for dt in (torch.float32, torch.bfloat16):
+        big = torch.full((n, D + 24), 7.0, dtype=dt, device=DEV)
+        kvq.decode(codec, rec, out=big[:, :D])
+        torch.cuda.synchronize()
+        recn = rec.cpu().numpy()
+        yref = oracle.decode(oracle_codec_like(codec), recn)
+        _, norms = unpack_records(recn, D, bits)
+        compare_decoded(big[:, :D].float().cpu().numpy(), yref, norms, f"strided decode {dt} n={n}",
+                        extra_ulp_bf16=dt == torch.bfloat16)
+        assert torch.all(big[:, D:] == 7.0), "decode wrote past the row's D columns"
+
+
 def test_scale_invariance_on_gpu():
     D, bits = 256, 4
     codec = kvq.Codec(D, bits, seed=13)

@@ -29,7 +29,7 @@ def _oracle_codec(D, r, bits, seed, mu, b):
 
 
 @pytest.mark.parametrize("D,r,bits", [(128, 64, 3), (128, 32, 2), (256, 64, 4), (256, 128, 3),
-                                      (64, 32, 1), (512, 64, 4)])
+                                      (64, 32, 1), (512, 64, 4), (256, 32, 3), (128, 64, 2)])
 def test_pca_single_basis_encode_decode(D, r, bits):
     mu, b = _bases(D, r, 1, seed=D + r)
     basis = torch.from_numpy(b[0].view(np.int16)).view(torch.bfloat16).to(DEV).contiguous()
