@@ -226,6 +226,27 @@ def score(cd: Codec, q_bf16: np.ndarray, records: np.ndarray) -> np.ndarray:
     return out
 
 
+def attend(kc: Codec, vc: Codec, q_bf16: np.ndarray, krecs: np.ndarray, vrecs: np.ndarray,
+           softmax_scale: float, softcap: float = 0.0) -> np.ndarray:
+    """Decode attention of the query heads of one KV head over packed K and V records:
+    q [G, D] bf16 bits, krecs [T, kc.rec_bytes], vrecs [T, vc.rec_bytes] -> f64 [G, D].
+
+    Logits l_t = softmax_scale * (q . k^_t); with softcap > 0 they become softcap * tanh(l / softcap),
+    after the scale multiply and before the maximum [arc PR #98, "Also: two silently-ignored
+    kernel parameters"]; weights w = softmax over t; output sum_t w_t v^_t with k^, v^ the
+    decoded records [arc PR #98 / #94 kernel commit: attention reads the packed cache]."""
+    K = decode(kc, krecs)                                    # [T, D]
+    V = decode(vc, vrecs)                                    # [T, D]
+    q = (np.ascontiguousarray(q_bf16, np.uint16).reshape(-1, kc.D).astype(np.uint32) << 16)
+    q = q.view(np.float32).astype(np.float64)                # [G, D]
+    logits = softmax_scale * (q @ K.T)                       # [G, T]
+    if softcap > 0:
+        logits = softcap * np.tanh(logits / softcap)
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    return w @ V
+
+
 # --------------------------------------------------------------------------------------------
 # Two-region cache model [arc PR #98]: a dense tail (list of bf16 rows) and a packed region.
 

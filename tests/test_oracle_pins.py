@@ -372,6 +372,73 @@ def test_score_equals_rotated_domain_identity(D, bits):
 
 
 # ---------------------------------------------------------------------------------------------
+# Decode attention over packed K and V
+
+
+def _attn_case(T, D=64, kb=3, vb=2, G=3, seed=0):
+    rng = np.random.default_rng(seed)
+    kc, vc = oracle.Codec(D, kb, seed=5), oracle.Codec(D, vb, seed=6)
+    krec = oracle.encode_records(kc, _bf16(rng.normal(size=(T, D))))
+    vrec = oracle.encode_records(vc, _bf16(rng.normal(size=(T, D))))
+    q = _bf16(rng.normal(size=(G, D)))
+    return kc, vc, q, krec, vrec
+
+
+def test_attend_single_token_returns_its_decoded_value():
+    kc, vc, q, krec, vrec = _attn_case(1)
+    got = oracle.attend(kc, vc, q, krec, vrec, 0.125)
+    want = oracle.decode(vc, vrec)[0]
+    np.testing.assert_allclose(got, np.repeat(want[None], q.shape[0], 0), rtol=0, atol=1e-15)
+
+
+def test_attend_zero_query_averages_the_values():
+    kc, vc, q, krec, vrec = _attn_case(37)
+    got = oracle.attend(kc, vc, np.zeros_like(q), krec, vrec, 0.125)
+    want = oracle.decode(vc, vrec).mean(axis=0)
+    np.testing.assert_allclose(got, np.repeat(want[None], q.shape[0], 0), rtol=1e-13, atol=1e-14)
+
+
+def test_attend_two_tokens_is_the_logistic_mix():
+    """T = 2: weights are sigma(l0 - l1) and sigma(l1 - l0), logits from the oracle's C score."""
+    kc, vc, q, krec, vrec = _attn_case(2, G=4, seed=3)
+    scale = 0.3
+    got = oracle.attend(kc, vc, q, krec, vrec, scale)
+    v = oracle.decode(vc, vrec)
+    for g in range(q.shape[0]):
+        l = scale * oracle.score(kc, np.repeat(q[g][None], 2, 0), krec)
+        w0 = 1.0 / (1.0 + math.exp(-(l[0] - l[1])))
+        np.testing.assert_allclose(got[g], w0 * v[0] + (1.0 - w0) * v[1], rtol=1e-12, atol=1e-13)
+
+
+def test_attend_sharp_limit_selects_the_top_scoring_token():
+    kc, vc, q, krec, vrec = _attn_case(29, G=2, seed=4)
+    v = oracle.decode(vc, vrec)
+    got = oracle.attend(kc, vc, q, krec, vrec, 1e6)
+    for g in range(q.shape[0]):
+        top = np.argmax(oracle.score(kc, np.repeat(q[g][None], 29, 0), krec))
+        np.testing.assert_allclose(got[g], v[top], rtol=0, atol=1e-9)
+
+
+def test_attend_ignores_token_order():
+    kc, vc, q, krec, vrec = _attn_case(50, seed=5)
+    perm = np.random.default_rng(1).permutation(50)
+    a = oracle.attend(kc, vc, q, krec, vrec, 0.2)
+    b = oracle.attend(kc, vc, q, krec[perm], vrec[perm], 0.2)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+def test_attend_softcap_limits():
+    """A huge cap changes nothing; a tiny cap flattens every logit towards 0 (uniform mean)."""
+    kc, vc, q, krec, vrec = _attn_case(41, seed=6)
+    plain = oracle.attend(kc, vc, q, krec, vrec, 0.5)
+    np.testing.assert_allclose(oracle.attend(kc, vc, q, krec, vrec, 0.5, softcap=1e9), plain,
+                               rtol=1e-9, atol=1e-12)
+    flat = oracle.attend(kc, vc, q, krec, vrec, 0.5, softcap=1e-7)
+    mean = oracle.decode(vc, vrec).mean(axis=0)
+    np.testing.assert_allclose(flat, np.repeat(mean[None], q.shape[0], 0), rtol=1e-5, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------------------------
 # PCA path
 
 
