@@ -171,6 +171,30 @@ kvq_status kvq_score_packed(const kvq_codec* codec, const void* q_dev, int32_t B
                             int64_t T, int64_t rec_sb, int64_t rec_sh, float* scores_dev,
                             int64_t s_sb, int64_t s_sh, void* stream);
 
+/* Decode attention over packed K and V, for the query heads of each (batch, KV head):
+ *   out[b][h] = sum_t w_t decode_V(vrec[b][kv][t]),  w = softmax_t(l_t),
+ *   l_t = softmax_scale * (q[b][h] . decode_K(krec[b][kv][t])), kv = h / (Hq/Hkv),
+ * and, when softcap > 0, l_t = softcap * tanh(l_t / softcap) after the scale multiply and before
+ * the maximum [arc PR #98 / #94 kernel commit: attention reads the packed cache; arc PR #98,
+ * "Also: two silently-ignored kernel parameters"]. Neither K nor V is materialised: logits are
+ * formed in the K codec's rotated domain, values are accumulated in the V codec's rotated
+ * domain and rotated back once per query head.
+ * kcodec: any codec kvq_score_packed accepts with head_dim 64 or 128 (projection ranks 32, 64).
+ * vcodec: Hadamard (proj_rank 0), same head_dim, bits 1..3. Neither may carry an outlier list.
+ * q_dev: bf16, row (b, h) at q_dev + b*q_sb + h*q_sh elements (16-byte aligned).
+ * krec_dev / vrec_dev: record (b, kv, t) at index b*rec_sb + kv*rec_sh + t of each array.
+ * out_dev: f32 [D] per (b, h) at out_dev + b*o_sb + h*o_sh floats.
+ * workspace_dev: kvq_attend_workspace_bytes(vcodec, B, Hkv, T) bytes, 16-byte aligned, caller
+ * owned, contents need not be initialised (per-block partial maxima, sums and accumulators).
+ * T must be >= 1. Two kernels on the stream; no synchronisation. */
+size_t kvq_attend_workspace_bytes(const kvq_codec* vcodec, int32_t B, int32_t Hkv, int64_t T);
+kvq_status kvq_attend_packed(const kvq_codec* kcodec, const kvq_codec* vcodec, const void* q_dev,
+                             int32_t B, int32_t Hq, int64_t q_sb, int64_t q_sh,
+                             const void* krec_dev, const void* vrec_dev, int32_t Hkv, int64_t T,
+                             int64_t rec_sb, int64_t rec_sh, float softmax_scale, float softcap,
+                             float* out_dev, int64_t o_sb, int64_t o_sh, void* workspace_dev,
+                             size_t workspace_bytes, void* stream);
+
 /* Build an empty cache over caller-owned buffers: packed_dev holds packed_cap records,
  * tail_dev holds tail_cap bf16 rows of head_dim. window >= 0, margin >= 0. Host only.
  * Outlier lists are not supported in caches (codec->outlier_T must be 0). */

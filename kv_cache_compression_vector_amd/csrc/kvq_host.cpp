@@ -387,6 +387,81 @@ kvq_status kvq_score_packed(const kvq_codec* codec, const void* q_dev, int32_t B
                   "score_packed");
 }
 
+size_t kvq_attend_workspace_bytes(const kvq_codec* vcodec, int32_t B, int32_t Hkv, int64_t T) {
+  Resolved r;
+  if (resolve_codec(vcodec, r) != KVQ_OK || B < 0 || Hkv < 0 || T < 0) return 0;
+  if (B == 0 || Hkv == 0 || T == 0) return 0;
+  return (size_t)(4 * kvq::attend_partial_floats((int64_t)B * Hkv, T, r.D));
+}
+
+kvq_status kvq_attend_packed(const kvq_codec* kcodec, const kvq_codec* vcodec, const void* q_dev,
+                             int32_t B, int32_t Hq, int64_t q_sb, int64_t q_sh,
+                             const void* krec_dev, const void* vrec_dev, int32_t Hkv, int64_t T,
+                             int64_t rec_sb, int64_t rec_sh, float softmax_scale, float softcap,
+                             float* out_dev, int64_t o_sb, int64_t o_sh, void* workspace_dev,
+                             size_t workspace_bytes, void* stream) {
+  Resolved rk, rv;
+  kvq_status st = resolve_codec(kcodec, rk);
+  if (st != KVQ_OK) return st;
+  st = resolve_codec(vcodec, rv);
+  if (st != KVQ_OK) return st;
+  if (rk.outliers || rv.outliers)
+    return fail(KVQ_E_OUTLIER, "attention reads codes and norms only: outlier_T must be 0 for K and V");
+  if (rv.pca) return fail(KVQ_E_ARG, "the V codec must be Hadamard (proj_rank=0), got proj_rank=%u", vcodec->proj_rank);
+  if (rk.D != rv.D) return fail(KVQ_E_DIM, "K head_dim=%d and V head_dim=%d differ", rk.D, rv.D);
+  if (!kvq::attend_supported(rk.D, rk.m, rk.bits, rv.bits))
+    return fail(KVQ_E_ARG, "attention supports head_dim 64/128, K coded length 32..D, K bits 1..4, V bits 1..3 "
+                "(got D=%d, K m=%d b=%d, V b=%d)", rk.D, rk.m, rk.bits, rv.bits);
+  if (B < 0 || Hq < 0 || Hkv < 0 || T < 0) return fail(KVQ_E_ARG, "negative size (B=%d Hq=%d Hkv=%d T=%lld)", B, Hq, Hkv, (long long)T);
+  if (B == 0 || Hq == 0) return ok();
+  if (T == 0) return fail(KVQ_E_ARG, "attention over T=0 tokens is undefined");
+  if (Hkv == 0 || Hq % Hkv) return fail(KVQ_E_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int group = Hq / Hkv;
+  if (group < 1 || group > 8) return fail(KVQ_E_ARG, "Hq/Hkv=%d not supported (1..8)", group);
+  if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY || softmax_scale == -INFINITY)
+    return fail(KVQ_E_ARG, "softmax_scale must be finite");
+  if (!(softcap >= 0.0f) || softcap == INFINITY) return fail(KVQ_E_ARG, "softcap must be finite and >= 0 (0 = off)");
+  if (!q_dev || !krec_dev || !vrec_dev || !out_dev || !workspace_dev)
+    return fail(KVQ_E_NULL, "q_dev, krec_dev, vrec_dev, out_dev or workspace_dev is NULL");
+  if (!aligned(q_dev, 16) || q_sb % 8 || q_sh % 8)
+    return fail(KVQ_E_STRIDE, "q rows must be 16-byte aligned (q_sb=%lld, q_sh=%lld elements)", (long long)q_sb, (long long)q_sh);
+  if (!aligned(krec_dev, 4) || !aligned(vrec_dev, 4)) return fail(KVQ_E_STRIDE, "records are not 4-byte aligned");
+  if (!aligned(out_dev, 4)) return fail(KVQ_E_STRIDE, "out_dev is not 4-byte aligned");
+  if (!aligned(workspace_dev, 16)) return fail(KVQ_E_STRIDE, "workspace_dev is not 16-byte aligned");
+  if (q_sb < 0 || q_sh < 0 || rec_sb < 0 || rec_sh < 0 || o_sb < 0 || o_sh < 0)
+    return fail(KVQ_E_STRIDE, "negative stride");
+  const size_t need = kvq_attend_workspace_bytes(vcodec, B, Hkv, T);
+  if (workspace_bytes < need)
+    return fail(KVQ_E_ARG, "workspace_bytes=%zu, need %zu", workspace_bytes, need);
+  if (rk.pca && rk.basis.count > 1 && (rk.basis.block_rows % 256 || rec_sb % 256 || rec_sh % 256))
+    return fail(KVQ_E_STRIDE,
+                "attention with several bases needs basis_block_rows, rec_sb, rec_sh multiples of 256 "
+                "(got %d, %lld, %lld)", rk.basis.block_rows, (long long)rec_sb, (long long)rec_sh);
+  kvq::AttendArgs a{};
+  a.k.tab = rk.tab;
+  a.k.q = static_cast<const uint16_t*>(q_dev);
+  a.k.q_sb = q_sb;
+  a.k.q_sh = q_sh;
+  a.k.rec = static_cast<const uint8_t*>(krec_dev);
+  a.k.rec_sb = rec_sb;
+  a.k.rec_sh = rec_sh;
+  a.k.T = T;
+  a.k.B = B;
+  a.k.Hq = Hq;
+  a.k.Hkv = Hkv;
+  a.k.pca = rk.basis;
+  a.tv = rv.tab;
+  a.vrec = static_cast<const uint8_t*>(vrec_dev);
+  a.part = static_cast<float*>(workspace_dev);
+  a.out = out_dev;
+  a.o_sb = o_sb;
+  a.o_sh = o_sh;
+  a.scale = softmax_scale;
+  a.softcap = softcap;
+  return from_hip(kvq::launch_attend(rk.D, rk.m, rk.bits, rv.bits, a, static_cast<hipStream_t>(stream)),
+                  "attend_packed");
+}
+
 kvq_status kvq_cache_init(const kvq_codec* codec, kvq_cache* cache, void* packed_dev,
                           int64_t packed_cap, void* tail_dev, int64_t tail_cap, int32_t window,
                           int32_t margin) {

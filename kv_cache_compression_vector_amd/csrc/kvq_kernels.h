@@ -49,6 +49,21 @@ struct ScoreArgs {
   Basis pca;                // PCA kernels only
 };
 
+// Decode attention over packed K and V: the K side is a score launch (query, K records and
+// their strides, K tables, projection); V records share the K records' (batch, KV head, token)
+// indexing. Blocks write per-wave partials (running max, sum, rotated accumulator) to `part`;
+// a second kernel merges them into `out`.
+struct AttendArgs {
+  ScoreArgs k;
+  Tables tv;                // V codec tables (Hadamard, coded length = head_dim)
+  const uint8_t* vrec;
+  float* part;
+  float* out;
+  int64_t o_sb, o_sh;       // in floats
+  float scale, softcap;     // logit multiplier; softcap > 0: softcap * tanh(logit / softcap)
+  int64_t chunk, chunks;    // tokens per block (multiple of 256) and blocks per (batch, KV head)
+};
+
 // One cache of an append/evict launch: rows [0, rows) of the concatenation (tail ring, new rows)
 // are encoded into dst.
 struct EvictCache {
@@ -101,6 +116,11 @@ hipError_t launch_decode_pca(int D, int r, int bits, bool bf16_out, const Decode
 hipError_t launch_decode(int D, int m, int bits, bool outliers, bool bf16_out,
                          const DecodeArgs& a, hipStream_t st);
 hipError_t launch_score(int D, int m, int bits, int group, const ScoreArgs& a, hipStream_t st);
+// Attention: token chunk per block for (pairs, T), and the partial floats the launch writes.
+int64_t attend_chunk(int64_t pairs, int64_t T);
+int64_t attend_partial_floats(int64_t pairs, int64_t T, int D);
+bool attend_supported(int D, int mk, int bk, int bv);
+hipError_t launch_attend(int D, int mk, int bk, int bv, const AttendArgs& a, hipStream_t st);
 hipError_t launch_evict(int m, int bits, bool sym, const EvictArgs& a, hipStream_t st);
 hipError_t launch_tail_copy(const TailCopyArgs& a, hipStream_t st);
 hipError_t launch_clear_u32(uint32_t* p, int64_t n_words, hipStream_t st);

@@ -185,6 +185,91 @@ __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int k
   __syncthreads();
 }
 
+// Pair table: entry e (bit 2p + i = plane p of code i) holds the centroids of its two codes as
+// their bf16 hi pair (lut[e COPIES + c]) and lo pair (lut[(NPAIR + e) COPIES + c]), copy c read by
+// lanes l with l % COPIES == c, so the lookups of a half-wave never share an LDS bank. Each
+// thread of the block forms one entry and writes its share of the copies.
+template <int BITS, int COPIES>
+__device__ __forceinline__ void fill_pair_table(const Tables& tab, uint32_t* lut, int tid) {
+  constexpr int NPAIR = 1 << (2 * BITS);
+  constexpr int ACT = kScoreThreads < NPAIR * COPIES ? kScoreThreads : NPAIR * COPIES;
+  static_assert(ACT % NPAIR == 0 && (NPAIR * COPIES) % ACT == 0, "pair table split");
+  constexpr int CSTEP = ACT / NPAIR;
+  for (int e = tid % NPAIR, c = tid / NPAIR; tid < ACT && c < COPIES; c += CSTEP) {
+    uint32_t ca = 0, cb = 0;
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) {
+      ca |= ((e >> (2 * p)) & 1u) << p;
+      cb |= ((e >> (2 * p + 1)) & 1u) << p;
+    }
+    float va = 0.0f, vb = 0.0f;
+#pragma unroll
+    for (int k = 0; k < (1 << BITS); ++k) {
+      va = (uint32_t)k == ca ? tab.c[k] : va;
+      vb = (uint32_t)k == cb ? tab.c[k] : vb;
+    }
+    uint32_t ha, la, hb, lb;
+    split_bf16(va, ha, la);
+    split_bf16(vb, hb, lb);
+    lut[e * COPIES + c] = ha | (hb << 16);
+    lut[(NPAIR + e) * COPIES + c] = la | (lb << 16);
+  }
+}
+
+// Copies per pair table: one per lane of a half-wave up to 3 bits (16 KB at 3 bits), 4 at 4 bits.
+template <int BITS>
+constexpr int pair_copies() { return BITS <= 3 ? 32 : 4; }
+
+// The MFMA A operand of the rotated queries (head tok, coordinates 32 ks + 8 oct + [0, 8)) as bf16
+// hi and lo halves, and q . mu of heads 4 oct + [0, 4), from what prepare_queries left in LDS.
+template <int M>
+__device__ __forceinline__ void query_operands(const float* qs, const float* qmu, int tok, int oct,
+                                               uint4 (&qa_hi)[M / 32], uint4 (&qa_lo)[M / 32],
+                                               float (&qm)[4]) {
+  constexpr int H = kScoreHeads;
+#pragma unroll
+  for (int ks = 0; ks < M / 32; ++ks) {
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = tok < H ? qs[tok * M + 32 * ks + 8 * oct + e] : 0.0f;
+      split_bf16(x, hi[e], lo[e]);
+    }
+    qa_hi[ks] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                           hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+    qa_lo[ks] = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                           lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) qm[k] = 4 * oct + k < H ? qmu[4 * oct + k] : 0.0f;
+}
+
+// Raw logits of one 16-token record tile against the rotated queries: acc[k] = q . k^ for head
+// 4 oct + k and the tile's token tok, before the norm scale and q . mu.
+template <int M, int BITS, int COPIES>
+__device__ __forceinline__ floatx4_t tile_dots(const uint32_t* w, const uint32_t* lut, int lane,
+                                               int oct, const uint4 (&qa_hi)[M / 32],
+                                               const uint4 (&qa_lo)[M / 32]) {
+  constexpr int NPAIR = 1 << (2 * BITS);
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < M / 32; ++ks) {
+    uint32_t zh[4], zl[4];
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      const uint32_t idx = pair_index<BITS>(w + ks * BITS, 8 * oct, 2 * pr);
+      zh[pr] = lut[idx * COPIES + (lane & (COPIES - 1))];
+      zl[pr] = lut[(NPAIR + idx) * COPIES + (lane & (COPIES - 1))];
+    }
+    const uint4 bh = make_uint4(zh[0], zh[1], zh[2], zh[3]);
+    const uint4 blo = make_uint4(zl[0], zl[1], zl[2], zl[3]);
+    acc = mfma16(qa_hi[ks], bh, acc);
+    acc = mfma16(qa_hi[ks], blo, acc);
+    acc = mfma16(qa_lo[ks], bh, acc);
+  }
+  return acc;
+}
+
 template <int D, int M, int BITS, bool PCA>
 __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t chunk,
                                                          int64_t chunks_per_pair) {
@@ -192,9 +277,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
   constexpr int KS = M / 32;              // MFMA k-steps (one 32-coordinate word group each)
   constexpr int NWC = KS * BITS, NWT = NWC + 1;
   constexpr int NPAIR = 1 << (2 * BITS);  // pair-table entries
-  // copies of the pair table, lane l reading copy l % COPIES: the lookups of a half-wave then
-  // never share an LDS bank
-  constexpr int COPIES = BITS <= 3 ? 32 : 4;
+  constexpr int COPIES = pair_copies<BITS>();
   // tiles in flight per wave: as many 16-token record tiles as fit ~64 registers (1 .. 7)
   constexpr int P = (64 / NWT - 1) < 1 ? 1 : ((64 / NWT - 1) > 7 ? 7 : (64 / NWT - 1));
   constexpr int R = P + 1;
@@ -211,32 +294,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
   const int64_t t_begin = (blockIdx.x % chunks_per_pair) * chunk;
   const int64_t t_end = t_begin + chunk < a.T ? t_begin + chunk : a.T;
   const int64_t rowbase = b * a.rec_sb + kv * a.rec_sh;
-  // pair table: entry e holds the centroids of code_a (bits 2p of e) and code_b (bits 2p+1) as
-  // their bf16 hi pair and lo pair; a thread forms one entry and writes its share of the copies
-  {
-    constexpr int ACT = kScoreThreads < NPAIR * COPIES ? kScoreThreads : NPAIR * COPIES;
-    static_assert(ACT % NPAIR == 0 && (NPAIR * COPIES) % ACT == 0, "pair table split");
-    constexpr int CSTEP = ACT / NPAIR;
-    for (int e = tid % NPAIR, c = tid / NPAIR; tid < ACT && c < COPIES; c += CSTEP) {
-      uint32_t ca = 0, cb = 0;
-#pragma unroll
-      for (int p = 0; p < BITS; ++p) {
-        ca |= ((e >> (2 * p)) & 1u) << p;
-        cb |= ((e >> (2 * p + 1)) & 1u) << p;
-      }
-      float va = 0.0f, vb = 0.0f;
-#pragma unroll
-      for (int k = 0; k < (1 << BITS); ++k) {
-        va = (uint32_t)k == ca ? a.tab.c[k] : va;
-        vb = (uint32_t)k == cb ? a.tab.c[k] : vb;
-      }
-      uint32_t ha, la, hb, lb;
-      split_bf16(va, ha, la);
-      split_bf16(vb, hb, lb);
-      lut[e * COPIES + c] = ha | (hb << 16);
-      lut[(NPAIR + e) * COPIES + c] = la | (lb << 16);
-    }
-  }
+  fill_pair_table<BITS, COPIES>(a.tab, lut, tid);
   uint4 qa_hi[KS], qa_lo[KS];  // A operand: head tok, coordinates 32 ks + 8 oct .. + 7
   float qm[4];
   int cur = -1;
@@ -267,42 +325,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
         if (bi != cur) {  // block-uniform
           __syncthreads();
           prepare_queries<D, M, PCA>(a, b, kv, G, bi, qs, qmu, sBT, uq);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            uint32_t hi[8], lo[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float x = tok < H ? qs[tok * M + 32 * ks + 8 * oct + e] : 0.0f;
-              split_bf16(x, hi[e], lo[e]);
-            }
-            qa_hi[ks] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                   hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-            qa_lo[ks] = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                   lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
-          }
-#pragma unroll
-          for (int k = 0; k < 4; ++k) qm[k] = 4 * oct + k < H ? qmu[4 * oct + k] : 0.0f;
+          query_operands<M>(qs, qmu, tok, oct, qa_hi, qa_lo, qm);
           cur = bi;
         }
       }
       if (j + P < n_tiles) load_tile(j + P, ring[(r + P) % R]);
       const uint32_t (&w)[NWT] = ring[r];
-      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint32_t zh[4], zl[4];
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const uint32_t idx = pair_index<BITS>(w + ks * BITS, 8 * oct, 2 * pr);
-          zh[pr] = lut[idx * COPIES + (lane & (COPIES - 1))];
-          zl[pr] = lut[(NPAIR + idx) * COPIES + (lane & (COPIES - 1))];
-        }
-        const uint4 bh = make_uint4(zh[0], zh[1], zh[2], zh[3]);
-        const uint4 blo = make_uint4(zl[0], zl[1], zl[2], zl[3]);
-        acc = mfma16(qa_hi[ks], bh, acc);
-        acc = mfma16(qa_hi[ks], blo, acc);
-        acc = mfma16(qa_lo[ks], bh, acc);
-      }
+      const floatx4_t acc = tile_dots<M, BITS, COPIES>(w, lut, lane, oct, qa_hi, qa_lo);
       // acc[k] = sum for head 4 oct + k, token t
       const int64_t t = t_begin + 64 * j + 16 * wave + tok;
       const int64_t se = t_begin + kScoreSegment * (j / 4 + 1);
@@ -315,6 +344,322 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
       }
     }
   }
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode attention over packed K and V [arc PR #98 / #94 kernel commit: the attention kernel
+// reads the packed cache directly; arc PR #98, "Also: two silently-ignored kernel parameters":
+// the soft cap acts after the scale multiply and before the running maximum].
+//
+// A block takes a run of tokens of one (batch, KV head) and the G <= 8 query heads of its
+// group. Each wave walks 32-token units: the logits of two 16-token tiles on MFMA exactly as in
+// k_score, an online softmax per head (running maximum m and sum l), and
+//   acc[h][P] += sum_t p[h][t] (n_t / m) z^_t[P]     (P = plane position of the V codec)
+// in the V codec's rotated domain, also on MFMA: A = the centroids of 16 positions x 32 tokens
+// expanded from the V records' bit planes (two tokens per pair-table entry, bf16 hi + lo), B =
+// the unit's weights p (n/m), transposed through LDS. The inverse rotation is linear, so it is
+// applied once per query head after the partials are merged (k_attend_combine):
+//   out = s (.) H (sum_c e^{m_c - M} acc_c) / (sum_c e^{m_c - M} l_c).
+
+constexpr int kAttnWaves = kScoreThreads / 64;
+
+template <int D>
+constexpr int attend_stride() { return D + 4; }  // partial of one head: m, l, pad, acc[D]
+
+template <int D, int M, int BK, bool PCA, int BV>
+__global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
+  constexpr int H = kScoreHeads;
+  constexpr int KS = M / 32, NWK = KS * BK + 1;
+  constexpr int CK = pair_copies<BK>();
+  constexpr int GV = D / 32, NWV = GV * BV + 1;  // V word groups, V record words
+  constexpr int NPV = 1 << (2 * BV), CV = pair_copies<BV>();
+  constexpr int CT = D / 16;                     // 16-position tiles of the V accumulator
+  constexpr int VPL = (32 * NWV + 63) / 64;      // V record dwords staged per lane
+  constexpr int S = attend_stride<D>();
+  __shared__ __attribute__((aligned(16))) float qs[H * M];
+  __shared__ float qmu[H];
+  __shared__ uint32_t lutk[2 * (1 << (2 * BK)) * CK];
+  __shared__ uint32_t lutv[2 * NPV * CV];
+  __shared__ uint4 sBT[PCA ? D * M / 8 : 1];
+  __shared__ float uq[PCA ? H * M : 1];
+  __shared__ uint32_t vst[kAttnWaves][32 * NWV];                         // the unit's V records
+  __shared__ __attribute__((aligned(16))) float pst[kAttnWaves][16][32];  // p (n/m) [head][token]
+  __shared__ float cst[kAttnWaves][16];                                   // accumulator rescale
+  const ScoreArgs& k = a.k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tok = lane & 15, oct = lane >> 4;
+  const int64_t pair = blockIdx.x / a.chunks;
+  const int b = (int)(pair / k.Hkv), kv = (int)(pair % k.Hkv);
+  const int G = k.Hq / k.Hkv;
+  const int64_t t_begin = (blockIdx.x % a.chunks) * a.chunk;
+  const int64_t t_end = t_begin + a.chunk < k.T ? t_begin + a.chunk : k.T;
+  const int64_t rowbase = b * k.rec_sb + kv * k.rec_sh;
+  fill_pair_table<BK, CK>(k.tab, lutk, tid);
+  fill_pair_table<BV, CV>(a.tv, lutv, tid);
+  const uint32_t* krec32 = reinterpret_cast<const uint32_t*>(k.rec);
+  const uint32_t* vrec32 = reinterpret_cast<const uint32_t*>(a.vrec);
+  uint4 qa_hi[KS], qa_lo[KS];
+  float qm[4], mrun[4], lrun[4];  // softmax state of heads 4 oct + kk
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    mrun[kk] = -INFINITY;
+    lrun[kk] = 0.0f;
+  }
+  floatx4_t acc[CT];  // acc[ct][i]: position 16 ct + 4 oct + i of head tok
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  int cur = -1;
+  const int64_t n_seg = (t_end - t_begin + kScoreSegment - 1) / kScoreSegment;
+  for (int64_t sg = 0; sg < n_seg; ++sg) {
+    const int64_t s0 = t_begin + kScoreSegment * sg;
+    const int bi = PCA ? basis_of_row(k.pca, rowbase + s0) : 0;
+    if (bi != cur) {  // block-uniform
+      __syncthreads();
+      prepare_queries<D, M, PCA>(k, b, kv, G, bi, qs, qmu, sBT, uq);
+      query_operands<M>(qs, qmu, tok, oct, qa_hi, qa_lo, qm);
+      cur = bi;
+    }
+    for (int u = 0; u < kScoreSegment / (32 * kAttnWaves); ++u) {
+      const int64_t t0 = s0 + 32 * (kAttnWaves * u + wave);
+      if (t0 >= t_end) break;  // wave-uniform
+      // records: K words of token tok of both tiles; V records of the 32 tokens into LDS
+      // (tokens past the end read the last record and get weight 0)
+      uint32_t wk[2][NWK];
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        int64_t t = t0 + 16 * tile + tok;
+        t = t < t_end ? t : t_end - 1;
+        const uint32_t* r32 = krec32 + (rowbase + t) * NWK;
+#pragma unroll
+        for (int i = 0; i < NWK; ++i) wk[tile][i] = r32[i];
+      }
+      uint32_t vv[VPL];
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int idx = lane + 64 * i;
+        int64_t t = t0 + idx / NWV;
+        t = t < t_end ? t : t_end - 1;
+        vv[i] = idx < 32 * NWV ? vrec32[(rowbase + t) * NWV + idx % NWV] : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (lane + 64 * i < 32 * NWV) vst[wave][lane + 64 * i] = vv[i];
+      // logits of heads 4 oct + kk for tokens t0 + tok and t0 + 16 + tok
+      float lg[2][4];
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        const floatx4_t d = tile_dots<M, BK, CK>(wk[tile], lutk, lane, oct, qa_hi, qa_lo);
+        const int64_t t = t0 + 16 * tile + tok;
+        const float ns = __uint_as_float(wk[tile][NWK - 1]) * k.tab.inv_m;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          float x = fmaf(d[kk], ns, qm[kk]) * a.scale;
+          if (a.softcap > 0.0f) x = a.softcap * tanhf(x / a.softcap);
+          lg[tile][kk] = (t < t_end && 4 * oct + kk < G) ? x : -INFINITY;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // online softmax; weights times the V norm scale into pst
+      const float nv0 = __uint_as_float(vst[wave][tok * NWV + NWV - 1]) * a.tv.inv_m;
+      const float nv1 = __uint_as_float(vst[wave][(16 + tok) * NWV + NWV - 1]) * a.tv.inv_m;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        float mx = fmaxf(lg[0][kk], lg[1][kk]);
+        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
+        const float mn = fmaxf(mrun[kk], mx);
+        // mn = -inf: no token of this head so far (or a head slot >= G); nothing to rescale
+        const float corr = mn == -INFINITY ? 1.0f : __expf(mrun[kk] - mn);
+        const float p0 = lg[0][kk] == -INFINITY ? 0.0f : __expf(lg[0][kk] - mn);
+        const float p1 = lg[1][kk] == -INFINITY ? 0.0f : __expf(lg[1][kk] - mn);
+        float ps = p0 + p1;
+        ps += __shfl_xor(ps, 1, 64);
+        ps += __shfl_xor(ps, 2, 64);
+        ps += __shfl_xor(ps, 4, 64);
+        ps += __shfl_xor(ps, 8, 64);
+        lrun[kk] = fmaf(lrun[kk], corr, ps);
+        mrun[kk] = mn;
+        pst[wave][4 * oct + kk][tok] = p0 * nv0;
+        pst[wave][4 * oct + kk][16 + tok] = p1 * nv1;
+        if (tok == 0) cst[wave][4 * oct + kk] = corr;
+      }
+      __builtin_amdgcn_wave_barrier();
+      // B operand: weights of head tok for tokens 8 oct + [0, 8), bf16 hi and lo
+      const float c = cst[wave][tok];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct] *= c;
+      uint4 bhi, blo;
+      {
+        const float4 w0 = *reinterpret_cast<const float4*>(&pst[wave][tok][8 * oct]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&pst[wave][tok][8 * oct + 4]);
+        const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_bf16(w[e], hi[e], lo[e]);
+        bhi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
+                         hi[6] | (hi[7] << 16));
+        blo = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
+                         lo[6] | (lo[7] << 16));
+      }
+      // A operands: centroids at position P = 32 g + 16 h2 + tok of tokens 8 oct + [0, 8)
+#pragma unroll
+      for (int g = 0; g < GV; ++g) {
+        uint32_t wv[8][BV];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int p = 0; p < BV; ++p) wv[e][p] = vst[wave][(8 * oct + e) * NWV + g * BV + p];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int j = 16 * h2 + tok;
+          uint32_t ah[4], al[4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            uint32_t idx = 0;
+#pragma unroll
+            for (int p = 0; p < BV; ++p)
+              idx |= (__builtin_amdgcn_ubfe(wv[2 * e2][p], j, 1) << (2 * p)) |
+                     (__builtin_amdgcn_ubfe(wv[2 * e2 + 1][p], j, 1) << (2 * p + 1));
+            ah[e2] = lutv[idx * CV + (lane & (CV - 1))];
+            al[e2] = lutv[(NPV + idx) * CV + (lane & (CV - 1))];
+          }
+          const uint4 ahi = make_uint4(ah[0], ah[1], ah[2], ah[3]);
+          const uint4 alo = make_uint4(al[0], al[1], al[2], al[3]);
+          floatx4_t& c4 = acc[2 * g + h2];
+          c4 = mfma16(ahi, bhi, c4);
+          c4 = mfma16(ahi, blo, c4);
+          c4 = mfma16(alo, bhi, c4);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();  // vst, pst and cst are refilled by the next unit
+    }
+  }
+  // this wave's partial of each head: [m, l, -, -, acc by plane position]
+  float* pw = a.part + ((int64_t)blockIdx.x * kAttnWaves + wave) * H * S;
+  if (tok < G) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      *reinterpret_cast<float4*>(pw + tok * S + 4 + 16 * ct + 4 * oct) =
+          make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
+  }
+  if (tok == 0) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int h = 4 * oct + kk;
+      if (h < G) {
+        pw[h * S] = mrun[kk];
+        pw[h * S + 1] = lrun[kk];
+      }
+    }
+  }
+}
+
+// Merge of the partials of one (batch, query head) and the inverse rotation of the V codec:
+// out = s (.) H a, a[i] = sum_w e^{m_w - M} acc_w[pi(i)] / sum_w e^{m_w - M} l_w.
+template <int D>
+__global__ __launch_bounds__(64) void k_attend_combine(AttendArgs a) {
+  constexpr int LPV = D / 8, H = kScoreHeads, S = attend_stride<D>();
+  const ScoreArgs& k = a.k;
+  const int lane = threadIdx.x, c = lane % LPV;
+  const int b = blockIdx.x / k.Hq, hq = blockIdx.x % k.Hq, G = k.Hq / k.Hkv;
+  const int kv = hq / G, h = hq % G;
+  const int64_t pair = (int64_t)b * k.Hkv + kv;
+  const int64_t np = a.chunks * kAttnWaves;
+  const float* base = a.part + pair * np * H * S + h * S;
+  float mx = -INFINITY;
+  for (int64_t w = 0; w < np; ++w) mx = fmaxf(mx, base[w * H * S]);
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float l = 0.0f;
+  for (int64_t w = 0; w < np; ++w) {
+    const float* pw = base + w * H * S;
+    const float mw = pw[0];
+    if (mw == -INFINITY) continue;  // a wave that saw no token
+    const float f = __expf(mw - mx);
+    l = fmaf(f, pw[1], l);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = fmaf(f, pw[4 + j * (D / 8) + c], v[j]);  // pi(8c + j)
+  }
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] *= inv;
+  fwht_vector<LPV>(v, c);
+  if (lane < LPV) {
+    float* o = a.out + b * a.o_sb + hq * a.o_sh;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = 8 * c + j;
+      const bool neg = (a.tv.sign_words[i >> 5] >> (i & 31)) & 1u;
+      o[i] = neg ? -v[j] : v[j];
+    }
+  }
+}
+
+int64_t attend_chunk(int64_t pairs, int64_t T) {
+  const int64_t segs = (T + kScoreSegment - 1) / kScoreSegment;
+  int64_t cpp = pairs > 0 ? 512 / pairs : 1;  // about two blocks per compute unit
+  if (cpp > segs) cpp = segs;
+  if (cpp < 1) cpp = 1;
+  return ((segs + cpp - 1) / cpp) * kScoreSegment;
+}
+
+int64_t attend_partial_floats(int64_t pairs, int64_t T, int D) {
+  const int64_t chunk = attend_chunk(pairs, T);
+  return pairs * ((T + chunk - 1) / chunk) * kAttnWaves * kScoreHeads * (D + 4);
+}
+
+template <int D, int M, int BK, bool PCA, int BV>
+static hipError_t launch_attend_t(AttendArgs a, hipStream_t st) {
+  const int64_t pairs = (int64_t)a.k.B * a.k.Hkv;
+  a.chunk = attend_chunk(pairs, a.k.T);
+  a.chunks = (a.k.T + a.chunk - 1) / a.chunk;
+  const int64_t blocks = pairs * a.chunks;
+  if (blocks > 0x7FFFFFFF || (int64_t)a.k.B * a.k.Hq > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_attend<D, M, BK, PCA, BV>), dim3((unsigned)blocks), dim3(kScoreThreads), 0,
+                     st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_attend_combine<D>), dim3((unsigned)(a.k.B * a.k.Hq)), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int M, bool PCA>
+static hipError_t launch_attend_dm(int bk, int bv, const AttendArgs& a, hipStream_t st) {
+#define KVQ_BV(K)                                                  \
+  switch (bv) {                                                    \
+    case 1: return launch_attend_t<D, M, K, PCA, 1>(a, st);        \
+    case 2: return launch_attend_t<D, M, K, PCA, 2>(a, st);        \
+    case 3: return launch_attend_t<D, M, K, PCA, 3>(a, st);        \
+  }                                                                \
+  return hipErrorInvalidValue;
+  switch (bk) {
+    case 1: KVQ_BV(1)
+    case 2: KVQ_BV(2)
+    case 3: KVQ_BV(3)
+    case 4: KVQ_BV(4)
+  }
+#undef KVQ_BV
+  return hipErrorInvalidValue;
+}
+
+bool attend_supported(int D, int mk, int bk, int bv) {
+  if (bk < 1 || bk > 4 || bv < 1 || bv > 3) return false;
+  if (D == 64) return mk == 64 || mk == 32;
+  if (D == 128) return mk == 128 || mk == 64 || mk == 32;
+  return false;
+}
+
+hipError_t launch_attend(int D, int mk, int bk, int bv, const AttendArgs& a, hipStream_t st) {
+  if (a.k.T <= 0 || a.k.B <= 0 || a.k.Hq <= 0) return hipSuccess;
+  if (!attend_supported(D, mk, bk, bv)) return hipErrorInvalidValue;
+  if (D == 64) {
+    if (mk == 64) return launch_attend_dm<64, 64, false>(bk, bv, a, st);
+    return launch_attend_dm<64, 32, true>(bk, bv, a, st);
+  }
+  if (mk == 128) return launch_attend_dm<128, 128, false>(bk, bv, a, st);
+  if (mk == 64) return launch_attend_dm<128, 64, true>(bk, bv, a, st);
+  return launch_attend_dm<128, 32, true>(bk, bv, a, st);
 }
 
 // Compute units of the current device (queried once per device).

@@ -82,10 +82,15 @@ def lib() -> ctypes.CDLL:
         L.kvq_append_evict_chunk.argtypes = [PC, ctypes.POINTER(ctypes.POINTER(_Cache)), I32,
                                              ctypes.POINTER(ctypes.c_void_p), I64, P,
                                              ctypes.POINTER(ctypes.c_int64)]
+        L.kvq_attend_workspace_bytes.argtypes = [PC, I32, I32, I64]
+        L.kvq_attend_workspace_bytes.restype = ctypes.c_size_t
+        L.kvq_attend_packed.argtypes = [PC, PC, P, I32, I32, I64, I64, P, P, I32, I64, I64, I64,
+                                        ctypes.c_float, ctypes.c_float, P, I64, I64, P,
+                                        ctypes.c_size_t, P]
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_abi_version.restype = ctypes.c_int32
         for name in ("kvq_codec_tables", "kvq_encode", "kvq_decode", "kvq_score_packed",
-                     "kvq_cache_init", "kvq_append_evict_chunk"):
+                     "kvq_attend_packed", "kvq_cache_init", "kvq_append_evict_chunk"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -209,6 +214,29 @@ def score_packed(codec: Codec, q: torch.Tensor, records: torch.Tensor, Hkv: int,
     _check(lib().kvq_score_packed(codec.ref, _ptr(q), B, Hq, q.stride(0), q.stride(1),
                                   _ptr(records), Hkv, T, rec_sb, rec_sh, _ptr(out),
                                   out.stride(0), out.stride(1), _stream(q)))
+    return out
+
+
+def attend_workspace_bytes(vcodec: Codec, B: int, Hkv: int, T: int) -> int:
+    return int(lib().kvq_attend_workspace_bytes(vcodec.ref, B, Hkv, T))
+
+
+def attend_packed(kcodec: Codec, vcodec: Codec, q: torch.Tensor, krecords: torch.Tensor,
+                  vrecords: torch.Tensor, Hkv: int, T: int, rec_sb: int, rec_sh: int,
+                  softmax_scale: float, softcap: float = 0.0, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """q: bf16 [B, Hq, D] (last dim contiguous); K and V record (b, kv, t) at index
+    b*rec_sb + kv*rec_sh + t of krecords / vrecords. Returns f32 [B, Hq, D]."""
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    need = attend_workspace_bytes(vcodec, B, Hkv, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().kvq_attend_packed(kcodec.ref, vcodec.ref, _ptr(q), B, Hq, q.stride(0),
+                                   q.stride(1), _ptr(krecords), _ptr(vrecords), Hkv, T, rec_sb,
+                                   rec_sh, softmax_scale, softcap, _ptr(out), out.stride(0),
+                                   out.stride(1), _ptr(workspace), workspace.numel(), _stream(q)))
     return out
 
 

@@ -123,6 +123,34 @@ def test_score_argument_refusals():
                    P(FAKE), 80, 10, None)[0] == "KVQ_E_OUTLIER"
 
 
+def test_attend_argument_refusals():
+    L = kvq.lib()
+    P = ctypes.c_void_p
+    kc, vc = kvq.Codec(128, 3), kvq.Codec(128, 2)
+    ws = L.kvq_attend_workspace_bytes(vc.ref, 2, 2, 1000)
+    assert ws > 0 and ws % 16 == 0
+
+    def call(kc_, vc_, B=2, Hq=8, Hkv=2, T=1000, scale=0.1, cap=0.0, wsb=ws, q=FAKE):
+        return _status(L.kvq_attend_packed, kc_.ref, vc_.ref, P(q), B, Hq, 1024, 128, P(FAKE),
+                       P(FAKE), Hkv, T, 2000, 1000, scale, cap, P(FAKE), 1024, 128, P(FAKE), wsb,
+                       None)
+
+    assert call(kc, kvq.Codec(128, 4))[0] == "KVQ_E_ARG"           # V bits 4
+    assert call(kc, kvq.Codec(128, 2, outlier_T=2.0))[0] == "KVQ_E_OUTLIER"
+    assert call(kc, kvq.Codec(64, 2))[0] == "KVQ_E_DIM"            # head_dim differs
+    assert call(kvq.Codec(256, 3), kvq.Codec(256, 2))[0] == "KVQ_E_ARG"  # head_dim 256
+    name, msg = call(kc, vc, T=0)
+    assert name == "KVQ_E_ARG" and "T=0" in msg
+    name, msg = call(kc, vc, Hq=18)
+    assert name == "KVQ_E_ARG" and "Hq/Hkv=9" in msg
+    name, msg = call(kc, vc, wsb=ws - 16)
+    assert name == "KVQ_E_ARG" and "workspace" in msg
+    assert call(kc, vc, cap=-1.0)[0] == "KVQ_E_ARG"
+    assert call(kc, vc, scale=float("nan"))[0] == "KVQ_E_ARG"
+    assert call(kc, vc, q=FAKE + 2)[0] == "KVQ_E_STRIDE"
+    assert call(kc, vc, B=0)[0] == "KVQ_OK"                         # nothing to do, nothing launched
+
+
 def test_cache_refusals():
     L = kvq.lib()
     cd = kvq.Codec(512, 4)
