@@ -23,9 +23,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-gpu-rdc"]
 
 
-# Per-source extras. The rotation kernels keep MFMA results in architectural VGPRs (the
-# quantiser reads every one of them; accumulator registers would cost a move each).
-EXTRA = {"kvq_encode_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# Per-source extras. The matrix-core kernels keep MFMA results in architectural VGPRs: the
+# quantiser or the softmax reads every one of them (accumulator registers would cost a move
+# each), and the unified register file then holds two attention waves per SIMD.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
+EXTRA = {"kvq_encode_mx.hip": _VGPR_FORM, "kvq_score.hip": _VGPR_FORM}
 
 
 def _compile(src: str, verbose: bool) -> str:

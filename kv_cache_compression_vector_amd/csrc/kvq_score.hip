@@ -408,6 +408,28 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
   floatx4_t acc[CT];  // acc[ct][i]: position 16 ct + 4 oct + i of head tok
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) acc[ct] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  // records of the unit starting at token t0: K words of token tok of both tiles, V record
+  // dwords of the 32 tokens (tokens past the end read the last record and get weight 0)
+  constexpr int kUnits = kScoreSegment / (32 * kAttnWaves);  // units per wave and segment
+  uint32_t wk_n[2][NWK], vv_n[VPL];
+  auto load_unit = [&](int64_t t0) {
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      int64_t t = t0 + 16 * tile + tok;
+      t = t < t_end ? t : t_end - 1;
+      const uint32_t* r32 = krec32 + (rowbase + t) * NWK;
+#pragma unroll
+      for (int i = 0; i < NWK; ++i) wk_n[tile][i] = r32[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int idx = lane + 64 * i;
+      int64_t t = t0 + idx / NWV;
+      t = t < t_end ? t : t_end - 1;
+      vv_n[i] = idx < 32 * NWV ? vrec32[(rowbase + t) * NWV + idx % NWV] : 0u;
+    }
+  };
+  if (t_begin + 32 * wave < t_end) load_unit(t_begin + 32 * wave);
   int cur = -1;
   const int64_t n_seg = (t_end - t_begin + kScoreSegment - 1) / kScoreSegment;
   for (int64_t sg = 0; sg < n_seg; ++sg) {
@@ -419,31 +441,24 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
       query_operands<M>(qs, qmu, tok, oct, qa_hi, qa_lo, qm);
       cur = bi;
     }
-    for (int u = 0; u < kScoreSegment / (32 * kAttnWaves); ++u) {
+    for (int u = 0; u < kUnits; ++u) {
       const int64_t t0 = s0 + 32 * (kAttnWaves * u + wave);
       if (t0 >= t_end) break;  // wave-uniform
-      // records: K words of token tok of both tiles; V records of the 32 tokens into LDS
-      // (tokens past the end read the last record and get weight 0)
+      // this unit's records (prefetched during the previous one) to LDS / registers, and the
+      // next unit's loads in flight while this one computes
       uint32_t wk[2][NWK];
 #pragma unroll
-      for (int tile = 0; tile < 2; ++tile) {
-        int64_t t = t0 + 16 * tile + tok;
-        t = t < t_end ? t : t_end - 1;
-        const uint32_t* r32 = krec32 + (rowbase + t) * NWK;
+      for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-        for (int i = 0; i < NWK; ++i) wk[tile][i] = r32[i];
-      }
-      uint32_t vv[VPL];
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        const int idx = lane + 64 * i;
-        int64_t t = t0 + idx / NWV;
-        t = t < t_end ? t : t_end - 1;
-        vv[i] = idx < 32 * NWV ? vrec32[(rowbase + t) * NWV + idx % NWV] : 0u;
-      }
+        for (int i = 0; i < NWK; ++i) wk[tile][i] = wk_n[tile][i];
 #pragma unroll
       for (int i = 0; i < VPL; ++i)
-        if (lane + 64 * i < 32 * NWV) vst[wave][lane + 64 * i] = vv[i];
+        if (lane + 64 * i < 32 * NWV) vst[wave][lane + 64 * i] = vv_n[i];
+      {
+        const int un = u + 1 < kUnits ? u + 1 : 0;
+        const int64_t tn = (u + 1 < kUnits ? s0 : s0 + kScoreSegment) + 32 * (kAttnWaves * un + wave);
+        if (tn < t_end) load_unit(tn);
+      }
       // logits of heads 4 oct + kk for tokens t0 + tok and t0 + 16 + tok
       float lg[2][4];
 #pragma unroll
