@@ -183,6 +183,7 @@ static hipError_t launch_decode_m(int bits, bool ol, bool bf16, const DecodeArgs
 
 hipError_t launch_decode(int D, int m, int bits, bool ol, bool bf16, const DecodeArgs& a,
                          hipStream_t st) {
+  if (decode_h_supported(D, m, ol)) return launch_decode_h(m, bits, bf16, a, st);
   if (D != m) {
     if (ol) return hipErrorInvalidValue;  // projection codecs carry no outlier list
     return launch_decode_pca(D, m, bits, bf16, a, st);

@@ -1,0 +1,318 @@
+// kvq_decode_h.hip — Hadamard-codec decode (m = 64, 128) with the inverse rotation split between
+// the matrix cores and the vector ALUs.
+//
+// x^ = (n/m) s (.) H_m z^ [kakeyaturbo PR #15, "M4 Phase A" (inverse rotation, then the norm),
+// "M5" (decode)]. In Sylvester order H_m = H_NB (x) H_32 with NB = m/32 (coordinate i = 32a + b,
+// H_m[32a' + b'][32a + b] = H_NB[a'][a] H_32[b'][b]), so
+//   y_a = H_32 z^_a           on MFMA for each 32-coordinate block a (entries +-1, exact in bf16;
+//                             z^ as bf16 hi + lo),
+//   x^_a' = sum_a H_NB[a'][a] y_a   as log2(NB) butterfly stages in registers,
+// which leaves log2(NB) of the log2(m) butterfly stages on the vector ALUs (2 of 7 at m = 128)
+// and needs no LDS operands: the H_32 fragments are formed once per wave in registers.
+//
+// Layout (16 vectors per MFMA tile, lane l: vector n = l % 16, group q = l / 16):
+//  - H_32's columns are permuted so that the 8 k-values of lane group q are the coordinates
+//    b = 8 q' + e' with e' = 2q + e/4, q' = e % 4, e = 0..7. Coordinate 32a + 8q' + e' has plane
+//    position e' m/8 + 4a + q', so for every block a the lane's coordinates are two runs of 4
+//    consecutive bits, (2q + r) m/8 mod 32 + 4a + [0, 4) for r = 0, 1, of one record word group
+//    (q m/128). A lane reads b + 1 words of its vector's record, and two coordinates' bit pairs
+//    index a table of their centroids' bf16 hi pair and lo pair (the MFMA operand words).
+//  - H_32's rows are permuted so that the two 16-row output tiles t give lane group q the
+//    output coordinates b' = 8q + 4t + [0, 4): after both, 8 consecutive outputs per block, one
+//    16-byte chunk. bf16 rows are assembled in LDS and leave as whole rows, 1 KB per store
+//    instruction.
+#include "kvq_device.h"
+#include "kvq_kernels.h"
+#include "kvq_mfma.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int kDhWaves = 4;
+constexpr int kDhVT = 2;  // 16-vector tiles per wave step
+
+template <int BITS>
+constexpr int dh_copies() { return BITS <= 3 ? 32 : 4; }
+
+// Pair index of the coordinates at bits sh + pr, sh + pr + 1 of the BITS plane words w
+// (bit 2p + i = plane p of coordinate i), from the planes' bytes at sh gathered into y.
+template <int BITS>
+__device__ __forceinline__ uint32_t gather_bytes(const uint32_t* w, int sh) {
+  uint32_t y = __builtin_amdgcn_ubfe(w[0], sh, 8);
+  if constexpr (BITS >= 2) y |= __builtin_amdgcn_ubfe(w[1], sh, 8) << 8;
+  if constexpr (BITS >= 3) y |= __builtin_amdgcn_ubfe(w[2], sh, 8) << 16;
+  if constexpr (BITS >= 4) y |= __builtin_amdgcn_ubfe(w[3], sh, 8) << 24;
+  return y;
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t pair_of(uint32_t y, int pr) {
+  if constexpr (BITS == 1) {
+    return (y >> pr) & 3u;
+  } else if constexpr (BITS == 2 || BITS == 3) {
+    // y = a + b 2^8 (+ c 2^16), a, b, c < 4 after the mask: y (2^16 + 2^10 (+ 2^4)) holds
+    // a + 4 b (+ 16 c) in bits 16.. and nothing else reaches or carries into those bits
+    const uint32_t mask = (BITS == 3 ? 0x030303u : 0x0303u) << pr;
+    const uint32_t prod = __umul24(y & mask, BITS == 3 ? 0x10410u : 0x10400u);
+    return __builtin_amdgcn_ubfe(prod, 16 + pr, 2 * BITS);
+  } else {
+    uint32_t idx = 0;
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) idx |= ((y >> (8 * p + pr)) & 3u) << (2 * p);
+    return idx;
+  }
+}
+
+// Pair table: entry e (bit 2p + i = plane p of code i) = the two centroids as a bf16 hi pair
+// (lut[e C + c]) and lo pair (lut[(NPAIR + e) C + c]), copy c read by lanes l % C == c.
+template <int BITS, int C>
+__device__ __forceinline__ void fill_pairs(const Tables& tab, uint32_t* lut, int tid, int nthr) {
+  constexpr int NPAIR = 1 << (2 * BITS);
+  for (int i = tid; i < NPAIR * C; i += nthr) {
+    const int e = i / C;
+    uint32_t ca = 0, cb = 0;
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) {
+      ca |= ((e >> (2 * p)) & 1u) << p;
+      cb |= ((e >> (2 * p + 1)) & 1u) << p;
+    }
+    float va = 0.0f, vb = 0.0f;
+#pragma unroll
+    for (int k = 0; k < (1 << BITS); ++k) {
+      va = (uint32_t)k == ca ? tab.c[k] : va;
+      vb = (uint32_t)k == cb ? tab.c[k] : vb;
+    }
+    const uint32_t ha = f32_to_bf16_rne(va), hb = f32_to_bf16_rne(vb);
+    const uint32_t la = f32_to_bf16_rne(va - __uint_as_float(ha << 16));
+    const uint32_t lb = f32_to_bf16_rne(vb - __uint_as_float(hb << 16));
+    lut[i] = ha | (hb << 16);
+    lut[NPAIR * C + i] = la | (lb << 16);
+  }
+}
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const f2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
+}  // namespace
+
+template <int M, int BITS, bool BF16>
+__global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
+  constexpr int NB = M / 32, NWC = (M / 32) * BITS, NWT = NWC + 1;
+  constexpr int C = dh_copies<BITS>(), NPAIR = 1 << (2 * BITS);
+  __shared__ uint32_t lut[2 * NPAIR * C];
+  // bf16 rows of a wave's step (16 kDhVT rows of M bf16 = M/8 16-byte chunks, chunk index
+  // XOR-swizzled with the row so the row-wise writes and chunk-wise reads spread over banks)
+  constexpr int RCH = M / 8;
+  __shared__ uint4 stage[BF16 ? kDhWaves * 16 * kDhVT * RCH : 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n16 = lane & 15, q = lane >> 4;
+  fill_pairs<BITS, C>(a.tab, lut, tid, 64 * kDhWaves);
+  // A operands (H_32, permuted) of the two output tiles: row m -> b' = 8 (m/4) + 4t + m % 4,
+  // column k = 8q + e -> b = 8 (e % 4) + 2q + e / 4
+  uint4 A[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int bo = 8 * (n16 >> 2) + 4 * t + (n16 & 3);
+    uint32_t w[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int e = 2 * h + s;
+        const int bi = 8 * (e & 3) + 2 * q + (e >> 2);
+        v |= (0x3F80u | (((uint32_t)__builtin_popcount(bo & bi) & 1u) << 15)) << (16 * s);
+      }
+      w[h] = v;
+    }
+    A[t] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  // signs of this lane's outputs d = 32 a' + 8q + [0, 8), as bf16-pair (or f32) sign masks:
+  // byte q of sign word a' (a wave-uniform index, so a scalar load)
+  uint32_t sg[NB][4];
+#pragma unroll
+  for (int ap = 0; ap < NB; ++ap) {
+    const uint32_t byte = (a.tab.sign_words[ap] >> (8 * q)) & 0xFFu;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {  // outputs 2h, 2h + 1 of the byte
+      const uint32_t s0 = (byte >> (2 * h)) & 1u, s1 = (byte >> (2 * h + 1)) & 1u;
+      sg[ap][h] = BF16 ? ((s0 << 15) | (s1 << 31)) : (s0 | (s1 << 1));
+    }
+  }
+  __syncthreads();
+  const uint32_t* rec32 = reinterpret_cast<const uint32_t*>(a.rec);
+  const int64_t n_steps = (a.n + 16 * kDhVT - 1) / (16 * kDhVT);
+  const int64_t stride = (int64_t)gridDim.x * kDhWaves;
+  // the lane's words (group q, all planes) and the norm of the vectors of a step
+  auto load = [&](int64_t st, uint32_t (&w)[kDhVT][BITS + 1]) {
+#pragma unroll
+    for (int vt = 0; vt < kDhVT; ++vt) {
+      int64_t v = st * 16 * kDhVT + 16 * vt + n16;
+      v = v < a.n ? v : a.n - 1;
+      const uint32_t* r = rec32 + v * NWT;
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) w[vt][p] = r[(q * M / 128) * BITS + p];
+      w[vt][BITS] = r[NWC];
+    }
+  };
+  int64_t st = (int64_t)blockIdx.x * kDhWaves + wave;
+  uint32_t wn[kDhVT][BITS + 1];
+  if (st < n_steps) load(st, wn);
+  // let the first step's words land before the loop, so the wait at the loop head only covers
+  // the path round the loop, where the previous step's stores may stay in flight
+  // (vmcnt(0) expcnt(7) lgkmcnt(15))
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  for (; st < n_steps; st += stride) {
+    uint32_t w[kDhVT][BITS + 1];
+#pragma unroll
+    for (int vt = 0; vt < kDhVT; ++vt)
+#pragma unroll
+      for (int p = 0; p <= BITS; ++p) w[vt][p] = wn[vt][p];
+    if (st + stride < n_steps) load(st + stride, wn);  // in flight during this step
+#pragma unroll
+    for (int vt = 0; vt < kDhVT; ++vt) {
+      floatx4 y[NB][2];
+#pragma unroll
+      for (int ab = 0; ab < NB; ++ab) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t yb = gather_bytes<BITS>(w[vt], ((2 * q + half) * (M / 8)) % 32 + 4 * ab);
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const uint32_t idx = pair_of<BITS>(yb, 2 * s);
+            hi[2 * half + s] = lut[idx * C + (lane & (C - 1))];
+            lo[2 * half + s] = lut[(NPAIR + idx) * C + (lane & (C - 1))];
+          }
+        }
+        const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        const uint4 bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          floatx4 c = {0.f, 0.f, 0.f, 0.f};
+          c = mfma_bf16(A[t], bh, c);
+          c = mfma_bf16(A[t], bl, c);
+          y[ab][t] = c;
+        }
+      }
+      // H_NB across the blocks (Sylvester: the partner of block a at stage h is a ^ h)
+#pragma unroll
+      for (int h = 1; h < NB; h <<= 1)
+#pragma unroll
+        for (int ab = 0; ab < NB; ++ab)
+          if ((ab & h) == 0) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const floatx4 u = y[ab][t], v = y[ab + h][t];
+              y[ab][t] = u + v;
+              y[ab + h][t] = u - v;
+            }
+          }
+      const float sc = __uint_as_float(w[vt][BITS]) * a.tab.inv_m;
+      if constexpr (BF16) {
+        const int row = 16 * vt + n16;
+#pragma unroll
+        for (int ap = 0; ap < NB; ++ap) {
+          const floatx4 y0 = y[ap][0], y1 = y[ap][1];
+          const int ch = 4 * ap + q;  // columns 32 a' + 8q .. + 7
+          stage[(wave * 16 * kDhVT + row) * RCH + (ch ^ (row & (RCH - 1)))] =
+              make_uint4(bf16_pair(y0[0] * sc, y0[1] * sc) ^ sg[ap][0],
+                         bf16_pair(y0[2] * sc, y0[3] * sc) ^ sg[ap][1],
+                         bf16_pair(y1[0] * sc, y1[1] * sc) ^ sg[ap][2],
+                         bf16_pair(y1[2] * sc, y1[3] * sc) ^ sg[ap][3]);
+        }
+      } else {
+        int64_t v = st * 16 * kDhVT + 16 * vt + n16;
+        // a lane past the end decoded the last record: it stores the last row's own bytes again
+        v = v < a.n ? v : a.n - 1;
+#pragma unroll
+        for (int ap = 0; ap < NB; ++ap) {
+          const floatx4 y0 = y[ap][0], y1 = y[ap][1];
+          const float o[8] = {y0[0] * sc, y0[1] * sc, y0[2] * sc, y0[3] * sc,
+                              y1[0] * sc, y1[1] * sc, y1[2] * sc, y1[3] * sc};
+          float* yp = static_cast<float*>(a.y) + v * a.ld + 32 * ap + 8 * q;
+          float r[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            r[j] = __uint_as_float(__float_as_uint(o[j]) ^ (((sg[ap][j >> 1] >> (j & 1)) & 1u) << 31));
+          *reinterpret_cast<float4*>(yp) = make_float4(r[0], r[1], r[2], r[3]);
+          *reinterpret_cast<float4*>(yp + 4) = make_float4(r[4], r[5], r[6], r[7]);
+        }
+      }
+    }
+    if constexpr (BF16) {
+      // whole rows: each instruction writes 64 consecutive 16-byte chunks of the step's rows
+      __builtin_amdgcn_wave_barrier();
+      constexpr int CH = 16 * kDhVT * RCH / 64;
+      uint4 out[CH];
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        const int id = 64 * k + lane, row = id / RCH, ch = id % RCH;
+        out[k] = stage[(wave * 16 * kDhVT + row) * RCH + (ch ^ (row & (RCH - 1)))];
+      }
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        const int id = 64 * k + lane, row = id / RCH, ch = id % RCH;
+        int64_t v = st * 16 * kDhVT + row;
+        v = v < a.n ? v : a.n - 1;  // rows past the end hold the last row's own bytes
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + v * a.ld + 8 * ch) = out[k];
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+// Compute units of the current device (queried once per device).
+static int dh_device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int M, int BITS>
+static hipError_t launch_dh_t(bool bf16, const DecodeArgs& a, hipStream_t st) {
+  // one resident round (4 blocks of 4 waves per compute unit, measured best against 2 and 8);
+  // waves stride over the steps
+  const int64_t steps = (a.n + 16 * kDhVT - 1) / (16 * kDhVT);
+  int64_t blocks = (steps + kDhWaves - 1) / kDhWaves;
+  const int64_t resident = 4 * (int64_t)dh_device_cus();
+  if (blocks > resident) blocks = resident;
+  const dim3 g((unsigned)blocks), b(64 * kDhWaves);
+  if (bf16) hipLaunchKernelGGL((k_decode_h<M, BITS, true>), g, b, 0, st, a);
+  else hipLaunchKernelGGL((k_decode_h<M, BITS, false>), g, b, 0, st, a);
+  return hipGetLastError();
+}
+
+template <int M>
+static hipError_t launch_dh_m(int bits, bool bf16, const DecodeArgs& a, hipStream_t st) {
+  switch (bits) {
+    case 1: return launch_dh_t<M, 1>(bf16, a, st);
+    case 2: return launch_dh_t<M, 2>(bf16, a, st);
+    case 3: return launch_dh_t<M, 3>(bf16, a, st);
+    case 4: return launch_dh_t<M, 4>(bf16, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool decode_h_supported(int D, int m, bool outliers) { return !outliers && D == m && (m == 64 || m == 128); }
+
+hipError_t launch_decode_h(int m, int bits, bool bf16, const DecodeArgs& a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  if (m == 64) return launch_dh_m<64>(bits, bf16, a, st);
+  if (m == 128) return launch_dh_m<128>(bits, bf16, a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq
