@@ -186,6 +186,7 @@ hipError_t launch_decode(int D, int m, int bits, bool ol, bool bf16, const Decod
   if (decode_h_supported(D, m, ol)) return launch_decode_h(m, bits, bf16, a, st);
   if (D != m) {
     if (ol) return hipErrorInvalidValue;  // projection codecs carry no outlier list
+    if (decode_pca_h_supported(D, m)) return launch_decode_pca_h(D, m, bits, bf16, a, st);
     return launch_decode_pca(D, m, bits, bf16, a, st);
   }
   switch (m) {

@@ -267,6 +267,224 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Projection-codec decode, x^ = mu + B diag(s) v', v' = (n/r) H_r z^ [kakeyaturbo PR #15, "M5":
+// inverse rotation, then the unprojection on the matrix engine]. The rotation is split as above
+// (H_r = H_{r/32} (x) H_32). After it each lane holds, for every 32-coordinate block, the 8
+// consecutive coordinates 32a + 8q + [0, 8) of its vector, which is exactly the unprojection's
+// MFMA B operand for k-step a; so v' goes from the accumulators into the second product without
+// leaving the registers (split into bf16 hi + lo: the basis is exact in bf16, v' is not). The
+// basis (signs folded into its columns, exact) is the A operand from LDS; the accumulator starts
+// at mu. Its rows are permuted within each pair of 16-row tiles so that a lane ends with 8
+// consecutive output columns (one 16-byte chunk); bf16 rows are assembled in LDS and stored
+// whole. A block takes 128 consecutive vectors per tile (one basis: basis blocks are multiples
+// of 256 rows) and re-stages the basis only when it changes.
+
+constexpr int kDpWaves = 4;
+constexpr int kDpVT = 2;                           // 16-vector tiles per wave and block tile
+constexpr int kDpRows = 16 * kDpVT * kDpWaves;     // vectors per block tile
+
+__device__ __forceinline__ int dp_out_col(int mt, int m) {
+  return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
+}
+
+template <int D, int R, int BITS, bool BF16>
+__global__ __launch_bounds__(64 * kDpWaves) void k_decode_pca_h(DecodeArgs a, int64_t tiles_per_block) {
+  constexpr int NB = R / 32, MT = D / 16, HCH = R / 8, RCH = D / 8;
+  constexpr int NWC = (R / 32) * BITS, NWT = NWC + 1;
+  constexpr int C = dh_copies<BITS>(), NPAIR = 1 << (2 * BITS);
+  constexpr int HMASK = (HCH < 16 ? HCH : 16) - 1;
+  __shared__ uint32_t lut[2 * NPAIR * C];
+  __shared__ uint4 s_B[D * HCH];                      // basis rows, chunk c at c ^ (row & HMASK)
+  __shared__ __attribute__((aligned(16))) float s_mu[D];
+  __shared__ uint4 stage[BF16 ? kDpWaves * 16 * RCH : 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n16 = lane & 15, q = lane >> 4;
+  fill_pairs<BITS, C>(a.tab, lut, tid, 64 * kDpWaves);
+  uint4 Ah[2];  // H_32 fragments, as in k_decode_h
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int bo = 8 * (n16 >> 2) + 4 * t + (n16 & 3);
+    uint32_t w[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int e = 2 * h + s;
+        const int bi = 8 * (e & 3) + 2 * q + (e >> 2);
+        v |= (0x3F80u | (((uint32_t)__builtin_popcount(bo & bi) & 1u) << 15)) << (16 * s);
+      }
+      w[h] = v;
+    }
+    Ah[t] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  const uint32_t* rec32 = reinterpret_cast<const uint32_t*>(a.rec);
+  const int64_t n_tiles = (a.n + kDpRows - 1) / kDpRows;
+  const int64_t t0 = blockIdx.x * tiles_per_block;
+  const int64_t t1 = t0 + tiles_per_block < n_tiles ? t0 + tiles_per_block : n_tiles;
+  auto load = [&](int64_t tile, uint32_t (&w)[kDpVT][BITS + 1]) {
+#pragma unroll
+    for (int vt = 0; vt < kDpVT; ++vt) {
+      int64_t v = tile * kDpRows + 32 * wave + 16 * vt + n16;
+      v = v < a.n ? v : a.n - 1;
+      const uint32_t* r = rec32 + v * NWT;
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) w[vt][p] = r[(q * R / 128) * BITS + p];
+      w[vt][BITS] = r[NWC];
+    }
+  };
+  // basis-index entry of a tile, loaded with its records and range-checked where it is used;
+  // tiles advance by kDpRows <= block_rows rows, so the entry advances by at most one per tile
+  const bool multi = a.pca.count > 1;
+  int64_t ib = multi ? t0 * kDpRows / a.pca.block_rows : 0;
+  int64_t ib_end = multi ? (ib + 1) * a.pca.block_rows : 0;
+  auto basis_raw = [&](int64_t tile) -> int {
+    if (!multi) return 0;
+    if (tile * kDpRows >= ib_end) {
+      ++ib;
+      ib_end += a.pca.block_rows;
+    }
+    return a.pca.index[ib];
+  };
+  uint32_t wn[kDpVT][BITS + 1];
+  int bn = 0, cur = -1;
+  if (t0 < t1) {
+    load(t0, wn);
+    bn = basis_raw(t0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loop head then waits only for its own loads
+  for (int64_t tile = t0; tile < t1; ++tile) {
+    int bi = __builtin_amdgcn_readfirstlane(bn);  // block-uniform
+    bi = bi < 0 ? 0 : (bi >= a.pca.count ? a.pca.count - 1 : bi);
+    if (bi != cur) {
+      __syncthreads();
+      const uint4* Bk = reinterpret_cast<const uint4*>(a.pca.basis + (int64_t)bi * D * R);
+      for (int e = tid; e < D * HCH; e += 64 * kDpWaves) {
+        const uint4 w = Bk[e];
+        const int row = e / HCH, c = e % HCH, j0 = 8 * c;  // signs of columns j0 .. j0 + 7
+        s_B[row * HCH + (c ^ (row & HMASK))] =
+            make_uint4(w.x ^ a.tab.sign_pairs[j0 / 2], w.y ^ a.tab.sign_pairs[j0 / 2 + 1],
+                       w.z ^ a.tab.sign_pairs[j0 / 2 + 2], w.w ^ a.tab.sign_pairs[j0 / 2 + 3]);
+      }
+      const float* mu = a.pca.mean ? a.pca.mean + (int64_t)bi * D : nullptr;
+      for (int i = tid; i < D; i += 64 * kDpWaves) s_mu[i] = mu ? mu[i] : 0.0f;
+      cur = bi;
+      __syncthreads();
+    }
+    uint32_t w[kDpVT][BITS + 1];
+#pragma unroll
+    for (int vt = 0; vt < kDpVT; ++vt)
+#pragma unroll
+      for (int p = 0; p <= BITS; ++p) w[vt][p] = wn[vt][p];
+    if (tile + 1 < t1) {  // in flight during this tile
+      load(tile + 1, wn);
+      bn = basis_raw(tile + 1);
+    }
+#pragma unroll
+    for (int vt = 0; vt < kDpVT; ++vt) {
+      // v' = (n/r) H_r z^ as B operands of the unprojection (k-step a: coordinates 32a + [0, 32))
+      floatx4 y[NB][2];
+#pragma unroll
+      for (int ab = 0; ab < NB; ++ab) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t yb = gather_bytes<BITS>(w[vt], ((2 * q + half) * (R / 8)) % 32 + 4 * ab);
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const uint32_t idx = pair_of<BITS>(yb, 2 * s);
+            hi[2 * half + s] = lut[idx * C + (lane & (C - 1))];
+            lo[2 * half + s] = lut[(NPAIR + idx) * C + (lane & (C - 1))];
+          }
+        }
+        const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        const uint4 bl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          floatx4 c = {0.f, 0.f, 0.f, 0.f};
+          c = mfma_bf16(Ah[t], bh, c);
+          c = mfma_bf16(Ah[t], bl, c);
+          y[ab][t] = c;
+        }
+      }
+      if constexpr (NB == 2) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const floatx4 u = y[0][t], v = y[1][t];
+          y[0][t] = u + v;
+          y[1][t] = u - v;
+        }
+      }
+      const float sc = __uint_as_float(w[vt][BITS]) * a.tab.inv_m;
+      uint4 vh[NB], vl[NB];
+#pragma unroll
+      for (int ab = 0; ab < NB; ++ab) {
+        const float x[8] = {y[ab][0][0] * sc, y[ab][0][1] * sc, y[ab][0][2] * sc, y[ab][0][3] * sc,
+                            y[ab][1][0] * sc, y[ab][1][1] * sc, y[ab][1][2] * sc, y[ab][1][3] * sc};
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          h[k] = bf16_pair(x[2 * k], x[2 * k + 1]);
+          l[k] = bf16_pair(x[2 * k] - __uint_as_float(h[k] << 16),
+                           x[2 * k + 1] - __uint_as_float(h[k] & 0xFFFF0000u));
+        }
+        vh[ab] = make_uint4(h[0], h[1], h[2], h[3]);
+        vl[ab] = make_uint4(l[0], l[1], l[2], l[3]);
+      }
+      int64_t v = (tile * kDpRows + 32 * wave + 16 * vt + n16);
+      v = v < a.n ? v : a.n - 1;  // a lane past the end decoded the last record
+#pragma unroll
+      for (int ap = 0; ap < MT / 2; ++ap) {
+        floatx4 o[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int mt = 2 * ap + hh;
+          const float4 m4 = *reinterpret_cast<const float4*>(s_mu + dp_out_col(mt, 4 * q));
+          floatx4 c = {m4.x, m4.y, m4.z, m4.w};
+          const int row = dp_out_col(mt, n16);
+#pragma unroll
+          for (int ks = 0; ks < NB; ++ks) {
+            const uint4 A = s_B[row * HCH + ((4 * ks + q) ^ (row & HMASK))];
+            c = mfma_bf16(A, vh[ks], c);
+            c = mfma_bf16(A, vl[ks], c);
+          }
+          o[hh] = c;
+        }
+        // columns 32 ap + 8q + [0, 8) of vector n16
+        if constexpr (BF16) {
+          stage[(wave * 16 + n16) * RCH + ((4 * ap + q) ^ (n16 & (RCH - 1)))] =
+              make_uint4(bf16_pair(o[0][0], o[0][1]), bf16_pair(o[0][2], o[0][3]),
+                         bf16_pair(o[1][0], o[1][1]), bf16_pair(o[1][2], o[1][3]));
+        } else {
+          float* yp = static_cast<float*>(a.y) + v * a.ld + 32 * ap + 8 * q;
+          *reinterpret_cast<float4*>(yp) = make_float4(o[0][0], o[0][1], o[0][2], o[0][3]);
+          *reinterpret_cast<float4*>(yp + 4) = make_float4(o[1][0], o[1][1], o[1][2], o[1][3]);
+        }
+      }
+      if constexpr (BF16) {
+        // the 16 rows leave whole: each instruction writes 64 consecutive 16-byte chunks
+        __builtin_amdgcn_wave_barrier();
+        constexpr int CH = 16 * RCH / 64;
+        uint4 out[CH];
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          const int id = 64 * k + lane, row = id / RCH, ch = id % RCH;
+          out[k] = stage[(wave * 16 + row) * RCH + (ch ^ (row & (RCH - 1)))];
+        }
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          const int id = 64 * k + lane, row = id / RCH, ch = id % RCH;
+          int64_t vr = tile * kDpRows + 32 * wave + 16 * vt + row;
+          vr = vr < a.n ? vr : a.n - 1;  // rows past the end hold the last row's own bytes
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + vr * a.ld + 8 * ch) = out[k];
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  }
+}
+
 // Compute units of the current device (queried once per device).
 static int dh_device_cus() {
   static int cus[64] = {0};
@@ -293,6 +511,48 @@ static hipError_t launch_dh_t(bool bf16, const DecodeArgs& a, hipStream_t st) {
   if (bf16) hipLaunchKernelGGL((k_decode_h<M, BITS, true>), g, b, 0, st, a);
   else hipLaunchKernelGGL((k_decode_h<M, BITS, false>), g, b, 0, st, a);
   return hipGetLastError();
+}
+
+template <int D, int R, int BITS>
+static hipError_t launch_dp_t(bool bf16, const DecodeArgs& a, hipStream_t st) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_pca_h<D, R, BITS, true>,
+                                                     64 * kDpWaves, 0) != hipSuccess || nb <= 0)
+      nb = 1;
+    per_cu = nb;
+  }
+  const int64_t tiles = (a.n + kDpRows - 1) / kDpRows;
+  const int64_t resident = (int64_t)per_cu * dh_device_cus();
+  const int64_t per = (tiles + resident - 1) / resident;
+  const dim3 g((unsigned)((tiles + per - 1) / per)), b(64 * kDpWaves);
+  if (bf16) hipLaunchKernelGGL((k_decode_pca_h<D, R, BITS, true>), g, b, 0, st, a, per);
+  else hipLaunchKernelGGL((k_decode_pca_h<D, R, BITS, false>), g, b, 0, st, a, per);
+  return hipGetLastError();
+}
+
+template <int D, int R>
+static hipError_t launch_dp_dr(int bits, bool bf16, const DecodeArgs& a, hipStream_t st) {
+  switch (bits) {
+    case 1: return launch_dp_t<D, R, 1>(bf16, a, st);
+    case 2: return launch_dp_t<D, R, 2>(bf16, a, st);
+    case 3: return launch_dp_t<D, R, 3>(bf16, a, st);
+    case 4: return launch_dp_t<D, R, 4>(bf16, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool decode_pca_h_supported(int D, int r) {
+  return (D == 64 && r == 32) || (D == 128 && r == 32) || (D == 128 && r == 64);
+}
+
+hipError_t launch_decode_pca_h(int D, int r, int bits, bool bf16, const DecodeArgs& a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  if (D == 64 && r == 32) return launch_dp_dr<64, 32>(bits, bf16, a, st);
+  if (D == 128 && r == 32) return launch_dp_dr<128, 32>(bits, bf16, a, st);
+  if (D == 128 && r == 64) return launch_dp_dr<128, 64>(bits, bf16, a, st);
+  return hipErrorInvalidValue;
 }
 
 template <int M>

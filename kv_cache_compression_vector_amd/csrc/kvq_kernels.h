@@ -118,6 +118,10 @@ hipError_t launch_decode(int D, int m, int bits, bool outliers, bool bf16_out,
 // Hadamard decode with the 32-point blocks of the inverse rotation on the matrix cores.
 bool decode_h_supported(int D, int m, bool outliers);
 hipError_t launch_decode_h(int m, int bits, bool bf16_out, const DecodeArgs& a, hipStream_t st);
+// Projection decode with the same split rotation feeding the unprojection from registers.
+bool decode_pca_h_supported(int D, int r);
+hipError_t launch_decode_pca_h(int D, int r, int bits, bool bf16_out, const DecodeArgs& a,
+                               hipStream_t st);
 hipError_t launch_score(int D, int m, int bits, int group, const ScoreArgs& a, hipStream_t st);
 // Attention: token chunk per block for (pairs, T), and the partial floats the launch writes.
 int64_t attend_chunk(int64_t pairs, int64_t T);
