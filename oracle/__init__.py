@@ -38,7 +38,7 @@ def build(force: bool = False) -> str:
 
 class _RefCodec(ctypes.Structure):
     _fields_ = [("D", ctypes.c_int32), ("bits", ctypes.c_int32), ("r", ctypes.c_int32),
-                ("pad", ctypes.c_int32), ("seed", ctypes.c_uint64), ("T", ctypes.c_double),
+                ("scale_rule", ctypes.c_int32), ("seed", ctypes.c_uint64), ("T", ctypes.c_double),
                 ("centroids", ctypes.c_void_p), ("basis", ctypes.c_void_p),
                 ("mean", ctypes.c_void_p)]
 
@@ -144,8 +144,12 @@ class Codec:
 
     def __init__(self, D: int, bits: int, seed: int, r: int = 0, T: float = 0.0,
                  centroids: np.ndarray | None = None, basis_bf16: np.ndarray | None = None,
-                 mean: np.ndarray | None = None):
+                 mean: np.ndarray | None = None, scale_rule: int = 0):
+        """scale_rule: the f32 scale a record stores: 0 the norm ||v||; 1 matched norm
+        (||x^|| = ||v||); 2 inner-product preserving (<x^, v> = ||v||^2); 3 least-squares
+        optimal (<v - x^, x^> = 0)."""
         self.D, self.bits, self.seed, self.r, self.T = D, bits, seed, r, float(T)
+        self.scale_rule = int(scale_rule)
         self.m = r if r > 0 else D
         if centroids is None:
             centroids = gaussian_table(bits)[1]
@@ -157,7 +161,7 @@ class Codec:
         self.rec_bytes = record_bytes(self.m, bits)
 
     def _c(self) -> _RefCodec:
-        return _RefCodec(self.D, self.bits, self.r, 0, self.seed, self.T,
+        return _RefCodec(self.D, self.bits, self.r, self.scale_rule, self.seed, self.T,
                          _p(self.centroids), _p(self.basis), _p(self.mean))
 
 

@@ -209,7 +209,8 @@ typedef struct {
   int32_t D;               /* head_dim                                                        */
   int32_t bits;            /* b                                                               */
   int32_t r;               /* 0 = no projection; else PCA rank                                */
-  int32_t pad;
+  int32_t scale_rule;      /* stored scale: 0 = ||v||, 1 = matched norm, 2 = inner-product     */
+                           /* preserving, 3 = least-squares optimal                           */
   uint64_t seed;           /* sign seed                                                       */
   double T;                /* outlier threshold, 0 = off                                      */
   const float* centroids;  /* f32[2^b] ascending                                              */
@@ -290,7 +291,24 @@ int64_t kvq_ref_encode(const ref_codec* cd, int64_t n, const uint16_t* x, int64_
       }
     }
     if (ol_off) ol_off[row + 1] = (uint32_t)total;
-    if (records) pack_record(code, m, b, (float)nrm, records + row * rb);
+    /* stored scale. Decode gives x^ = (scale/m) s .* H z^, so ||x^||^2 = scale^2 ||z^||^2 / m and
+     * <x^, v> = (scale/m) ||v|| <z, z^>. The rules [turboquant_plus log: EDEN and matched-norm
+     * scales]: 1 matched norm, ||x^|| = ||v||; 2 inner-product preserving (EDEN's S), <x^, v> =
+     * ||v||^2; 3 least-squares optimal (the per-vector MSE minimum), <v - x^, x^> = 0. */
+    double scale = nrm;
+    if (cd->scale_rule != 0 && nrm > 0.0) {
+      double zz = 0.0, zh2 = 0.0;
+      for (int i = 0; i < m; ++i) {
+        const double zh = (double)cd->centroids[code[i]];
+        zz += (u[i] / nrm) * zh;
+        zh2 += zh * zh;
+      }
+      /* a rule whose denominator is not positive keeps the plain norm */
+      if (cd->scale_rule == 1 && zh2 > 0.0) scale = nrm * sqrt((double)m / zh2);
+      else if (cd->scale_rule == 2 && zz > 0.0) scale = nrm * (double)m / zz;
+      else if (cd->scale_rule == 3 && zh2 > 0.0) scale = nrm * zz / zh2;
+    }
+    if (records) pack_record(code, m, b, (float)scale, records + row * rb);
   }
   return total;
 }

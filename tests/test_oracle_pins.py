@@ -372,6 +372,49 @@ def test_score_equals_rotated_domain_identity(D, bits):
 
 
 # ---------------------------------------------------------------------------------------------
+# Stored-scale rules (matched norm, inner-product preserving, least squares)
+
+
+@pytest.mark.parametrize("D,bits", [(64, 1), (128, 2), (128, 3), (512, 4)])
+def test_scale_rules_meet_their_defining_identities(D, bits):
+    """Decoded x^ of each rule: ||x^|| = ||x|| (matched), <x^, x> = ||x||^2 (inner product),
+    <x - x^, x^> = 0 (least squares); the codes are those of the plain rule."""
+    rng = np.random.default_rng(D + bits)
+    x = _bf16(rng.normal(size=(40, D)) * rng.lognormal(0.0, 1.0, size=(40, 1)))
+    xf = _bf16_to_f64(x)
+    plain = oracle.Codec(D, bits, seed=21)
+    base = oracle.encode(plain, x)
+    for rule in (1, 2, 3):
+        cd = oracle.Codec(D, bits, seed=21, scale_rule=rule)
+        out = oracle.encode(cd, x)
+        np.testing.assert_array_equal(out["codes"], base["codes"])
+        y = oracle.decode(cd, out["records"])
+        nx2 = (xf * xf).sum(1)
+        if rule == 1:
+            np.testing.assert_allclose(np.sqrt((y * y).sum(1)), np.sqrt(nx2), rtol=2e-7)
+        elif rule == 2:
+            np.testing.assert_allclose((y * xf).sum(1), nx2, rtol=2e-7)
+        else:
+            resid = ((xf - y) * y).sum(1)
+            assert np.all(np.abs(resid) <= 2e-7 * np.sqrt(nx2 * (y * y).sum(1)))
+
+
+def test_least_squares_rule_minimises_the_error_among_the_rules():
+    rng = np.random.default_rng(7)
+    x = _bf16(rng.normal(size=(64, 128)))
+    xf = _bf16_to_f64(x)
+    errs = []
+    for rule in (0, 1, 2, 3):
+        cd = oracle.Codec(128, 2, seed=3, scale_rule=rule)
+        y = oracle.decode(cd, oracle.encode(cd, x)["records"])
+        errs.append(((xf - y) ** 2).sum(1))
+    errs = np.array(errs)
+    assert np.all(errs[3] <= errs.min(axis=0) * (1 + 1e-6))
+    # the plain norm is not the per-vector optimum, so least squares is strictly better on average
+    assert errs[3].mean() < errs[0].mean()
+
+
+# ---------------------------------------------------------------------------------------------
 # Decode attention over packed K and V
 
 
