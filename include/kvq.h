@@ -59,10 +59,26 @@ typedef enum {
   KVQ_E_CAPACITY = 7,   /* a capacity is too small (outlier list, cache region, workspace) */
   KVQ_E_CACHE = 8,      /* cache struct not built by kvq_cache_init, or built for another codec */
   KVQ_E_DEVICE = 9,     /* HIP launch / runtime error                                    */
-  KVQ_E_ARG = 10        /* any other invalid argument (negative size, flags != 0, ...)   */
+  KVQ_E_ARG = 10        /* any other invalid argument (negative size, unknown flags, ...) */
 } kvq_status;
 
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+/* The f32 scale a record stores, chosen by codec->flags & KVQ_SCALE_RULE_MASK. Decode computes
+ * x^ = (scale/m) s (.) H z^ whatever the rule, so only encode changes [turboquant_plus log: the
+ * EDEN scales and the matched-norm scale]:
+ *   KVQ_SCALE_NORM     ||v||                          (the default)
+ *   KVQ_SCALE_MATCHED  ||v|| sqrt(m) / ||z^||          ||x^|| = ||v||
+ *   KVQ_SCALE_INNER    ||v|| m / <z, z^>               <x^, v> = ||v||^2 (inner-product preserving)
+ *   KVQ_SCALE_LSQ      ||v|| <z, z^> / ||z^||^2        <v - x^, x^> = 0 (least-squares optimal)
+ * with z = H (s (.) v) / ||v|| and z^ the chosen centroids. A rule whose denominator is not
+ * positive stores ||v||. Rules other than KVQ_SCALE_NORM need a Hadamard codec (proj_rank 0)
+ * without outlier list, and caches use KVQ_SCALE_NORM. */
+#define KVQ_SCALE_NORM 0u
+#define KVQ_SCALE_MATCHED 1u
+#define KVQ_SCALE_INNER 2u
+#define KVQ_SCALE_LSQ 3u
+#define KVQ_SCALE_RULE_MASK 3u
 
 /* Codec descriptor: caller-owned POD in host memory. */
 typedef struct kvq_codec {
@@ -72,7 +88,7 @@ typedef struct kvq_codec {
                                  r in {32, 64, 128}, r < D, D*r <= 32768: PCA projection to r
                                  coordinates (MFMA), then rotation over r (m = r). Projection
                                  codecs carry no outlier list.                               */
-  uint32_t flags;             /* reserved, must be 0                                         */
+  uint32_t flags;             /* bits 0..1: the stored scale (KVQ_SCALE_*); other bits 0     */
   uint64_t seed;              /* seed of the +-1 sign diagonal (SplitMix64 stream)           */
   float outlier_T;            /* 0: no side list. > 0: coordinates with |z| > T are listed
                                  (requires m <= 256). Units: rotated, normalised (z).        */

@@ -11,7 +11,43 @@
 
 namespace kvq {
 
-template <int M, int BITS, bool SYM>
+// The centroid the quantiser picks for rotated coordinate u (code = #{k : u > n t_k}), decided
+// with the quantiser's own thresholds. Symmetric tables: the magnitude cell from |u|, the sign
+// from u (u <= 0 takes the lower half: c[L/2 - 1 - j] = -c[L/2 + j]).
+template <int BITS, bool SYM>
+__device__ __forceinline__ float chosen_centroid(float u, const Quant<BITS, SYM>& q, const Tables& tab) {
+  constexpr int L = 1 << BITS, NT = Quant<BITS, SYM>::NT;
+  int cnt = 0;
+  if constexpr (SYM) {
+#pragma unroll
+    for (int k = 0; k < NT; ++k) cnt += fabsf(u) > q.thr[k] ? 1 : 0;
+    float mag = tab.c[L / 2];
+#pragma unroll
+    for (int j = 1; j < L / 2; ++j) mag = cnt == j ? tab.c[L / 2 + j] : mag;
+    return (q.nz && u > 0.0f) ? mag : -mag;
+  } else {
+#pragma unroll
+    for (int k = 0; k < NT; ++k) cnt += u > q.thr[k] ? 1 : 0;
+    float c = tab.c[0];
+#pragma unroll
+    for (int j = 1; j < L; ++j) c = cnt == j ? tab.c[j] : c;
+    return c;
+  }
+}
+
+// Stored scale of a rule from n = ||v||, zu = sum_i u_i z^_i (u = H (s .* v) = n z) and
+// zz = sum_i z^_i^2 [turboquant_plus log: EDEN and matched-norm scales]. Decode gives
+// x^ = (scale/m) s .* H z^, so: 1 matched norm n sqrt(m / zz) (||x^|| = ||v||); 2 inner-product
+// preserving n^2 m / zu (<x^, v> = ||v||^2); 3 least squares zu / zz (<v - x^, x^> = 0).
+// A rule whose denominator is not positive keeps the norm.
+__device__ __forceinline__ float rule_scale(int rule, float n, float zu, float zz, int m) {
+  if (rule == 1 && zz > 0.0f) return n * sqrtf((float)m / zz);
+  if (rule == 2 && zu > 0.0f) return n * n * (float)m / zu;
+  if (rule == 3 && zz > 0.0f) return zu / zz;
+  return n;
+}
+
+template <int M, int BITS, bool SYM, bool RULE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LV<M>::WAVES)))
 void k_encode(EncodeArgs a) {
   using L = LV<M>;
@@ -38,7 +74,19 @@ void k_encode(EncodeArgs a) {
     const float n = sqrtf(part_sum<L::Q>(ss));
     fwht_regs<L::K, 8>(v);
     fwht_cross<L::Q, L::K>(v, q);
-    quantize_store_lv<M, BITS, SYM>(v, n, valid, q, a.tab,
+    float stored = n;
+    if constexpr (RULE) {
+      const Quant<BITS, SYM> qq(a.tab, n);
+      float zu = 0.0f, zz = 0.0f;
+#pragma unroll
+      for (int i = 0; i < L::K; ++i) {
+        const float zh = chosen_centroid<BITS, SYM>(v[i], qq, a.tab);
+        zu = fmaf(v[i], zh, zu);
+        zz = fmaf(zh, zh, zz);
+      }
+      stored = n > 0.0f ? rule_scale(a.scale_rule, n, part_sum<L::Q>(zu), part_sum<L::Q>(zz), M) : 0.0f;
+    }
+    quantize_store_lv<M, BITS, SYM>(v, n, stored, valid, q, a.tab,
                                     reinterpret_cast<uint32_t*>(a.rec) + vec * NWT);
   }
 }
@@ -108,7 +156,7 @@ void k_encode_count(EncodeArgs a) {
     for (int k = 0; k < L::K; ++k) cnt += is_outlier(v[k], rn, a.tab.T) ? 1u : 0u;
     cnt += other_part_u32<L::Q>(cnt);
     if (valid && q == 0) a.ol_off[vec] = cnt;
-    quantize_store_lv<M, BITS, SYM>(v, n, valid, q, a.tab,
+    quantize_store_lv<M, BITS, SYM>(v, n, n, valid, q, a.tab,
                                     reinterpret_cast<uint32_t*>(a.rec) + vec * NWT);
   }
 }
@@ -321,7 +369,7 @@ void k_evict(EvictArgs a) {
     const float n = sqrtf(part_sum<L::Q>(ss));
     fwht_regs<L::K, 8>(v);
     fwht_cross<L::Q, L::K>(v, q);
-    quantize_store_lv<M, BITS, SYM>(v, n, true, q, a.tab,
+    quantize_store_lv<M, BITS, SYM>(v, n, n, true, q, a.tab,
                                     reinterpret_cast<uint32_t*>(ec.dst) + r * NWT);
   }
 }
@@ -372,7 +420,10 @@ static hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t st) {
   int64_t blocks = (n_iter + 3) / 4;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL((k_encode<M, BITS, SYM>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (a.scale_rule != 0)
+    hipLaunchKernelGGL((k_encode<M, BITS, SYM, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_encode<M, BITS, SYM, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -392,7 +443,8 @@ static hipError_t launch_encode_m(int bits, bool sym, const EncodeArgs& a, hipSt
 }
 
 hipError_t launch_encode(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
-  if (encode_mx_supported(m)) return launch_encode_mx(m, bits, sym, a, st);
+  // a scale rule needs the chosen centroids, which the lane-per-vector kernel forms
+  if (a.scale_rule == 0 && encode_mx_supported(m)) return launch_encode_mx(m, bits, sym, a, st);
   switch (m) {
     case 32: return launch_encode_m<32>(bits, sym, a, st);
     case 64: return launch_encode_m<64>(bits, sym, a, st);

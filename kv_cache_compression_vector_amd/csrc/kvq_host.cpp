@@ -109,7 +109,7 @@ uint64_t splitmix64_next(uint64_t& state) {
 // Codec validation
 
 struct Resolved {
-  int D, m, bits, L;
+  int D, m, bits, L, rule;
   bool pca, sym, outliers;
   kvq::Tables tab;
   kvq::Basis basis;
@@ -124,7 +124,10 @@ kvq_status resolve_codec(const kvq_codec* cd, Resolved& r) {
   if (!is_pow2_in(cd->head_dim, 64, 512))
     return fail(KVQ_E_DIM, "head_dim=%u not supported (64, 128, 256, 512)", cd->head_dim);
   if (cd->bits < 1 || cd->bits > 4) return fail(KVQ_E_BITS, "bits=%u outside 1..4", cd->bits);
-  if (cd->flags != 0) return fail(KVQ_E_ARG, "flags=%u must be 0", cd->flags);
+  if (cd->flags & ~KVQ_SCALE_RULE_MASK)
+    return fail(KVQ_E_ARG, "flags=%u: only the scale-rule bits (0x%x) may be set", cd->flags,
+                (unsigned)KVQ_SCALE_RULE_MASK);
+  r.rule = (int)(cd->flags & KVQ_SCALE_RULE_MASK);
   if (cd->reserved0 != 0) return fail(KVQ_E_ARG, "reserved0=%u must be 0", cd->reserved0);
   r.D = (int)cd->head_dim;
   r.bits = (int)cd->bits;
@@ -159,6 +162,9 @@ kvq_status resolve_codec(const kvq_codec* cd, Resolved& r) {
                 cd->proj_rank, (double)cd->outlier_T);
   if (r.outliers && r.m > 256)
     return fail(KVQ_E_OUTLIER, "outlier lists need coded length <= 256 (u8 index), got m=%d", r.m);
+  if (r.rule != 0 && (r.pca || r.outliers))
+    return fail(KVQ_E_ARG, "scale rule %d needs a Hadamard codec without outlier list "
+                "(proj_rank=%u, outlier_T=%g)", r.rule, cd->proj_rank, (double)cd->outlier_T);
   std::memset(&r.tab, 0, sizeof(r.tab));
   const float* c = cd->centroids_host ? cd->centroids_host : gaussian_centroids(r.bits);
   for (int k = 0; k < r.L; ++k) {
@@ -199,6 +205,7 @@ uint64_t codec_key(const kvq_codec* cd, const Resolved& r) {
   mix(&cd->proj_rank, 4);
   mix(&cd->seed, 8);
   mix(&cd->outlier_T, 4);
+  mix(&cd->flags, 4);
   mix(r.tab.c, sizeof(float) * r.L);
   return h;
 }
@@ -276,6 +283,7 @@ kvq_status kvq_encode(const kvq_codec* codec, const void* x_dev, int64_t n, int6
   a.n = n;
   a.rec = static_cast<uint8_t*>(records_dev);
   a.pca = r.basis;
+  a.scale_rule = r.rule;
   if (!r.outliers) {
     if (n == 0) return ok();
     if (r.pca) return from_hip(kvq::launch_encode_pca(r.D, r.m, r.bits, r.sym, a, s), "encode_pca");
@@ -469,9 +477,10 @@ kvq_status kvq_cache_init(const kvq_codec* codec, kvq_cache* cache, void* packed
   kvq_status st = resolve_codec(codec, r);
   if (st != KVQ_OK) return st;
   if (!cache) return fail(KVQ_E_NULL, "cache is NULL");
-  if (r.outliers || r.pca)
-    return fail(KVQ_E_ARG, "caches hold Hadamard records without outlier lists (proj_rank=%u, outlier_T=%g)",
-                codec->proj_rank, (double)codec->outlier_T);
+  if (r.outliers || r.pca || r.rule != 0)
+    return fail(KVQ_E_ARG, "caches hold Hadamard records with the plain norm and no outlier list "
+                "(proj_rank=%u, outlier_T=%g, flags=%u)", codec->proj_rank, (double)codec->outlier_T,
+                codec->flags);
   if (packed_cap < 0 || tail_cap <= 0 || window < 0 || margin < 0)
     return fail(KVQ_E_ARG, "packed_cap=%lld tail_cap=%lld window=%d margin=%d", (long long)packed_cap,
                 (long long)tail_cap, window, margin);

@@ -21,6 +21,8 @@ struct EncodeArgs {
   int64_t ol_cap;
   // PCA projection (PCA kernels only)
   Basis pca;                // PCA kernels only
+  // stored scale: 0 the norm; 1 matched norm; 2 inner-product preserving; 3 least squares
+  int32_t scale_rule, pad2;
 };
 
 struct DecodeArgs {

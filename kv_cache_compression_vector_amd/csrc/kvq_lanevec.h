@@ -383,18 +383,20 @@ __device__ __forceinline__ void load_words(const uint32_t* __restrict__ src, uin
   for (int i = (NWT / 4) * 4; i < NWT; ++i) w[i] = src[i];
 }
 
-// Encode one vector part (rotated coordinates u, norm n) and store the record.
+// Encode one vector part (rotated coordinates u, norm n) and store the record with `stored` as
+// its scale (the norm itself, or a scale rule's value).
 // Q == 1: the lane writes its whole record. Q > 1: lanes of a pair (q, q^1) merge their
 // halves; each lane of the pair stores the words of every other slot s; part 0 writes the norm.
 template <int M, int BITS, bool SYM>
-__device__ __forceinline__ void quantize_store_lv(float (&u)[LV<M>::K], float n, bool valid,
-                                                  int q, const Tables& tab, uint32_t* __restrict__ rec) {
+__device__ __forceinline__ void quantize_store_lv(float (&u)[LV<M>::K], float n, float stored,
+                                                  bool valid, int q, const Tables& tab,
+                                                  uint32_t* __restrict__ rec) {
   constexpr int Q = LV<M>::Q, NWC = (M / 32) * BITS, NWT = NWC + 1;
   if constexpr (Q == 1) {
     uint32_t w[NWT];
     uint32_t (&cw)[NWC] = *reinterpret_cast<uint32_t(*)[NWC]>(w);
     pack_vector<M, BITS, SYM>(u, n, tab, cw);
-    w[NWC] = __float_as_uint(n);
+    w[NWC] = __float_as_uint(stored);
     if (valid) store_words<NWT>(rec, w);
   } else {
     uint32_t half[8][BITS];
@@ -417,7 +419,7 @@ __device__ __forceinline__ void quantize_store_lv(float (&u)[LV<M>::K], float n,
         if constexpr (BITS == 1) d[0] = word[0];
       }
     }
-    if (valid && q == 0) rec[NWC] = __float_as_uint(n);
+    if (valid && q == 0) rec[NWC] = __float_as_uint(stored);
   }
 }
 

@@ -165,7 +165,7 @@ void k_encode_pca(EncodeArgs a, int64_t tiles_per_block) {
     __builtin_amdgcn_wave_barrier();
     const float n = sqrtf(ss);
     fwht_regs<R>(v);
-    quantize_store_lv<R, BITS, SYM>(v, n, vec < a.n, 0, a.tab,
+    quantize_store_lv<R, BITS, SYM>(v, n, n, vec < a.n, 0, a.tab,
                                     reinterpret_cast<uint32_t*>(a.rec) + vec * NWT);
   }
 }

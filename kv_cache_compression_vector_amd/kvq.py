@@ -119,7 +119,7 @@ class Codec:
                  outlier_T: float = 0.0, centroids=None, basis: torch.Tensor | None = None,
                  mean: torch.Tensor | None = None, flags: int = 0,
                  basis_index: torch.Tensor | None = None, basis_block_rows: int = 0):
-        self.head_dim, self.bits, self.seed = head_dim, bits, seed
+        self.head_dim, self.bits, self.seed, self.flags = head_dim, bits, seed, flags
         self.proj_rank, self.outlier_T = proj_rank, float(outlier_T)
         self.m = proj_rank if proj_rank else head_dim
         self._centroids = None if centroids is None else np.ascontiguousarray(centroids, np.float32)

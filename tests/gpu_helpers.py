@@ -74,4 +74,4 @@ def oracle_codec_like(codec, basis_host=None, mean_host=None) -> oracle.Codec:
     # the oracle builds its own Gaussian table; a custom table is an input given to both sides
     return oracle.Codec(codec.head_dim, codec.bits, seed=codec.seed, r=codec.proj_rank,
                         T=codec.outlier_T, centroids=codec._centroids, basis_bf16=basis_host,
-                        mean=mean_host)
+                        mean=mean_host, scale_rule=codec.flags & 3)

@@ -69,7 +69,8 @@ FAKE = 1 << 40  # a 16-byte-aligned non-NULL address; never dereferenced (valida
     (dict(head_dim=1024), "KVQ_E_DIM", "head_dim=1024"),
     (dict(bits=0), "KVQ_E_BITS", "bits=0"),
     (dict(bits=5), "KVQ_E_BITS", "bits=5"),
-    (dict(flags=1), "KVQ_E_ARG", "flags=1"),
+    (dict(flags=4), "KVQ_E_ARG", "flags=4"),
+    (dict(flags=2, outlier_T=2.0), "KVQ_E_ARG", "scale rule 2"),
     (dict(proj_rank=128), "KVQ_E_DIM", "proj_rank=128"),
     (dict(proj_rank=48), "KVQ_E_DIM", "proj_rank=48"),
     (dict(head_dim=512, outlier_T=2.0), "KVQ_E_OUTLIER", "m=512"),
@@ -156,6 +157,9 @@ def test_cache_refusals():
     cd = kvq.Codec(512, 4)
     c = kvq._Cache()
     P = ctypes.c_void_p
+    name, msg = _status(L.kvq_cache_init, kvq.Codec(512, 4, flags=3).ref, ctypes.byref(c), P(FAKE),
+                        100, P(FAKE), 200, 64, 16)
+    assert name == "KVQ_E_ARG" and "plain norm" in msg
     assert _status(L.kvq_cache_init, cd.ref, ctypes.byref(c), P(FAKE), 10, P(FAKE), 0, 8, 16)[0] == "KVQ_E_ARG"
     assert _status(L.kvq_cache_init, cd.ref, ctypes.byref(c), P(FAKE), 10, P(FAKE), 64, 8, 16)[0] == "KVQ_OK"
     assert L.kvq_cache_init(cd.ref, ctypes.byref(c), P(FAKE), 256, P(FAKE), 2000, 1024, 16) == 0

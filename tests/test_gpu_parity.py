@@ -244,3 +244,57 @@ def test_config1_full_roundtrip():
         yref = oracle.decode(oracle_codec_like(codec), rec)
         worst = compare_decoded(y.cpu().numpy(), yref, unpack_records(rec, 128, bits)[1], "config1")
         say(f"config1 {name}: mismatches {mism} flagged {flagged} worst decode err/||x|| {worst:.2e}")
+
+
+def _rule_scale(rule, n, z, zh, m):
+    """The stored scale of a rule in f64 from the norm, z and the chosen centroids."""
+    zu, zz = float((z * zh).sum()), float((zh * zh).sum())
+    if n == 0:
+        return 0.0
+    if rule == 1 and zz > 0:
+        return n * np.sqrt(m / zz)
+    if rule == 2 and zu > 0:
+        return n * m / zu
+    if rule == 3 and zz > 0:
+        return n * zu / zz
+    return n
+
+
+@pytest.mark.parametrize("rule", [1, 2, 3])
+@pytest.mark.parametrize("D,bits,custom", [(64, 1, False), (128, 2, False), (128, 3, True),
+                                           (256, 3, False), (512, 4, False)])
+def test_scale_rules_parity(rule, D, bits, custom):
+    """Codes equal the plain rule's; the stored scale matches the oracle's (recomputed from the
+    GPU's own codes where a boundary-flagged coordinate differs); the decoded vectors meet the
+    rule's identity."""
+    c = None
+    if custom:  # an asymmetric table takes the kernels' general compare path
+        c = oracle.gaussian_table(bits)[1].astype(np.float64)
+        c = (c * (1.0 + 0.05 * np.sin(np.arange(1 << bits))) + 0.03).astype(np.float32)
+    codec = kvq.Codec(D, bits, seed=70 + rule, centroids=c, flags=rule)
+    n = 777
+    x = _rows(n, D, seed=D + bits + rule, scale=1.5)
+    say(f"scale rule {rule} D={D} b={bits} custom={custom}")
+    rec = kvq.encode(codec, x)
+    torch.cuda.synchronize()
+    recn = rec.cpu().numpy()
+    ocd = oracle_codec_like(codec)
+    ref = oracle.encode(ocd, bf16_host(x))
+    gc, gs = unpack_records(recn, D, bits)
+    rc, rs = unpack_records(ref["records"], D, bits)
+    mism = gc != rc
+    assert not (mism & (ref["flags"] == 0)).any(), "unflagged code mismatch"
+    cen = ocd.centroids.astype(np.float64)
+    for v in range(n):
+        want = rs[v] if not mism[v].any() else _rule_scale(rule, ref["norms"][v], ref["z"][v],
+                                                           cen[gc[v]], D)
+        assert abs(gs[v] - want) <= 1e-5 * abs(want) + 1e-30, f"vector {v}: {gs[v]} vs {want}"
+    y = kvq.decode(codec, rec).double().cpu()
+    xf = torch.from_numpy((bf16_host(x).astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    if rule == 1:
+        torch.testing.assert_close(y.norm(dim=1), xf.norm(dim=1), rtol=1e-4, atol=0)
+    elif rule == 2:
+        torch.testing.assert_close((y * xf).sum(1), (xf * xf).sum(1), rtol=1e-4, atol=0)
+    else:
+        r = ((xf - y) * y).sum(1).abs()
+        assert torch.all(r <= 1e-4 * xf.norm(dim=1) * y.norm(dim=1))
