@@ -40,7 +40,7 @@ class _RefCodec(ctypes.Structure):
     _fields_ = [("D", ctypes.c_int32), ("bits", ctypes.c_int32), ("r", ctypes.c_int32),
                 ("scale_rule", ctypes.c_int32), ("seed", ctypes.c_uint64), ("T", ctypes.c_double),
                 ("centroids", ctypes.c_void_p), ("basis", ctypes.c_void_p),
-                ("mean", ctypes.c_void_p)]
+                ("mean", ctypes.c_void_p), ("unbasis", ctypes.c_void_p)]
 
 
 _lib = None
@@ -144,10 +144,16 @@ class Codec:
 
     def __init__(self, D: int, bits: int, seed: int, r: int = 0, T: float = 0.0,
                  centroids: np.ndarray | None = None, basis_bf16: np.ndarray | None = None,
-                 mean: np.ndarray | None = None, scale_rule: int = 0):
+                 mean: np.ndarray | None = None, scale_rule: int = 0,
+                 unbasis_bf16: np.ndarray | None = None):
         """scale_rule: the f32 scale a record stores: 0 the norm ||v||; 1 matched norm
         (||x^|| = ||v||); 2 inner-product preserving (<x^, v> = ||v||^2); 3 least-squares
-        optimal (<v - x^, x^> = 0)."""
+        optimal (<v - x^, x^> = 0).
+
+        unbasis_bf16: projection codecs only, the decode basis C ([D][r] bf16 bits): decode
+        returns mu + C v^ instead of mu + B v^ (score and attention follow decode). With
+        Sigma_q = L L^T, Q-preconditioning is basis = L B_w, unbasis = L^-T B_w, mean = L^-T mu_w
+        [kakeyaturbo PR #15: K_tilde = K @ L before the codec, the inverse factor after it]."""
         self.D, self.bits, self.seed, self.r, self.T = D, bits, seed, r, float(T)
         self.scale_rule = int(scale_rule)
         self.m = r if r > 0 else D
@@ -158,11 +164,14 @@ class Codec:
         self.mean = None if mean is None else np.ascontiguousarray(mean, np.float32)
         if r > 0 and (self.basis is None or self.basis.shape != (D, r)):
             raise ValueError("PCA codec needs a bf16 basis of shape [D][r]")
+        self.unbasis = None if unbasis_bf16 is None else np.ascontiguousarray(unbasis_bf16, np.uint16)
+        if self.unbasis is not None and (r == 0 or self.unbasis.shape != (D, r)):
+            raise ValueError("a decode basis needs a projection codec and shape [D][r]")
         self.rec_bytes = record_bytes(self.m, bits)
 
     def _c(self) -> _RefCodec:
         return _RefCodec(self.D, self.bits, self.r, self.scale_rule, self.seed, self.T,
-                         _p(self.centroids), _p(self.basis), _p(self.mean))
+                         _p(self.centroids), _p(self.basis), _p(self.mean), _p(self.unbasis))
 
 
 def encode(cd: Codec, x_bf16: np.ndarray, ol_cap: int | None = None) -> dict:

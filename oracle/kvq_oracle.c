@@ -216,6 +216,14 @@ typedef struct {
   const float* centroids;  /* f32[2^b] ascending                                              */
   const uint16_t* basis;   /* bf16 [D][r] (PCA only)                                          */
   const float* mean;       /* f32 [D] or NULL (PCA only)                                      */
+  const uint16_t* unbasis; /* bf16 [D][r] decode basis C, or NULL = basis (PCA only). Q-       */
+                           /* preconditioning with Sigma_q = L L^T [kakeyaturbo PR #15: the    */
+                           /* artefacts commit (K_tilde = K @ L), the full-recipe commit (K is */
+                           /* whitened before the codec and unwhitened after it) and "M6 Phase */
+                           /* B.2a" (whiten by the Cholesky factor before encode, multiply by  */
+                           /* its inverse after decode)] gives the pair basis = L B_w,          */
+                           /* unbasis = L^-T B_w, mean = L^-T mu_w for a whitened-domain fit   */
+                           /* (B_w, mu_w); B_w = I when nothing is projected away.             */
 } ref_codec;
 
 #define FLAG_NEAR_BOUNDARY 1u
@@ -336,11 +344,14 @@ void kvq_ref_decode(const ref_codec* cd, int64_t n, const uint8_t* records,
     fwht(w, m);
     double* yr = y + row * D;
     if (cd->r > 0) {
+      /* x^ = mu + C v^, C the decode basis (the projection basis itself unless a separate one
+         is given) */
+      const uint16_t* C = cd->unbasis ? cd->unbasis : cd->basis;
       double vh[512];
       for (int i = 0; i < m; ++i) vh[i] = (double)nrm32 * (double)s[i] * w[i] / m;
       for (int d = 0; d < D; ++d) {
         double acc = cd->mean ? (double)cd->mean[d] : 0.0;
-        for (int j = 0; j < m; ++j) acc += bf16_to_double(cd->basis[(int64_t)d * m + j]) * vh[j];
+        for (int j = 0; j < m; ++j) acc += bf16_to_double(C[(int64_t)d * m + j]) * vh[j];
         yr[d] = acc;
       }
     } else {

@@ -528,6 +528,100 @@ def test_pca_fit_residual_equals_discarded_eigenvalues():
 
 
 # ---------------------------------------------------------------------------------------------
+# Q-preconditioning: the projection pair (basis L B_w, decode basis L^-T B_w, mean L^-T mu_w)
+
+
+def _exact_whitening_factor(D, seed):
+    """A lower-triangular factor L whose inverse is exact in bf16: unit diagonal, subdiagonal
+    +-1/2, so (L^-1)[i][j] = prod_{k=j+1..i} (-a_k), a signed power of two (>= 2^-127)."""
+    a = np.random.default_rng(seed).choice([-0.5, 0.5], size=D - 1)
+    L = np.eye(D)
+    L[np.arange(1, D), np.arange(D - 1)] = a
+    Linv = np.eye(D)
+    for i in range(D):
+        for j in range(i):
+            Linv[i, j] = np.prod(-a[j:i])
+    assert np.array_equal(L @ Linv, np.eye(D))
+    return L, Linv
+
+
+def _bf16_exact(a):
+    bits = _bf16(a)
+    assert np.array_equal(_bf16_to_f64(bits).reshape(np.shape(a)), a)
+    return bits
+
+
+@pytest.mark.parametrize("D,bits", [(64, 2), (128, 3)])
+def test_q_preconditioning_error_in_the_query_metric(D, bits):
+    """Sigma_q = L L^T; whitening by L before the codec and by L^-T after it makes the
+    query-metric error (x - x^)^T Sigma_q (x - x^) equal the codec's own error on the whitened
+    vector, (1/m) ||n z - n32 z^||^2 (n32 the stored f32 scale). A transposed or swapped factor
+    on either side breaks the identity, as L is not symmetric."""
+    L, Linv = _exact_whitening_factor(D, seed=D + bits)
+    cd = oracle.Codec(D, bits, seed=6, r=D, basis_bf16=_bf16_exact(L),
+                      unbasis_bf16=_bf16_exact(Linv.T))
+    x = _bf16(np.random.default_rng(7).normal(size=(40, D)))
+    out = oracle.encode(cd, x)
+    y = oracle.decode(cd, out["records"])
+    e = _bf16_to_f64(x) - y
+    lhs = np.einsum("nd,de,ne->n", e, L @ L.T, e)
+    n32 = np.array([oracle.unpack_codes(D, bits, r)[1] for r in out["records"]], np.float64)
+    zhat = cd.centroids.astype(np.float64)[out["codes"]]
+    rhs = ((out["norms"][:, None] * out["z"] - n32[:, None] * zhat) ** 2).sum(1) / D
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-9)
+    # the whitened norm is what the record scales by
+    np.testing.assert_allclose(out["norms"], np.linalg.norm(_bf16_to_f64(x) @ L, axis=1), rtol=1e-12)
+
+
+def test_q_preconditioning_with_projection_and_mean():
+    """Whitened-domain projection B_w (r of the D coordinates) and mean mu_w: the query-metric
+    error splits into the discarded whitened energy plus the codec's error on the r kept
+    coordinates, ||(I - B_w B_w^T) L^T (x - mu)||^2 + (1/r) ||n z - n32 z^||^2."""
+    D, r, bits = 128, 64, 3
+    L, Linv = _exact_whitening_factor(D, seed=21)
+    keep = np.sort(np.random.default_rng(22).choice(D, size=r, replace=False))
+    Bw = np.eye(D)[:, keep]
+    mu_w = np.random.default_rng(23).normal(size=D)
+    mu = (Linv.T @ mu_w).astype(np.float32)
+    cd = oracle.Codec(D, bits, seed=8, r=r, basis_bf16=_bf16_exact(L @ Bw),
+                      unbasis_bf16=_bf16_exact(Linv.T @ Bw), mean=mu)
+    x = _bf16(np.random.default_rng(24).normal(size=(30, D)) * 2.0)
+    out = oracle.encode(cd, x)
+    y = oracle.decode(cd, out["records"])
+    xc = _bf16_to_f64(x) - mu.astype(np.float64)
+    e = _bf16_to_f64(x) - y
+    lhs = np.einsum("nd,de,ne->n", e, L @ L.T, e)
+    w = xc @ L                                   # whitened, centred rows (L^T (x - mu))
+    dropped = (w ** 2).sum(1) - (w[:, keep] ** 2).sum(1)
+    n32 = np.array([oracle.unpack_codes(r, bits, rec)[1] for rec in out["records"]], np.float64)
+    zhat = cd.centroids.astype(np.float64)[out["codes"]]
+    rhs = dropped + ((out["norms"][:, None] * out["z"] - n32[:, None] * zhat) ** 2).sum(1) / r
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-9)
+
+
+def test_q_preconditioning_score_is_the_whitened_dot_product():
+    """q . x^ = (L^-1 q) . (L^T x^): the score of a preconditioned record equals the score of
+    the whitened query against the plain record of the whitened row when L is a signed
+    permutation times powers of two (every product exact, so the two codecs see the same
+    vector)."""
+    D, bits = 64, 3
+    rng = np.random.default_rng(31)
+    P = np.eye(D)[rng.permutation(D)] * rng.choice([-1.0, 1.0], size=D)
+    L = P * (2.0 ** rng.integers(-2, 3, size=D))[None, :]
+    Linv = np.linalg.inv(L)
+    qp = oracle.Codec(D, bits, seed=9, r=D, basis_bf16=_bf16_exact(L),
+                      unbasis_bf16=_bf16_exact(Linv.T))
+    plain = oracle.Codec(D, bits, seed=9)
+    x = _bf16(rng.normal(size=(25, D)))
+    q = _bf16(rng.normal(size=(25, D)))
+    xw = _bf16_exact(_bf16_to_f64(x) @ L)
+    rec = oracle.encode(qp, x)["records"]
+    np.testing.assert_array_equal(rec, oracle.encode(plain, xw)["records"])
+    qw = _bf16_exact(_bf16_to_f64(q) @ Linv.T)
+    np.testing.assert_allclose(oracle.score(qp, q, rec), oracle.score(plain, qw, rec), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
 # Two-region cache model
 
 
