@@ -85,9 +85,10 @@ typedef struct kvq_codec {
   uint32_t head_dim;          /* D in {64, 128, 256, 512}                                    */
   uint32_t bits;              /* b in 1..4                                                   */
   uint32_t proj_rank;         /* 0: rotate all D coordinates (m = D).
-                                 r in {32, 64, 128}, r < D, D*r <= 32768: PCA projection to r
-                                 coordinates (MFMA), then rotation over r (m = r). Projection
-                                 codecs carry no outlier list.                               */
+                                 r in {32, 64, 128}, r < D, D*r <= 32768, or r = D for D in
+                                 {64, 128}: projection to r coordinates v = B^T (x - mu) (MFMA),
+                                 then rotation over r (m = r). Projection codecs carry no
+                                 outlier list.                                               */
   uint32_t flags;             /* bits 0..1: the stored scale (KVQ_SCALE_*); other bits 0     */
   uint64_t seed;              /* seed of the +-1 sign diagonal (SplitMix64 stream)           */
   float outlier_T;            /* 0: no side list. > 0: coordinates with |z| > T are listed
@@ -104,6 +105,16 @@ typedef struct kvq_codec {
                                     (b, kv, t) is b*rec_sb + kv*rec_sh + t.                     */
   const int32_t* basis_index_dev;   /* PCA with basis_count > 1: int32 per block, < basis_count;
                                        the caller guarantees it covers every block touched      */
+  const uint16_t* unbasis_dev;   /* projection codecs only: bf16 [basis_count][D][r], the decode
+                                    basis C (same layout and indexing as basis_dev). Decode gives
+                                    x^ = mu + C v^, the packed score and attention use C^T q. NULL:
+                                    C = B (an orthonormal PCA basis). Q-preconditioning
+                                    [kakeyaturbo PR #15: the artefacts commit (K_tilde = K @ L for
+                                    Sigma_q = L L^T), the full-recipe commit (whiten K before the
+                                    codec, unwhiten after it) and "M6 Phase B.2a"] is the pair
+                                    B = L B_w, C = L^-T B_w, mu = L^-T mu_w, with (B_w, mu_w) a fit
+                                    in the whitened domain (B_w = I, mu_w = 0 and r = D for
+                                    whitening alone): the transform costs no extra pass.        */
 } kvq_codec;
 
 /* Outlier side list, CSR by vector. Entry e of vector v is at offsets[v] + e; within a vector
@@ -195,7 +206,8 @@ kvq_status kvq_score_packed(const kvq_codec* codec, const void* q_dev, int32_t B
  * "Also: two silently-ignored kernel parameters"]. Neither K nor V is materialised: logits are
  * formed in the K codec's rotated domain, values are accumulated in the V codec's rotated
  * domain and rotated back once per query head.
- * kcodec: any codec kvq_score_packed accepts with head_dim 64 or 128 (projection ranks 32, 64).
+ * kcodec: any codec kvq_score_packed accepts with head_dim 64 or 128 (projection ranks 32, 64,
+ * or r = D).
  * vcodec: Hadamard (proj_rank 0), same head_dim, bits 1..3. Neither may carry an outlier list.
  * q_dev: bf16, row (b, h) at q_dev + b*q_sb + h*q_sh elements (16-byte aligned).
  * krec_dev / vrec_dev: record (b, kv, t) at index b*rec_sb + kv*rec_sh + t of each array.

@@ -181,10 +181,10 @@ static hipError_t launch_decode_m(int bits, bool ol, bool bf16, const DecodeArgs
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(int D, int m, int bits, bool ol, bool bf16, const DecodeArgs& a,
+hipError_t launch_decode(int D, int m, bool proj, int bits, bool ol, bool bf16, const DecodeArgs& a,
                          hipStream_t st) {
-  if (decode_h_supported(D, m, ol)) return launch_decode_h(m, bits, bf16, a, st);
-  if (D != m) {
+  if (!proj && decode_h_supported(D, m, ol)) return launch_decode_h(m, bits, bf16, a, st);
+  if (proj) {
     if (ol) return hipErrorInvalidValue;  // projection codecs carry no outlier list
     if (decode_pca_h_supported(D, m)) return launch_decode_pca_h(D, m, bits, bf16, a, st);
     return launch_decode_pca(D, m, bits, bf16, a, st);

@@ -112,7 +112,8 @@ struct Resolved {
   int D, m, bits, L, rule;
   bool pca, sym, outliers;
   kvq::Tables tab;
-  kvq::Basis basis;
+  kvq::Basis basis;    // encode side: v = B^T (x - mu)
+  kvq::Basis unbasis;  // decode side (decode, score, attention): x^ = mu + C v^
 };
 
 bool is_pow2_in(uint32_t v, uint32_t lo, uint32_t hi) {
@@ -136,8 +137,8 @@ kvq_status resolve_codec(const kvq_codec* cd, Resolved& r) {
   std::memset(&r.basis, 0, sizeof(r.basis));
   if (r.pca) {
     if (!kvq::pca_shape_supported((int)cd->head_dim, (int)cd->proj_rank))
-      return fail(KVQ_E_DIM, "proj_rank=%u with head_dim=%u not supported (r in {32,64,128}, r < D, D*r <= 32768)",
-                  cd->proj_rank, cd->head_dim);
+      return fail(KVQ_E_DIM, "proj_rank=%u with head_dim=%u not supported (r in {32,64,128}, r < D, "
+                  "D*r <= 32768, or r = D for D in {64,128})", cd->proj_rank, cd->head_dim);
     if (!cd->basis_dev) return fail(KVQ_E_NULL, "proj_rank=%u needs basis_dev", cd->proj_rank);
     if (cd->basis_count > 1) {
       if (!cd->basis_index_dev)
@@ -152,7 +153,11 @@ kvq_status resolve_codec(const kvq_codec* cd, Resolved& r) {
     r.basis.block_rows = cd->basis_count > 1 ? (int32_t)cd->basis_block_rows : 0;
   } else if (cd->basis_count > 1) {
     return fail(KVQ_E_ARG, "basis_count=%u without proj_rank", cd->basis_count);
+  } else if (cd->unbasis_dev) {
+    return fail(KVQ_E_ARG, "unbasis_dev needs a projection codec (proj_rank > 0)");
   }
+  r.unbasis = r.basis;
+  if (r.pca && cd->unbasis_dev) r.unbasis.basis = cd->unbasis_dev;
   r.m = r.pca ? (int)cd->proj_rank : r.D;
   if (!(cd->outlier_T >= 0.0f) || std::isinf(cd->outlier_T))
     return fail(KVQ_E_OUTLIER, "outlier_T=%g must be finite and >= 0", (double)cd->outlier_T);
@@ -343,8 +348,8 @@ kvq_status kvq_decode(const kvq_codec* codec, const void* records_dev, int64_t n
   }
   a.y = y_dev;
   a.ld = ld_y;
-  a.pca = r.basis;
-  return from_hip(kvq::launch_decode(r.D, r.m, r.bits, ol != nullptr, y_dtype == KVQ_BF16, a,
+  a.pca = r.unbasis;
+  return from_hip(kvq::launch_decode(r.D, r.m, r.pca, r.bits, ol != nullptr, y_dtype == KVQ_BF16, a,
                                      static_cast<hipStream_t>(stream)),
                   "decode");
 }
@@ -385,13 +390,13 @@ kvq_status kvq_score_packed(const kvq_codec* codec, const void* q_dev, int32_t B
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
-  a.pca = r.basis;
+  a.pca = r.unbasis;
   if (r.pca && r.basis.count > 1 &&
       (r.basis.block_rows % 256 || rec_sb % 256 || rec_sh % 256))
     return fail(KVQ_E_STRIDE,
                 "score with several bases needs basis_block_rows, rec_sb, rec_sh multiples of 256 "
                 "(got %d, %lld, %lld)", r.basis.block_rows, (long long)rec_sb, (long long)rec_sh);
-  return from_hip(kvq::launch_score(r.D, r.m, r.bits, group, a, static_cast<hipStream_t>(stream)),
+  return from_hip(kvq::launch_score(r.D, r.m, r.pca, r.bits, group, a, static_cast<hipStream_t>(stream)),
                   "score_packed");
 }
 
@@ -417,7 +422,7 @@ kvq_status kvq_attend_packed(const kvq_codec* kcodec, const kvq_codec* vcodec, c
     return fail(KVQ_E_OUTLIER, "attention reads codes and norms only: outlier_T must be 0 for K and V");
   if (rv.pca) return fail(KVQ_E_ARG, "the V codec must be Hadamard (proj_rank=0), got proj_rank=%u", vcodec->proj_rank);
   if (rk.D != rv.D) return fail(KVQ_E_DIM, "K head_dim=%d and V head_dim=%d differ", rk.D, rv.D);
-  if (!kvq::attend_supported(rk.D, rk.m, rk.bits, rv.bits))
+  if (!kvq::attend_supported(rk.D, rk.m, rk.pca, rk.bits, rv.bits))
     return fail(KVQ_E_ARG, "attention supports head_dim 64/128, K coded length 32..D, K bits 1..4, V bits 1..3 "
                 "(got D=%d, K m=%d b=%d, V b=%d)", rk.D, rk.m, rk.bits, rv.bits);
   if (B < 0 || Hq < 0 || Hkv < 0 || T < 0) return fail(KVQ_E_ARG, "negative size (B=%d Hq=%d Hkv=%d T=%lld)", B, Hq, Hkv, (long long)T);
@@ -457,7 +462,7 @@ kvq_status kvq_attend_packed(const kvq_codec* kcodec, const kvq_codec* vcodec, c
   a.k.B = B;
   a.k.Hq = Hq;
   a.k.Hkv = Hkv;
-  a.k.pca = rk.basis;
+  a.k.pca = rk.unbasis;
   a.tv = rv.tab;
   a.vrec = static_cast<const uint8_t*>(vrec_dev);
   a.part = static_cast<float*>(workspace_dev);
@@ -466,7 +471,7 @@ kvq_status kvq_attend_packed(const kvq_codec* kcodec, const kvq_codec* vcodec, c
   a.o_sh = o_sh;
   a.scale = softmax_scale;
   a.softcap = softcap;
-  return from_hip(kvq::launch_attend(rk.D, rk.m, rk.bits, rv.bits, a, static_cast<hipStream_t>(stream)),
+  return from_hip(kvq::launch_attend(rk.D, rk.m, rk.pca, rk.bits, rv.bits, a, static_cast<hipStream_t>(stream)),
                   "attend_packed");
 }
 

@@ -115,7 +115,8 @@ bool pca_shape_supported(int D, int r);
 hipError_t launch_encode_pca(int D, int r, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
 hipError_t launch_decode_pca(int D, int r, int bits, bool bf16_out, const DecodeArgs& a,
                              hipStream_t st);
-hipError_t launch_decode(int D, int m, int bits, bool outliers, bool bf16_out,
+// proj: a projection codec (a.pca holds the decode basis), also when m == D.
+hipError_t launch_decode(int D, int m, bool proj, int bits, bool outliers, bool bf16_out,
                          const DecodeArgs& a, hipStream_t st);
 // Hadamard decode with the 32-point blocks of the inverse rotation on the matrix cores.
 bool decode_h_supported(int D, int m, bool outliers);
@@ -124,12 +125,12 @@ hipError_t launch_decode_h(int m, int bits, bool bf16_out, const DecodeArgs& a, 
 bool decode_pca_h_supported(int D, int r);
 hipError_t launch_decode_pca_h(int D, int r, int bits, bool bf16_out, const DecodeArgs& a,
                                hipStream_t st);
-hipError_t launch_score(int D, int m, int bits, int group, const ScoreArgs& a, hipStream_t st);
+hipError_t launch_score(int D, int m, bool proj, int bits, int group, const ScoreArgs& a, hipStream_t st);
 // Attention: token chunk per block for (pairs, T), and the partial floats the launch writes.
 int64_t attend_chunk(int64_t pairs, int64_t T);
 int64_t attend_partial_floats(int64_t pairs, int64_t T, int D);
-bool attend_supported(int D, int mk, int bk, int bv);
-hipError_t launch_attend(int D, int mk, int bk, int bv, const AttendArgs& a, hipStream_t st);
+bool attend_supported(int D, int mk, bool proj, int bk, int bv);
+hipError_t launch_attend(int D, int mk, bool proj, int bk, int bv, const AttendArgs& a, hipStream_t st);
 hipError_t launch_evict(int m, int bits, bool sym, const EvictArgs& a, hipStream_t st);
 hipError_t launch_tail_copy(const TailCopyArgs& a, hipStream_t st);
 hipError_t launch_clear_u32(uint32_t* p, int64_t n_words, hipStream_t st);

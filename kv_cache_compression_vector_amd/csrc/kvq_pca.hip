@@ -302,7 +302,8 @@ void k_decode_pca(DecodeArgs a, int64_t tiles_per_block) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Launchers. Supported (D, r): r in {32, 64, 128}, r <= D/2, D*r <= 32768.
+// Launchers. Supported (D, r): r in {32, 64, 128}, r <= D/2, D*r <= 32768, and r = D for D in
+// {64, 128} (a square transform such as a whitening factor, then the rotation over all D).
 
 // Blocks take consecutive tiles (consecutive tiles share a basis), as many as keeps the grid
 // within what the chip holds at once.
@@ -363,8 +364,8 @@ static hipError_t dec_dr(int bits, bool bf16, const DecodeArgs& a, hipStream_t s
   return hipErrorInvalidValue;
 }
 
-#define KVQ_PCA_PAIRS(X) X(64, 32) X(128, 32) X(128, 64) X(256, 32) X(256, 64) X(256, 128) \
-                         X(512, 32) X(512, 64)
+#define KVQ_PCA_PAIRS(X) X(64, 32) X(64, 64) X(128, 32) X(128, 64) X(128, 128) X(256, 32) \
+                         X(256, 64) X(256, 128) X(512, 32) X(512, 64)
 
 bool pca_shape_supported(int D, int r) {
 #define KVQ_PCA_CASE(d, rr) if (D == d && r == rr) return true;

@@ -658,21 +658,24 @@ static hipError_t launch_attend_dm(int bk, int bv, const AttendArgs& a, hipStrea
   return hipErrorInvalidValue;
 }
 
-bool attend_supported(int D, int mk, int bk, int bv) {
+// K: Hadamard (mk = D) or a projection to mk in {32, 64} or mk = D.
+bool attend_supported(int D, int mk, bool proj, int bk, int bv) {
   if (bk < 1 || bk > 4 || bv < 1 || bv > 3) return false;
-  if (D == 64) return mk == 64 || mk == 32;
-  if (D == 128) return mk == 128 || mk == 64 || mk == 32;
-  return false;
+  if (D != 64 && D != 128) return false;
+  if (!proj) return mk == D;
+  return mk == 32 || mk == 64 || mk == D;
 }
 
-hipError_t launch_attend(int D, int mk, int bk, int bv, const AttendArgs& a, hipStream_t st) {
+hipError_t launch_attend(int D, int mk, bool proj, int bk, int bv, const AttendArgs& a, hipStream_t st) {
   if (a.k.T <= 0 || a.k.B <= 0 || a.k.Hq <= 0) return hipSuccess;
-  if (!attend_supported(D, mk, bk, bv)) return hipErrorInvalidValue;
+  if (!attend_supported(D, mk, proj, bk, bv)) return hipErrorInvalidValue;
   if (D == 64) {
-    if (mk == 64) return launch_attend_dm<64, 64, false>(bk, bv, a, st);
+    if (!proj) return launch_attend_dm<64, 64, false>(bk, bv, a, st);
+    if (mk == 64) return launch_attend_dm<64, 64, true>(bk, bv, a, st);
     return launch_attend_dm<64, 32, true>(bk, bv, a, st);
   }
-  if (mk == 128) return launch_attend_dm<128, 128, false>(bk, bv, a, st);
+  if (!proj) return launch_attend_dm<128, 128, false>(bk, bv, a, st);
+  if (mk == 128) return launch_attend_dm<128, 128, true>(bk, bv, a, st);
   if (mk == 64) return launch_attend_dm<128, 64, true>(bk, bv, a, st);
   return launch_attend_dm<128, 32, true>(bk, bv, a, st);
 }
@@ -729,10 +732,11 @@ static hipError_t launch_score_dm(int bits, const ScoreArgs& a, hipStream_t st) 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_score(int D, int m, int bits, int group, const ScoreArgs& a, hipStream_t st) {
+hipError_t launch_score(int D, int m, bool proj, int bits, int group, const ScoreArgs& a, hipStream_t st) {
   if (a.T <= 0 || a.B <= 0 || a.Hkv <= 0) return hipSuccess;
   if (group < 1 || group > 8) return hipErrorInvalidValue;
-  if (D == m) {
+  if (!proj) {
+    if (D != m) return hipErrorInvalidValue;
     switch (m) {
       case 64: return launch_score_dm<64, 64, false>(bits, a, st);
       case 128: return launch_score_dm<128, 128, false>(bits, a, st);
@@ -743,8 +747,8 @@ hipError_t launch_score(int D, int m, int bits, int group, const ScoreArgs& a, h
   }
 #define KVQ_CASE(d, r) \
   if (D == d && m == r) return launch_score_dm<d, r, true>(bits, a, st);
-  KVQ_CASE(64, 32) KVQ_CASE(128, 32) KVQ_CASE(128, 64) KVQ_CASE(256, 32) KVQ_CASE(256, 64)
-  KVQ_CASE(256, 128) KVQ_CASE(512, 32) KVQ_CASE(512, 64)
+  KVQ_CASE(64, 32) KVQ_CASE(64, 64) KVQ_CASE(128, 32) KVQ_CASE(128, 64) KVQ_CASE(128, 128)
+  KVQ_CASE(256, 32) KVQ_CASE(256, 64) KVQ_CASE(256, 128) KVQ_CASE(512, 32) KVQ_CASE(512, 64)
 #undef KVQ_CASE
   return hipErrorInvalidValue;
 }

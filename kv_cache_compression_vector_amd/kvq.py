@@ -37,7 +37,7 @@ class _Codec(ctypes.Structure):
                 ("reserved0", ctypes.c_uint32), ("centroids_host", ctypes.c_void_p),
                 ("basis_dev", ctypes.c_void_p), ("mean_dev", ctypes.c_void_p),
                 ("basis_count", ctypes.c_uint32), ("basis_block_rows", ctypes.c_uint32),
-                ("basis_index_dev", ctypes.c_void_p)]
+                ("basis_index_dev", ctypes.c_void_p), ("unbasis_dev", ctypes.c_void_p)]
 
 
 class _Outliers(ctypes.Structure):
@@ -113,17 +113,19 @@ def _ptr(t: torch.Tensor | None):
 class Codec:
     """Codec descriptor. centroids: host f32 array (or None = Gaussian Lloyd-Max).
     PCA: basis device bf16 [D, r] or [k, D, r]; mean device f32 [D] or [k, D] (optional);
-    with k > 1 bases, basis_index (device int32, one per block of basis_block_rows rows)."""
+    with k > 1 bases, basis_index (device int32, one per block of basis_block_rows rows);
+    unbasis: the decode basis (same shape as basis), or None = basis."""
 
     def __init__(self, head_dim: int, bits: int, seed: int = 42, proj_rank: int = 0,
                  outlier_T: float = 0.0, centroids=None, basis: torch.Tensor | None = None,
                  mean: torch.Tensor | None = None, flags: int = 0,
-                 basis_index: torch.Tensor | None = None, basis_block_rows: int = 0):
+                 basis_index: torch.Tensor | None = None, basis_block_rows: int = 0,
+                 unbasis: torch.Tensor | None = None):
         self.head_dim, self.bits, self.seed, self.flags = head_dim, bits, seed, flags
         self.proj_rank, self.outlier_T = proj_rank, float(outlier_T)
         self.m = proj_rank if proj_rank else head_dim
         self._centroids = None if centroids is None else np.ascontiguousarray(centroids, np.float32)
-        self.basis, self.mean, self.basis_index = basis, mean, basis_index
+        self.basis, self.mean, self.basis_index, self.unbasis = basis, mean, basis_index, unbasis
         count = 0 if basis is None else (basis.shape[0] if basis.dim() == 3 else 1)
         if basis is not None:
             assert basis.dtype == torch.bfloat16 and basis.is_contiguous()
@@ -131,12 +133,15 @@ class Codec:
             assert mean.dtype == torch.float32 and mean.is_contiguous()
         if basis_index is not None:
             assert basis_index.dtype == torch.int32 and basis_index.is_contiguous()
+        if unbasis is not None:
+            assert unbasis.dtype == torch.bfloat16 and unbasis.is_contiguous()
         self._c = _Codec(head_dim, bits, proj_rank, flags, seed, self.outlier_T, 0,
                          None if self._centroids is None else self._centroids.ctypes.data,
                          None if basis is None else basis.data_ptr(),
                          None if mean is None else mean.data_ptr(),
                          count, basis_block_rows,
-                         None if basis_index is None else basis_index.data_ptr())
+                         None if basis_index is None else basis_index.data_ptr(),
+                         None if unbasis is None else unbasis.data_ptr())
 
     @property
     def ref(self):

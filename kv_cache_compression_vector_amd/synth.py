@@ -16,6 +16,13 @@ device the data will live on. Recipes:
                              per (layer, head), drawn without replacement, scaled x16
   pca_basis_from_calibration top-r eigenvectors of the centred covariance of a calibration slice
                              (the frozen, one-time fit the codec is given as an input)
+  query_covariance           synthetic Sigma_q = U diag(lambda) U^T: U Haar-random orthogonal,
+                             lambda log-spaced over [1, cond] (the pages report a median condition
+                             number of 4506 for real pre-RoPE query covariances), trace = D
+  q_precondition_codec_inputs  the one-time host calibration of Q-preconditioning: the Cholesky
+                             factor L of Sigma_q, optionally a PCA fit on whitened calibration rows,
+                             folded into the projection pair (basis, decode basis, mean) that the
+                             codec is given as inputs
 """
 from __future__ import annotations
 
@@ -123,6 +130,40 @@ def pca_basis_from_calibration(calib_bf16: torch.Tensor, rank: int):
             basis[:, j] = -basis[:, j]
     basis_bf16 = torch.from_numpy(basis.astype(np.float32)).to(torch.bfloat16)
     return mu.astype(np.float32), basis_bf16
+
+
+def query_covariance(head_dim: int, cond: float, seed: int) -> np.ndarray:
+    """Synthetic query covariance Sigma_q [D][D] (f64): Haar-random eigenvectors (QR of a
+    Gaussian matrix, column signs fixed by R's diagonal), eigenvalues log-spaced over [1, cond]
+    and scaled to trace D."""
+    rng = np.random.default_rng(seed)
+    z = rng.normal(size=(head_dim, head_dim))
+    q, r = np.linalg.qr(z)
+    q = q * np.sign(np.diag(r))[None, :]
+    lam = np.exp(np.linspace(0.0, np.log(cond), head_dim))
+    lam *= head_dim / lam.sum()
+    return (q * lam) @ q.T
+
+
+def q_precondition_codec_inputs(sigma_q: np.ndarray, calib_bf16: torch.Tensor | None = None,
+                                rank: int = 0):
+    """Projection pair for a Q-preconditioned codec, from Sigma_q = L L^T (L lower Cholesky).
+
+    Whitening alone (rank 0): basis = L, decode basis = L^-T, no mean (coded length D).
+    With a calibration slice and rank r: (mu_w, B_w) = the PCA fit of the whitened rows
+    (calib @ L), then basis = L B_w, decode basis = L^-T B_w, mean = L^-T mu_w.
+    Returns (basis bf16 [D][r], decode basis bf16 [D][r], mean f32 [D] or None)."""
+    L = np.linalg.cholesky(sigma_q)
+    Lit = np.linalg.inv(L).T
+    if rank == 0:
+        enc, dec, mean = L, Lit, None
+    else:
+        x = calib_bf16.float().cpu().double().numpy() @ L
+        mu_w, bw = pca_basis_from_calibration(torch.from_numpy(x).to(torch.bfloat16), rank)
+        bw = bw.float().double().numpy()
+        enc, dec, mean = L @ bw, Lit @ bw, (Lit @ mu_w.astype(np.float64)).astype(np.float32)
+    as_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16)
+    return as_bf16(enc), as_bf16(dec), mean
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

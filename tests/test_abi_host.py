@@ -71,7 +71,8 @@ FAKE = 1 << 40  # a 16-byte-aligned non-NULL address; never dereferenced (valida
     (dict(bits=5), "KVQ_E_BITS", "bits=5"),
     (dict(flags=4), "KVQ_E_ARG", "flags=4"),
     (dict(flags=2, outlier_T=2.0), "KVQ_E_ARG", "scale rule 2"),
-    (dict(proj_rank=128), "KVQ_E_DIM", "proj_rank=128"),
+    (dict(head_dim=64, proj_rank=128), "KVQ_E_DIM", "proj_rank=128"),
+    (dict(head_dim=256, proj_rank=256), "KVQ_E_DIM", "proj_rank=256"),
     (dict(proj_rank=48), "KVQ_E_DIM", "proj_rank=48"),
     (dict(head_dim=512, outlier_T=2.0), "KVQ_E_OUTLIER", "m=512"),
     (dict(outlier_T=-1.0), "KVQ_E_OUTLIER", "outlier_T"),
@@ -86,6 +87,23 @@ def test_codec_refusals(kw, status, needle):
                         ctypes.c_void_p(FAKE), None, None, None)
     assert name == status and needle in msg, msg
     assert kvq.lib().kvq_record_bytes(cd.ref) == 0
+
+
+def test_decode_basis_needs_a_projection_codec():
+    cd = kvq.Codec(128, 3)
+    cd._c.unbasis_dev = FAKE
+    name, msg = _status(kvq.lib().kvq_encode, cd.ref, ctypes.c_void_p(FAKE), 4, 128,
+                        ctypes.c_void_p(FAKE), None, None, None)
+    assert name == "KVQ_E_ARG" and "unbasis_dev" in msg, msg
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_square_projection_is_accepted(D):
+    """r = D (a whitening factor with no rank cut): records of D coordinates."""
+    cd = kvq.Codec(D, 3, proj_rank=D)
+    cd._c.basis_dev = FAKE
+    cd._c.unbasis_dev = FAKE
+    assert cd.record_bytes() == oracle.record_bytes(D, 3)
 
 
 def test_encode_argument_refusals():
