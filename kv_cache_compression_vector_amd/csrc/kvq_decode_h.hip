@@ -408,14 +408,19 @@ __global__ __launch_bounds__(64 * kDpWaves) void k_decode_pca_h(DecodeArgs a, in
           y[ab][t] = c;
         }
       }
-      if constexpr (NB == 2) {
+      // H_NB across the blocks (Sylvester: the partner of block a at stage h is a ^ h)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const floatx4 u = y[0][t], v = y[1][t];
-          y[0][t] = u + v;
-          y[1][t] = u - v;
-        }
-      }
+      for (int h = 1; h < NB; h <<= 1)
+#pragma unroll
+        for (int ab = 0; ab < NB; ++ab)
+          if ((ab & h) == 0) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const floatx4 u = y[ab][t], v = y[ab + h][t];
+              y[ab][t] = u + v;
+              y[ab + h][t] = u - v;
+            }
+          }
       const float sc = __uint_as_float(w[vt][BITS]) * a.tab.inv_m;
       uint4 vh[NB], vl[NB];
 #pragma unroll
@@ -544,14 +549,16 @@ static hipError_t launch_dp_dr(int bits, bool bf16, const DecodeArgs& a, hipStre
 }
 
 bool decode_pca_h_supported(int D, int r) {
-  return (D == 64 && r == 32) || (D == 128 && r == 32) || (D == 128 && r == 64);
+  return (D == 64 && (r == 32 || r == 64)) || (D == 128 && (r == 32 || r == 64 || r == 128));
 }
 
 hipError_t launch_decode_pca_h(int D, int r, int bits, bool bf16, const DecodeArgs& a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
   if (D == 64 && r == 32) return launch_dp_dr<64, 32>(bits, bf16, a, st);
+  if (D == 64 && r == 64) return launch_dp_dr<64, 64>(bits, bf16, a, st);
   if (D == 128 && r == 32) return launch_dp_dr<128, 32>(bits, bf16, a, st);
   if (D == 128 && r == 64) return launch_dp_dr<128, 64>(bits, bf16, a, st);
+  if (D == 128 && r == 128) return launch_dp_dr<128, 128>(bits, bf16, a, st);
   return hipErrorInvalidValue;
 }
 
