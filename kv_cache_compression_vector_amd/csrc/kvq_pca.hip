@@ -171,6 +171,199 @@ void k_encode_pca(EncodeArgs a, int64_t tiles_per_block) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Encode at r = 64, D <= 128 with two lanes per vector. Registers, not LDS or bandwidth, set
+// the occupancy of the kernel above (about 200 registers for a lane that owns 64 coordinates:
+// 2 waves per SIMD, 8 per CU, too few loads in flight to stream HBM). Here a wave takes 32 rows
+// and lane pair (2p, 2p+1) owns vector p: lane q holds the 32 coordinates whose index bit 2 is
+// q, i = 8j + 4q + e (j < 8, e < 4), locally k = 4j + e. The rotation is the Sylvester
+// transform over the five in-lane index bits plus one butterfly across the pair (index bit 2);
+// the bit order of a Hadamard transform's stages is free. With this split the word group of
+// the record's plane layout (g = pi(i) / 32 = bit 2 of i) is the lane: lane q quantises exactly
+// the 32 coordinates of word group q, bit t of its words holding k = 4 (t mod 8) + t / 8.
+// Rows are not staged: each lane loads its MFMA B operands (16 bytes of one row per k-step)
+// straight from memory, with ordinary loads (a streaming hint that bypasses the caches costs
+// 7 % here, since the 64-byte pieces of one 128-byte line arrive from two instructions), and
+// the next tile's operands stay in flight while a tile computes. LDS holds the basis (16 KB)
+// and 8 KB per wave for the projected rows and the records; a block of 4 waves takes 128 rows
+// under one basis, and three blocks (12 waves, 140-155 registers each) share a CU.
+constexpr int kPqWaves = 4;
+constexpr int kPqRows = 32;                       // rows per wave tile
+constexpr int kPqTile = kPqWaves * kPqRows;       // rows per block tile
+
+template <int D, int BITS, bool SYM>
+__global__ __launch_bounds__(64 * kPqWaves) __attribute__((amdgpu_waves_per_eu(3)))
+void k_encode_pq(EncodeArgs a, int64_t tiles_per_block) {
+  constexpr int R = 64, NT = R / 16, BCH = D / 8;
+  constexpr int CCH = D / 8;                       // input row in 16-byte chunks
+  constexpr int RCH = 16;                          // region row stride: 16 chunks (64 f32)
+  constexpr int NWC = 2 * BITS, NWT = NWC + 1;
+  constexpr int KS = D / 32;                       // k-steps of the projection
+  __shared__ uint4 s_bT[R * BCH];
+  __shared__ uint4 s_reg[kPqWaves * kPqRows * RCH];
+  __shared__ float4 s_mp[R / 4];  // -(s (.) B^T mu), the projection's initial value
+  __shared__ float s_muf[D];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  uint4* reg = s_reg + wave * kPqRows * RCH;
+  int cur = -1;
+  const int64_t n_tiles = (a.n + kPqTile - 1) / kPqTile;
+  const int64_t t0 = blockIdx.x * tiles_per_block;
+  const int64_t t1 = t0 + tiles_per_block < n_tiles ? t0 + tiles_per_block : n_tiles;
+  // The MFMA B operands straight from memory: lane l takes row 16 rt + l % 16, bytes
+  // 64 ks + 16 (l / 16) .. +15 (rows past the end repeat the last); the next tile's are in flight
+  // while a tile computes.
+  auto load_x = [&](int64_t tile, uint4 (&dst)[2][KS]) {
+    const int l = opaque_lane();
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      int64_t row = tile * kPqTile + kPqRows * wave + 16 * rt + (l & 15);
+      row = row < a.n ? row : a.n - 1;
+      const uint4* src = reinterpret_cast<const uint4*>(a.x + row * a.ld) + (l >> 4);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dst[rt][ks] = src[4 * ks];
+    }
+  };
+  uint4 nxt[2][KS];
+  if (t0 < t1) load_x(t0, nxt);
+  for (int64_t tile = t0; tile < t1; ++tile) {
+    const int64_t row0 = tile * kPqTile;
+    const int bi = basis_of_row(a.pca, row0);  // block tiles never straddle basis blocks
+    if (bi != cur) {
+      __syncthreads();
+      const uint16_t* Bk = a.pca.basis + (int64_t)bi * D * R;
+      uint16_t* bt16 = reinterpret_cast<uint16_t*>(s_bT);
+      for (int e = tid; e < D * R; e += 64 * kPqWaves) {
+        const int d = e / R, j = e % R;
+        const uint32_t flip = (a.tab.sign_pairs[j >> 1] >> (16 * (j & 1))) & 0x8000u;
+        bt16[swz<BCH>(j, d / 8) * 8 + d % 8] = (uint16_t)(Bk[e] ^ flip);
+      }
+      const float* mu = a.pca.mean ? a.pca.mean + (int64_t)bi * D : nullptr;
+      if (tid < D) s_muf[tid] = mu ? mu[tid] : 0.0f;
+      __syncthreads();
+      // -(s (.) B^T mu): TPC threads per column j, each over BCH / TPC chunks, then summed
+      {
+        constexpr int TPC = 64 * kPqWaves / R;
+        static_assert(TPC * R == 64 * kPqWaves && BCH % TPC == 0 && TPC <= 8, "column split");
+        const int j = tid / TPC, part = tid % TPC;
+        float acc = 0.0f;
+#pragma unroll
+        for (int c2 = 0; c2 < BCH / TPC; ++c2) {
+          const int c = part * (BCH / TPC) + c2;
+          const uint4 w = s_bT[swz<BCH>(j, c)];
+          const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc = fmaf(bf16lo_to_f32(u[e]), s_muf[8 * c + 2 * e], acc);
+            acc = fmaf(bf16hi_to_f32(u[e]), s_muf[8 * c + 2 * e + 1], acc);
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < TPC; o <<= 1) acc += __shfl_xor(acc, o, 64);
+        if (part == 0) reinterpret_cast<float*>(s_mp)[j] = -acc;
+      }
+      __syncthreads();
+      cur = bi;
+    }
+    const int64_t rw0 = row0 + kPqRows * wave;
+    const int ln = opaque_lane();
+    uint4 xf[2][KS];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) xf[rt][ks] = nxt[rt][ks];
+    if (tile + 1 < t1) load_x(tile + 1, nxt);  // in flight while this tile computes
+    // y^T = (s (.) B^T) x^T - s (.) B^T mu: acc[rt][t] = y[16 rt + l % 16][16 t + 4 (l / 16) ..+3]
+    floatx4 acc[2][NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float4 m = s_mp[4 * t + (ln >> 4)];  // columns 16 t + 4 (l / 16) .. +3
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) acc[rt][t] = floatx4{m.x, m.y, m.z, m.w};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ck = 4 * ks + (ln >> 4);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint4 bf = s_bT[swz<BCH>(16 * t + (ln & 15), ck)];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[rt][t] = mfma_bf16(bf, xf[rt][ks], acc[rt][t]);
+      }
+    }
+    phase_fence();
+    // projected rows (f32) into the region: chunk c of a row holds coordinates 4c .. 4c + 3
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        reg[swz<RCH>(16 * rt + (ln & 15), 4 * t + (ln >> 4))] =
+            make_uint4(__float_as_uint(acc[rt][t][0]), __float_as_uint(acc[rt][t][1]),
+                       __float_as_uint(acc[rt][t][2]), __float_as_uint(acc[rt][t][3]));
+    __builtin_amdgcn_wave_barrier();
+    // lane pair per vector: lane q takes chunks 2j + q (coordinates 8j + 4q + e)
+    const int p = ln >> 1, q = ln & 1;
+    float v[32];
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 f = reg[swz<RCH>(p, 2 * j + q)];
+      v[4 * j + 0] = __uint_as_float(f.x);
+      v[4 * j + 1] = __uint_as_float(f.y);
+      v[4 * j + 2] = __uint_as_float(f.z);
+      v[4 * j + 3] = __uint_as_float(f.w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = fmaf(v[4 * j + e], v[4 * j + e], ss);
+    }
+    __builtin_amdgcn_wave_barrier();
+    phase_fence();
+    ss += quad_xor<1>(ss);
+    const float n = sqrtf(ss);
+    fwht_regs<32>(v);          // index bits 0, 1, 3, 4, 5 (local bits 0 .. 4)
+    fwht_cross<2, 32>(v, q);   // index bit 2, across the pair
+    // quantise word group q: bit t of each plane word is local coordinate 4 (t mod 8) + t / 8
+    uint32_t pl[BITS];
+    {
+      const Quant<BITS, SYM> qz(a.tab, n);
+      QuantAcc<BITS, SYM> qa;
+#pragma unroll
+      for (int t = 31; t >= 0; --t) qa.push(v[4 * (t % 8) + t / 8], qz);
+      qa.planes(qz, 0xFFFFFFFFu, pl);
+    }
+    // the tile's records through the (now free) region, then coalesced 16-byte stores
+    uint32_t* rec_lds = reinterpret_cast<uint32_t*>(reg);
+#pragma unroll
+    for (int pp = 0; pp < BITS; ++pp) rec_lds[p * NWT + q * BITS + pp] = pl[pp];
+    if (q == 0) rec_lds[p * NWT + NWC] = __float_as_uint(n);
+    __builtin_amdgcn_wave_barrier();
+    {
+      constexpr int CH = kPqRows * NWT / 4;  // 16-byte pieces of the tile's records
+      const int64_t valid_rows = a.n - rw0 < kPqRows ? (a.n - rw0 > 0 ? a.n - rw0 : 0) : kPqRows;
+      const int64_t valid_ch = (valid_rows * NWT) / 4;
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(a.rec) + rw0 * NWT);
+      const uint4* src = reinterpret_cast<const uint4*>(rec_lds);
+#pragma unroll
+      for (int k = 0; k < (CH + 63) / 64; ++k) {
+        const int id = k * 64 + ln;
+        if (id < CH && id < valid_ch) st_stream(dst + id, src[id]);
+      }
+      const int64_t tail_w = valid_rows * NWT - valid_ch * 4;  // words of a partial last piece
+      if (ln < tail_w)
+        reinterpret_cast<uint32_t*>(a.rec)[rw0 * NWT + valid_ch * 4 + ln] = rec_lds[valid_ch * 4 + ln];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int D, int BITS, bool SYM>
+static hipError_t enc_pq_t(const EncodeArgs& a, hipStream_t st) {
+  const int64_t tiles = (a.n + kPqTile - 1) / kPqTile;
+  const int64_t resident = 256 * 3;  // three blocks per CU (registers and LDS: 16 KB + 32 KB)
+  const int64_t per = (tiles + resident - 1) / resident;
+  hipLaunchKernelGGL((k_encode_pq<D, BITS, SYM>), dim3((unsigned)((tiles + per - 1) / per)),
+                     dim3(64 * kPqWaves), 0, st, a, per);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // Decode: out^T[d][row] = sum_j B[d][j] v^[row][j] + mu[d]. The A operand is B as stored (row d,
 // k = j contiguous) with the signs folded into its columns, the B operand the rows of
 // scale * H z^, so lane l receives 4 consecutive d of one row.
@@ -323,6 +516,7 @@ static PcaGrid pca_grid(int64_t n) {
 
 template <int D, int R, int BITS, bool SYM>
 static hipError_t enc_t(const EncodeArgs& a, hipStream_t st) {
+  if constexpr (R == 64 && D <= 128) return enc_pq_t<D, BITS, SYM>(a, st);
   const PcaGrid g = pca_grid<D, R>(a.n);
   hipLaunchKernelGGL((k_encode_pca<D, R, BITS, SYM>), dim3(g.blocks), dim3(64 * PcaShape<D, R>::W), 0, st,
                      a, g.per_block);
