@@ -60,95 +60,87 @@ __device__ __forceinline__ uint32_t pair_index(const uint32_t* w, int sh, int pr
 }
 
 // Rotated queries of heads [0, 8) of one (batch, kv head) into qs[h * M + pos] (plane-position
-// order pos = (i mod 8) * (M/8) + i/8; heads >= G are zero) and qmu[h] = q_h . mu (PCA).
-// Every thread of the block calls this; it synchronises.
+// order pos = (i mod 8) * (M/8) + i/8; heads >= G are zero) and qmu[h] = q_h . mu (projection).
+// The projection uq[h][j] = sum_d q[h][d] B[d][j] runs on the vector ALUs: the queries are
+// staged in LDS as f32 [d][h] (qT), thread (row slice, column pair) reads its slice's basis rows
+// two columns per 32-bit load straight from memory (a wave reads whole basis rows), and the
+// slices' partial sums meet in LDS (part, [slice][h][M]). Every thread of the block calls this;
+// it synchronises.
+template <int D, int M>
+constexpr int proj_slices() { return kScoreThreads / (M / 2); }
+
 template <int D, int M, bool PCA>
 __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int kv, int G, int bi,
-                                                float* qs, float* qmu, uint4* sBT, float* uq) {
+                                                float* qs, float* qmu, float* qT, float* part,
+                                                float* qpow) {
+  float* qmp = part + proj_slices<D, M>() * kScoreHeads * M;  // q . mu pair products [h][D / 2]
   constexpr int H = kScoreHeads;
   constexpr int LPV = M / 8;
   constexpr int HPB = kScoreThreads / LPV;  // heads per rotation pass
-  const int tid = threadIdx.x, lane = tid & 63;
+  constexpr int NS = proj_slices<D, M>();
+  const int tid = threadIdx.x;
   const uint16_t* qb = a.q + b * a.q_sb + (int64_t)kv * G * a.q_sh;
   if constexpr (PCA) {
-    // every global load of the prologue first (one memory round trip): the basis (16-byte
-    // pieces), wave 0 the query fragments, wave 1 the query and mean slices of q . mu
-    constexpr int BCH = D / 8, MASK = (BCH < 16 ? BCH : 16) - 1;
-    constexpr int NB = D * M / 8 / kScoreThreads;
-    const uint4* Bk = reinterpret_cast<const uint4*>(a.pca.basis + (int64_t)bi * D * M);
-    uint4 bl[NB];
+    constexpr int CP = M / 2, RS = D / NS;
+    constexpr int QP = D * H / 2 / kScoreThreads;  // query bf16 pairs staged per thread
+    static_assert(kScoreThreads % CP == 0 && D % NS == 0 && QP >= 1, "projection split");
+    const int cp = tid % CP, sl = tid / CP;
+    // every global load first (one memory round trip): basis rows, query pairs, mean pairs
+    const uint32_t* Bk = reinterpret_cast<const uint32_t*>(a.pca.basis + (int64_t)bi * D * M) + cp;
+    uint32_t bw[RS];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) bl[i] = Bk[tid + kScoreThreads * i];
-    const int h = lane & 15;
-    uint4 qf[D / 32];
-    if (tid < 64) {
+    for (int i = 0; i < RS; ++i) bw[i] = Bk[(sl * RS + i) * CP];
+    uint32_t qw[QP];
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        qf[ks] = h < G ? *reinterpret_cast<const uint4*>(qb + (int64_t)h * a.q_sh + 32 * ks + 8 * (lane >> 4))
-                       : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < QP; ++i) {
+      const int e = tid + kScoreThreads * i, h = e / (D / 2), d = 2 * (e % (D / 2));
+      qw[i] = h < G ? *reinterpret_cast<const uint32_t*>(qb + (int64_t)h * a.q_sh + d) : 0u;
     }
-    // q . mu: 8 lanes per head, D/8 consecutive coordinates each
-    const int hm = (tid - 64) / 8, lm = (tid - 64) % 8;
-    const bool mu_lane = tid >= 64 && tid < 64 + 8 * H && a.pca.mean && hm < G;
-    uint4 qm4[D / 64];
-    float4 mu4[D / 32];
-    if (mu_lane) {
-      const float* mu = a.pca.mean + (int64_t)bi * D + lm * (D / 8);
-      const uint16_t* qh = qb + (int64_t)hm * a.q_sh + lm * (D / 8);
+    // the mean's coordinate pairs matching the staged query pairs, for q . mu
+    const float* mub = a.pca.mean ? a.pca.mean + (int64_t)bi * D : nullptr;
+    float2 mw[QP];
 #pragma unroll
-      for (int i = 0; i < D / 64; ++i) qm4[i] = *reinterpret_cast<const uint4*>(qh + 8 * i);
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) mu4[i] = *reinterpret_cast<const float4*>(mu + 4 * i);
+    for (int i = 0; i < QP; ++i) {
+      const int e = tid + kScoreThreads * i, d = 2 * (e % (D / 2));
+      mw[i] = mub ? *reinterpret_cast<const float2*>(mub + d) : make_float2(0.0f, 0.0f);
     }
-    // basis transposed into LDS: sBT row j = basis column j (D bf16), chunk-swizzled
-    uint16_t* bt16 = reinterpret_cast<uint16_t*>(sBT);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int e = tid + kScoreThreads * i;
-      const int d = e / (M / 8), j0 = 8 * (e % (M / 8));
-      const uint32_t u[4] = {bl[i].x, bl[i].y, bl[i].z, bl[i].w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = j0 + k;
-        bt16[(j * BCH + ((d / 8) ^ (j & MASK))) * 8 + d % 8] = (uint16_t)(u[k / 2] >> (16 * (k & 1)));
-      }
+    for (int i = 0; i < QP; ++i) {
+      const int e = tid + kScoreThreads * i, h = e / (D / 2), d = 2 * (e % (D / 2));
+      const float q0 = bf16lo_to_f32(qw[i]), q1 = bf16hi_to_f32(qw[i]);
+      qT[d * H + h] = q0;
+      qT[(d + 1) * H + h] = q1;
+      qmp[e] = fmaf(q1, mw[i].y, q0 * mw[i].x);  // [h][d / 2]
     }
     __syncthreads();
-    if (tid < 64) {
-      // uq^T = B^T q^T on MFMA: A = basis^T rows (16 columns j), B = query rows (16 heads)
+    float p0[H], p1[H];
 #pragma unroll
-      for (int nt = 0; nt < M / 16; ++nt) {
-        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-        const int j = 16 * nt + (lane & 15);
+    for (int h = 0; h < H; ++h) p0[h] = p1[h] = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const int ck = 4 * ks + (lane >> 4);
-          acc = mfma16(sBT[j * BCH + (ck ^ (j & MASK))], qf[ks], acc);
-        }
-        // acc[i] = uq[head lane % 16][j = 16 nt + 4 (lane / 16) + i]
-        if (h < H) {
+    for (int i = 0; i < RS; ++i) {
+      const int d = sl * RS + i;
+      const float4 x0 = *reinterpret_cast<const float4*>(qT + d * H);
+      const float4 x1 = *reinterpret_cast<const float4*>(qT + d * H + 4);
+      const float qq[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      const float b0 = bf16lo_to_f32(bw[i]), b1 = bf16hi_to_f32(bw[i]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) uq[h * M + 16 * nt + 4 * (lane >> 4) + i] = acc[i];
-        }
+      for (int h = 0; h < H; ++h) {
+        p0[h] = fmaf(qq[h], b0, p0[h]);
+        p1[h] = fmaf(qq[h], b1, p1[h]);
       }
-    } else if (tid < 64 + 8 * H) {
-      float s = 0.0f;
-      if (mu_lane) {
+    }
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i) {
-          const uint32_t w[4] = {qm4[i].x, qm4[i].y, qm4[i].z, qm4[i].w};
+    for (int h = 0; h < H; ++h)
+      *reinterpret_cast<float2*>(part + (sl * H + h) * M + 2 * cp) = make_float2(p0[h], p1[h]);
+    if (tid < 8 * H) {  // q . mu: 8 lanes per head sum the head's pair products
+      const int hm = tid / 8, lm = tid % 8;
+      float sm = 0.0f;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float4 m = mu4[2 * i + k / 2];
-            s = fmaf(bf16lo_to_f32(w[k]), (k & 1) ? m.z : m.x, s);
-            s = fmaf(bf16hi_to_f32(w[k]), (k & 1) ? m.w : m.y, s);
-          }
-        }
-      }
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      s += __shfl_xor(s, 4, 64);
-      if (lm == 0) qmu[hm] = s;
+      for (int k = 0; k < D / 16; ++k) sm += qmp[hm * (D / 2) + lm * (D / 16) + k];
+      sm += __shfl_xor(sm, 1, 64);
+      sm += __shfl_xor(sm, 2, 64);
+      sm += __shfl_xor(sm, 4, 64);
+      if (lm == 0) qmu[hm] = sm;
     }
     __syncthreads();
   } else {
@@ -161,11 +153,18 @@ __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int k
     const int h = h0 + tid / LPV;
     float v[8];
     if constexpr (PCA) {
+      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (h < H) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = h < H ? uq[h * M + 8 * c + j] : 0.0f;
-        v[j] = __uint_as_float(__float_as_uint(x) ^ (((sbyte >> j) & 1u) << 31));
+        for (int sl = 0; sl < NS; ++sl) {
+          const float4 u0 = *reinterpret_cast<const float4*>(part + (sl * H + h) * M + 8 * c);
+          const float4 u1 = *reinterpret_cast<const float4*>(part + (sl * H + h) * M + 8 * c + 4);
+          x[0] += u0.x; x[1] += u0.y; x[2] += u0.z; x[3] += u0.w;
+          x[4] += u1.x; x[5] += u1.y; x[6] += u1.z; x[7] += u1.w;
+        }
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((sbyte >> j) & 1u) << 31));
     } else {
       uint4 raw = make_uint4(0, 0, 0, 0);
       if (h < G) raw = *reinterpret_cast<const uint4*>(qb + (int64_t)h * a.q_sh + 8 * c);
@@ -177,9 +176,17 @@ __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int k
       }
     }
     fwht_vector<LPV>(v, c);
+    // qpow[h] = the power of two 2^e with max_i |q'_h,i| / 2^e in [2^14, 2^15) (1 for a zero
+    // query): scaled by it, the head's coordinates use the whole f16 range
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
+#pragma unroll
+    for (int m = 1; m < LPV; m <<= 1) mx = fmaxf(mx, lane_xor(mx, m));
     if (h < H) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) qs[h * M + j * LPV + c] = v[j];
+      if (c == 0) qpow[h] = mx > 0.0f ? ldexpf(1.0f, ilogbf(mx) - 14) : 1.0f;
     }
   }
   __syncthreads();
@@ -187,15 +194,13 @@ __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int k
 
 // Pair table: entry e (bit 2p + i = plane p of code i) holds the centroids of its two codes as
 // their bf16 hi pair (lut[e COPIES + c]) and lo pair (lut[(NPAIR + e) COPIES + c]), copy c read by
-// lanes l with l % COPIES == c, so the lookups of a half-wave never share an LDS bank. Each
-// thread of the block forms one entry and writes its share of the copies.
+// lanes l with l % COPIES == c, so the lookups of a half-wave never share an LDS bank. Thread i
+// of the block writes words i, i + 256, ...: consecutive lanes, consecutive banks.
 template <int BITS, int COPIES>
 __device__ __forceinline__ void fill_pair_table(const Tables& tab, uint32_t* lut, int tid) {
   constexpr int NPAIR = 1 << (2 * BITS);
-  constexpr int ACT = kScoreThreads < NPAIR * COPIES ? kScoreThreads : NPAIR * COPIES;
-  static_assert(ACT % NPAIR == 0 && (NPAIR * COPIES) % ACT == 0, "pair table split");
-  constexpr int CSTEP = ACT / NPAIR;
-  for (int e = tid % NPAIR, c = tid / NPAIR; tid < ACT && c < COPIES; c += CSTEP) {
+  for (int i = tid; i < NPAIR * COPIES; i += kScoreThreads) {
+    const int e = i / COPIES;
     uint32_t ca = 0, cb = 0;
 #pragma unroll
     for (int p = 0; p < BITS; ++p) {
@@ -211,8 +216,8 @@ __device__ __forceinline__ void fill_pair_table(const Tables& tab, uint32_t* lut
     uint32_t ha, la, hb, lb;
     split_bf16(va, ha, la);
     split_bf16(vb, hb, lb);
-    lut[e * COPIES + c] = ha | (hb << 16);
-    lut[(NPAIR + e) * COPIES + c] = la | (lb << 16);
+    lut[i] = ha | (hb << 16);
+    lut[NPAIR * COPIES + i] = la | (lb << 16);
   }
 }
 
@@ -270,23 +275,163 @@ __device__ __forceinline__ floatx4_t tile_dots(const uint32_t* w, const uint32_t
   return acc;
 }
 
+// ---- f16 products for the score kernel -------------------------------------------------
+// The score multiplies each rotated query, scaled per head by a power of two into the f16
+// range and split into f16 hi + lo, by the f16 centroids (scaled by one power of two per table):
+// each product is exact in the f32 accumulator, q'_hi + q'_lo carries ~2^-22 of q', and the
+// centroid's f16 rounding (<= 2^-11 relative) bounds the error of every term, so
+// |score error| <= ~5e-4 * (n/m) sum_i |q'_i c_i|. One table word (a pair of f16 centroids)
+// per two coordinates and two products per k-step.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ floatx4_t mfma16h(const uint4& a, const uint4& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// The power of two that brings the table's largest centroid magnitude into [2^14, 2^15).
+template <int BITS>
+__device__ __forceinline__ float table_pow(const Tables& tab) {
+  float mx = 0.0f;
+#pragma unroll
+  for (int k = 0; k < (1 << BITS); ++k) mx = fmaxf(mx, fabsf(tab.c[k]));
+  return mx > 0.0f ? ldexpf(1.0f, ilogbf(mx) - 14) : 1.0f;
+}
+
+// f16 pair table: word e COPIES + c = the two centroids of entry e (bit 2p + i = plane p of
+// code i) divided by cpow, as an f16 pair; copy c read by lanes l % COPIES == c.
+template <int BITS, int COPIES>
+__device__ __forceinline__ void fill_pair_table_f16(const Tables& tab, float inv_cpow, uint32_t* lut,
+                                                    int tid) {
+  constexpr int NPAIR = 1 << (2 * BITS);
+  for (int i = tid; i < NPAIR * COPIES; i += kScoreThreads) {
+    const int e = i / COPIES;
+    uint32_t ca = 0, cb = 0;
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) {
+      ca |= ((e >> (2 * p)) & 1u) << p;
+      cb |= ((e >> (2 * p + 1)) & 1u) << p;
+    }
+    float va = 0.0f, vb = 0.0f;
+#pragma unroll
+    for (int k = 0; k < (1 << BITS); ++k) {
+      va = (uint32_t)k == ca ? tab.c[k] : va;
+      vb = (uint32_t)k == cb ? tab.c[k] : vb;
+    }
+    lut[i] = f16_bits(va * inv_cpow) | (f16_bits(vb * inv_cpow) << 16);
+  }
+}
+
+// A operands of the rotated queries (head tok, coordinates 32 ks + 8 oct + [0, 8)) divided by
+// their head's power of two, as f16 hi and lo halves.
+template <int M>
+__device__ __forceinline__ void query_operands_f16(const float* qs, const float* qpow, int tok,
+                                                   int oct, uint4 (&qa_hi)[M / 32],
+                                                   uint4 (&qa_lo)[M / 32]) {
+  constexpr int H = kScoreHeads;
+  const float inv = tok < H ? 1.0f / qpow[tok] : 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < M / 32; ++ks) {
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = tok < H ? qs[tok * M + 32 * ks + 8 * oct + e] * inv : 0.0f;
+      const _Float16 xh = (_Float16)x;
+      hi[e] = (uint32_t)__builtin_bit_cast(uint16_t, xh);
+      lo[e] = f16_bits(x - (float)xh);
+    }
+    qa_hi[ks] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                           hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+    qa_lo[ks] = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                           lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
+  }
+}
+
+// Byte permute selectors that gather, for lane group oct, byte oct of plane words w[0], w[1]
+// (sel01) and then w[2] (sel2) into bytes 0, 1, 2 of one word.
+__device__ __forceinline__ uint32_t planes_sel01(int oct) {
+  return 0x0c0c0000u | ((uint32_t)(4 + oct) << 8) | (uint32_t)oct;
+}
+__device__ __forceinline__ uint32_t planes_sel2(int oct) {
+  return 0x0c000100u | ((uint32_t)(4 + oct) << 16);
+}
+
+// Raw logits (divided by the head's and the table's powers of two) of one 16-token record tile:
+// acc[k] for head 4 oct + k and token tok. mulc is the pair-gathering multiplier of
+// pair_index, held in a register so that the compiler keeps it a 24-bit multiply.
+template <int M, int BITS, int COPIES>
+__device__ __forceinline__ floatx4_t tile_dots_f16(const uint32_t* w, const uint32_t* lut, int lane,
+                                                   int oct, uint32_t sel01, uint32_t sel2,
+                                                   uint32_t mulc, const uint4 (&qa_hi)[M / 32],
+                                                   const uint4 (&qa_lo)[M / 32]) {
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t* lc = lut + (lane & (COPIES - 1));
+#pragma unroll
+  for (int ks = 0; ks < M / 32; ++ks) {
+    const uint32_t* wk = w + ks * BITS;
+    uint32_t z[4];
+    if constexpr (BITS == 2 || BITS == 3) {
+      uint32_t y = __builtin_amdgcn_perm(wk[1], wk[0], sel01);
+      if constexpr (BITS == 3) y = __builtin_amdgcn_perm(wk[2], y, sel2);
+      const uint32_t mask = BITS == 3 ? 0x030303u : 0x0303u;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const uint32_t idx = __builtin_amdgcn_ubfe(__umul24(y & (mask << (2 * pr)), mulc),
+                                                   16 + 2 * pr, 2 * BITS);
+        z[pr] = lc[idx * COPIES];
+      }
+    } else {
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) z[pr] = lc[pair_index<BITS>(wk, 8 * oct, 2 * pr) * COPIES];
+    }
+    const uint4 bz = make_uint4(z[0], z[1], z[2], z[3]);
+    acc = mfma16h(qa_hi[ks], bz, acc);
+    acc = mfma16h(qa_lo[ks], bz, acc);
+  }
+  return acc;
+}
+
+// Steps of the score loop. A wave takes the 64 consecutive tokens s0 + 64 wave + [0, 64) of each
+// 256-token segment, in steps of TPS 16-token tiles. A step's records are one contiguous byte
+// range: they leave memory as dword loads spread over the wave's lanes (SW per lane, no lane
+// loading what another lane loads) and reach the lanes that multiply them through the wave's
+// LDS slice. PF steps are in flight while one computes.
+template <int NWT>
+struct ScoreSteps {
+  static constexpr int TPS = NWT <= 16 ? 4 : (NWT <= 32 ? 2 : 1);  // tiles per step
+  static constexpr int WORDS = 16 * TPS * NWT;                      // record dwords per step
+  static constexpr int SW = (WORDS + 63) / 64;                      // dwords per lane
+  static constexpr int PF = (32 / SW) < 1 ? 1 : ((32 / SW) > 4 ? 4 : 32 / SW);
+  static constexpr int SPS = 4 / TPS;                               // steps per segment
+};
+
 template <int D, int M, int BITS, bool PCA>
 __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t chunk,
                                                          int64_t chunks_per_pair) {
   constexpr int H = kScoreHeads;
   constexpr int KS = M / 32;              // MFMA k-steps (one 32-coordinate word group each)
   constexpr int NWC = KS * BITS, NWT = NWC + 1;
-  constexpr int NPAIR = 1 << (2 * BITS);  // pair-table entries
   constexpr int COPIES = pair_copies<BITS>();
-  // tiles in flight per wave: as many 16-token record tiles as fit ~64 registers (1 .. 7)
-  constexpr int P = (64 / NWT - 1) < 1 ? 1 : ((64 / NWT - 1) > 7 ? 7 : (64 / NWT - 1));
-  constexpr int R = P + 1;
+  using St = ScoreSteps<NWT>;
+  constexpr int TPS = St::TPS, SW = St::SW, PF = St::PF, SPS = St::SPS, WORDS = St::WORDS;
   __shared__ __attribute__((aligned(16))) float qs[H * M];
   __shared__ float qmu[H];
-  __shared__ uint32_t lut[2 * NPAIR * COPIES];  // [hi | lo][entry][copy]
-  __shared__ uint4 sBT[PCA ? D * M / 8 : 1];
-  __shared__ float uq[PCA ? H * M : 1];
+  __shared__ float qpow[H];
+  __shared__ uint32_t lut[(1 << (2 * BITS)) * COPIES];  // [entry][copy]: f16 centroid pairs
+  // the projection's staging (queries, partial sums) and the loop's record staging share LDS:
+  // the former is live only inside prepare_queries, between barriers, before a step's records
+  // are staged
+  constexpr int PRE = PCA ? D * H + proj_slices<D, M>() * H * M + H * D / 2 : 0;
+  constexpr int STG = (kScoreThreads / 64) * WORDS;
+  __shared__ __attribute__((aligned(16))) float work[PRE > STG ? PRE : STG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* qT = work;
+  float* part = work + D * H;
+  uint32_t* stage = reinterpret_cast<uint32_t*>(work) + wave * WORDS;
   const int tok = lane & 15, oct = lane >> 4;
   const int64_t pair = blockIdx.x / chunks_per_pair;
   const int b = (int)(pair / a.Hkv), kv = (int)(pair % a.Hkv);
@@ -294,54 +439,84 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
   const int64_t t_begin = (blockIdx.x % chunks_per_pair) * chunk;
   const int64_t t_end = t_begin + chunk < a.T ? t_begin + chunk : a.T;
   const int64_t rowbase = b * a.rec_sb + kv * a.rec_sh;
-  fill_pair_table<BITS, COPIES>(a.tab, lut, tid);
-  uint4 qa_hi[KS], qa_lo[KS];  // A operand: head tok, coordinates 32 ks + 8 oct .. + 7
-  float qm[4];
-  int cur = -1;
-  // Tiles of 16 tokens: tile j of this wave covers tokens t_begin + 64 j + 16 wave + [0, 16);
-  // four tiles per wave make a 256-token segment (one basis). R = P + 1 record slots form a
-  // ring: while tile j computes, tiles j + 1 .. j + P are in flight.
-  const int64_t n_tiles = ((t_end - t_begin + kScoreSegment - 1) / kScoreSegment) * 4;
-  auto load_tile = [&](int64_t j, uint32_t (&w)[NWT]) {
-    const int64_t t = t_begin + 64 * j + 16 * wave + tok;
-    const int64_t se = t_begin + kScoreSegment * (j / 4 + 1);
-    const int64_t te = se < t_end ? se : t_end;
-    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(a.rec) +
-                          (rowbase + (t < te ? t : te - 1)) * NWT;
-#pragma unroll
-    for (int k = 0; k < NWT; ++k) w[k] = r32[k];
+  const int64_t n_steps = ((t_end - t_begin + kScoreSegment - 1) / kScoreSegment) * SPS;
+  const uint32_t* rec32 = reinterpret_cast<const uint32_t*>(a.rec);
+  // first token of step g of this wave
+  auto step_t0 = [&](int64_t g) {
+    return t_begin + kScoreSegment * (g / SPS) + 64 * wave + 16 * TPS * (g % SPS);
   };
-  uint32_t ring[R][NWT];
+  auto load_step = [&](int64_t g, uint32_t (&buf)[SW]) {
+    const int64_t t0 = step_t0(g), left = t_end - t0;
+    const int lim = left >= 16 * TPS ? WORDS : (left > 0 ? (int)left * NWT : 0);  // uniform
+    const uint32_t* src = rec32 + (rowbase + t0) * NWT + lane;
 #pragma unroll
-  for (int r = 0; r < P; ++r)
-    if (r < n_tiles) load_tile(r, ring[r]);
-  for (int64_t j0 = 0; j0 < n_tiles; j0 += R) {
+    for (int i = 0; i < SW; ++i) buf[i] = lane + 64 * i < lim ? src[64 * i] : 0u;
+  };
+  int bi = PCA ? basis_of_row(a.pca, rowbase + t_begin) : 0;
+  uint32_t ring[PF][SW];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t j = j0 + r;
-      if (j >= n_tiles) break;  // uniform
-      if (j % 4 == 0) {
-        const int bi = PCA ? basis_of_row(a.pca, rowbase + t_begin + 64 * j) : 0;
-        if (bi != cur) {  // block-uniform
-          __syncthreads();
-          prepare_queries<D, M, PCA>(a, b, kv, G, bi, qs, qmu, sBT, uq);
-          query_operands<M>(qs, qmu, tok, oct, qa_hi, qa_lo, qm);
-          cur = bi;
+  for (int r = 0; r < PF; ++r)
+    if (r < n_steps) load_step(r, ring[r]);
+  const float cpow = table_pow<BITS>(a.tab);
+  fill_pair_table_f16<BITS, COPIES>(a.tab, 1.0f / cpow, lut, tid);
+  prepare_queries<D, M, PCA>(a, b, kv, G, bi, qs, qmu, qT, part, qpow);
+  uint4 qa_hi[KS], qa_lo[KS];  // A operand: head tok, coordinates 32 ks + 8 oct .. + 7
+  float qm[4], qsc[4];         // q . mu and the product's scale of heads 4 oct + k
+  auto operands = [&]() {
+    query_operands_f16<M>(qs, qpow, tok, oct, qa_hi, qa_lo);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      qm[k] = 4 * oct + k < H ? qmu[4 * oct + k] : 0.0f;
+      qsc[k] = 4 * oct + k < H ? qpow[4 * oct + k] * cpow * a.tab.inv_m : 0.0f;
+    }
+  };
+  operands();
+  const uint32_t sel01 = planes_sel01(oct), sel2 = planes_sel2(oct);
+  uint32_t mulc = BITS == 3 ? 0x10410u : 0x10400u;
+  asm volatile("" : "+s"(mulc));
+  int bnext = bi;
+  for (int64_t g0 = 0; g0 < n_steps; g0 += PF) {
+#pragma unroll
+    for (int r = 0; r < PF; ++r) {
+      const int64_t g = g0 + r;
+      if (g >= n_steps) break;  // uniform
+      if constexpr (PCA) {
+        if (g % SPS == 0) {
+          if (g > 0 && bnext != bi) {  // block-uniform: a new basis from this segment on
+            __syncthreads();
+            prepare_queries<D, M, PCA>(a, b, kv, G, bnext, qs, qmu, qT, part, qpow);
+            operands();
+            bi = bnext;
+          }
+          // the next segment's basis, looked up one segment ahead
+          const int64_t sn = t_begin + kScoreSegment * (g / SPS + 1);
+          bnext = sn < t_end ? basis_of_row(a.pca, rowbase + sn) : bi;
         }
       }
-      if (j + P < n_tiles) load_tile(j + P, ring[(r + P) % R]);
-      const uint32_t (&w)[NWT] = ring[r];
-      const floatx4_t acc = tile_dots<M, BITS, COPIES>(w, lut, lane, oct, qa_hi, qa_lo);
-      // acc[k] = sum for head 4 oct + k, token t
-      const int64_t t = t_begin + 64 * j + 16 * wave + tok;
-      const int64_t se = t_begin + kScoreSegment * (j / 4 + 1);
-      const float scale = __uint_as_float(w[NWC]) * a.tab.inv_m;
-      float* srow = a.s + b * a.s_sb + t;
+      // this step's records to the wave's LDS slice, then the slot refills
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int h = 4 * oct + k;
-        if (t < se && t < t_end && h < G) srow[(int64_t)(kv * G + h) * a.s_sh] = fmaf(acc[k], scale, qm[k]);
+      for (int i = 0; i < SW; ++i)
+        if (lane + 64 * i < WORDS) stage[lane + 64 * i] = ring[r][i];
+      if (g + PF < n_steps) load_step(g + PF, ring[r]);
+      __builtin_amdgcn_wave_barrier();
+      const int64_t t0 = step_t0(g);
+      float* srow = a.s + b * a.s_sb + (int64_t)kv * G * a.s_sh + t0 + tok;
+#pragma unroll
+      for (int tt = 0; tt < TPS; ++tt) {
+        uint32_t w[NWT];
+#pragma unroll
+        for (int k = 0; k < NWT; ++k) w[k] = stage[(16 * tt + tok) * NWT + k];
+        const floatx4_t acc = tile_dots_f16<M, BITS, COPIES>(w, lut, lane, oct, sel01, sel2, mulc,
+                                                             qa_hi, qa_lo);
+        const float nrm = __uint_as_float(w[NWC]);
+        const bool tv = t0 + 16 * tt + tok < t_end;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int h = 4 * oct + k;
+          if (tv && h < G) srow[(int64_t)h * a.s_sh + 16 * tt] = fmaf(acc[k], nrm * qsc[k], qm[k]);
+        }
       }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
@@ -378,10 +553,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
   constexpr int S = attend_stride<D>();
   __shared__ __attribute__((aligned(16))) float qs[H * M];
   __shared__ float qmu[H];
+  __shared__ float qpow[H];
   __shared__ uint32_t lutk[2 * (1 << (2 * BK)) * CK];
   __shared__ uint32_t lutv[2 * NPV * CV];
-  __shared__ uint4 sBT[PCA ? D * M / 8 : 1];
-  __shared__ float uq[PCA ? H * M : 1];
+  __shared__ __attribute__((aligned(16))) float qT[PCA ? D * H : 1];
+  __shared__ __attribute__((aligned(16))) float part[PCA ? proj_slices<D, M>() * H * M + H * D / 2 : 1];
   __shared__ uint32_t vst[kAttnWaves][32 * NWV];                         // the unit's V records
   __shared__ __attribute__((aligned(16))) float pst[kAttnWaves][16][32];  // p (n/m) [head][token]
   __shared__ float cst[kAttnWaves][16];                                   // accumulator rescale
@@ -437,7 +613,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
     const int bi = PCA ? basis_of_row(k.pca, rowbase + s0) : 0;
     if (bi != cur) {  // block-uniform
       __syncthreads();
-      prepare_queries<D, M, PCA>(k, b, kv, G, bi, qs, qmu, sBT, uq);
+      prepare_queries<D, M, PCA>(k, b, kv, G, bi, qs, qmu, qT, part, qpow);
       query_operands<M>(qs, qmu, tok, oct, qa_hi, qa_lo, qm);
       cur = bi;
     }
