@@ -69,10 +69,16 @@ __device__ __forceinline__ uint32_t pair_index(const uint32_t* w, int sh, int pr
 template <int D, int M>
 constexpr int proj_slices() { return kScoreThreads / (M / 2); }
 
-template <int D, int M, bool PCA>
+// hook(0) runs once the prologue's global loads are issued, hook(1) after a block barrier that
+// follows it (the pair tables are filled in these two phases while the loads are in flight).
+struct NoHook {
+  __device__ void operator()(int) const {}
+};
+
+template <int D, int M, bool PCA, class Hook = NoHook>
 __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int kv, int G, int bi,
                                                 float* qs, float* qmu, float* qT, float* part,
-                                                float* qpow) {
+                                                float* qpow, Hook hook = Hook()) {
   float* qmp = part + proj_slices<D, M>() * kScoreHeads * M;  // q . mu pair products [h][D / 2]
   constexpr int H = kScoreHeads;
   constexpr int LPV = M / 8;
@@ -86,16 +92,16 @@ __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int k
     static_assert(kScoreThreads % CP == 0 && D % NS == 0 && QP >= 1, "projection split");
     const int cp = tid % CP, sl = tid / CP;
     // every global load first (one memory round trip): basis rows, query pairs, mean pairs
-    const uint32_t* Bk = reinterpret_cast<const uint32_t*>(a.pca.basis + (int64_t)bi * D * M) + cp;
-    uint32_t bw[RS];
-#pragma unroll
-    for (int i = 0; i < RS; ++i) bw[i] = Bk[(sl * RS + i) * CP];
     uint32_t qw[QP];
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
       const int e = tid + kScoreThreads * i, h = e / (D / 2), d = 2 * (e % (D / 2));
       qw[i] = h < G ? *reinterpret_cast<const uint32_t*>(qb + (int64_t)h * a.q_sh + d) : 0u;
     }
+    const uint32_t* Bk = reinterpret_cast<const uint32_t*>(a.pca.basis + (int64_t)bi * D * M) + cp;
+    uint32_t bw[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i) bw[i] = Bk[(sl * RS + i) * CP];
     // the mean's coordinate pairs matching the staged query pairs, for q . mu
     const float* mub = a.pca.mean ? a.pca.mean + (int64_t)bi * D : nullptr;
     float2 mw[QP];
@@ -104,6 +110,7 @@ __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int k
       const int e = tid + kScoreThreads * i, d = 2 * (e % (D / 2));
       mw[i] = mub ? *reinterpret_cast<const float2*>(mub + d) : make_float2(0.0f, 0.0f);
     }
+    hook(0);
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
       const int e = tid + kScoreThreads * i, h = e / (D / 2), d = 2 * (e % (D / 2));
@@ -113,6 +120,7 @@ __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int k
       qmp[e] = fmaf(q1, mw[i].y, q0 * mw[i].x);  // [h][d / 2]
     }
     __syncthreads();
+    hook(1);
     float p0[H], p1[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) p0[h] = p1[h] = 0.0f;
@@ -143,11 +151,17 @@ __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int k
       if (lm == 0) qmu[hm] = sm;
     }
     __syncthreads();
-  } else {
-    if (tid < H) qmu[tid] = 0.0f;
   }
   // s (.) v, then the M-point Hadamard transform, LPV lanes per head with 8 coordinates each
   const int c = tid % LPV;
+  uint4 raw0 = make_uint4(0, 0, 0, 0);  // the first pass's query coordinates (no projection)
+  if constexpr (!PCA) {
+    if (tid / LPV < G) raw0 = *reinterpret_cast<const uint4*>(qb + (int64_t)(tid / LPV) * a.q_sh + 8 * c);
+    if (tid < H) qmu[tid] = 0.0f;
+    hook(0);
+    __syncthreads();
+    hook(1);
+  }
   const uint32_t sbyte = (a.tab.sign_words[(c >> 2) & 15] >> (8 * (c & 3))) & 0xFFu;
   for (int h0 = 0; h0 < H; h0 += HPB) {
     const int h = h0 + tid / LPV;
@@ -166,8 +180,8 @@ __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int k
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((sbyte >> j) & 1u) << 31));
     } else {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (h < G) raw = *reinterpret_cast<const uint4*>(qb + (int64_t)h * a.q_sh + 8 * c);
+      uint4 raw = raw0;
+      if (h0 > 0 && h < G) raw = *reinterpret_cast<const uint4*>(qb + (int64_t)h * a.q_sh + 8 * c);
       const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -194,31 +208,45 @@ __device__ __forceinline__ void prepare_queries(const ScoreArgs& a, int b, int k
 
 // Pair table: entry e (bit 2p + i = plane p of code i) holds the centroids of its two codes as
 // their bf16 hi pair (lut[e COPIES + c]) and lo pair (lut[(NPAIR + e) COPIES + c]), copy c read by
-// lanes l with l % COPIES == c, so the lookups of a half-wave never share an LDS bank. Thread i
-// of the block writes words i, i + 256, ...: consecutive lanes, consecutive banks.
+// lanes l with l % COPIES == c, so the lookups of a half-wave never share an LDS bank. Filled in
+// two phases around a block barrier: pair_entries forms each entry once (copy 0), and
+// pair_replicate copies it, consecutive threads writing consecutive words.
 template <int BITS, int COPIES>
-__device__ __forceinline__ void fill_pair_table(const Tables& tab, uint32_t* lut, int tid) {
-  constexpr int NPAIR = 1 << (2 * BITS);
-  for (int i = tid; i < NPAIR * COPIES; i += kScoreThreads) {
-    const int e = i / COPIES;
-    uint32_t ca = 0, cb = 0;
+__device__ __forceinline__ void pair_codes(int e, uint32_t& ca, uint32_t& cb) {
+  ca = cb = 0;
 #pragma unroll
-    for (int p = 0; p < BITS; ++p) {
-      ca |= ((e >> (2 * p)) & 1u) << p;
-      cb |= ((e >> (2 * p + 1)) & 1u) << p;
-    }
-    float va = 0.0f, vb = 0.0f;
-#pragma unroll
-    for (int k = 0; k < (1 << BITS); ++k) {
-      va = (uint32_t)k == ca ? tab.c[k] : va;
-      vb = (uint32_t)k == cb ? tab.c[k] : vb;
-    }
-    uint32_t ha, la, hb, lb;
-    split_bf16(va, ha, la);
-    split_bf16(vb, hb, lb);
-    lut[i] = ha | (hb << 16);
-    lut[NPAIR * COPIES + i] = la | (lb << 16);
+  for (int p = 0; p < BITS; ++p) {
+    ca |= ((e >> (2 * p)) & 1u) << p;
+    cb |= ((e >> (2 * p + 1)) & 1u) << p;
   }
+}
+
+template <int BITS>
+__device__ __forceinline__ float centroid_of(const Tables& tab, uint32_t code) {
+  float v = 0.0f;
+#pragma unroll
+  for (int k = 0; k < (1 << BITS); ++k) v = (uint32_t)k == code ? tab.c[k] : v;
+  return v;
+}
+
+template <int BITS, int COPIES>
+__device__ __forceinline__ void pair_entries(const Tables& tab, uint32_t* lut, int tid) {
+  constexpr int NPAIR = 1 << (2 * BITS);
+  for (int e = tid; e < NPAIR; e += kScoreThreads) {
+    uint32_t ca, cb, ha, la, hb, lb;
+    pair_codes<BITS, COPIES>(e, ca, cb);
+    split_bf16(centroid_of<BITS>(tab, ca), ha, la);
+    split_bf16(centroid_of<BITS>(tab, cb), hb, lb);
+    lut[e * COPIES] = ha | (hb << 16);
+    lut[(NPAIR + e) * COPIES] = la | (lb << 16);
+  }
+}
+
+// WORDS = table words per copy set (NPAIR, or 2 NPAIR with the lo pairs).
+template <int WORDS, int COPIES>
+__device__ __forceinline__ void pair_replicate(uint32_t* lut, int tid) {
+  for (int i = tid; i < WORDS * COPIES; i += kScoreThreads)
+    if (i % COPIES != 0) lut[i] = lut[i - i % COPIES];
 }
 
 // Copies per pair table: one per lane of a half-wave up to 3 bits (16 KB at 3 bits), 4 at 4 bits.
@@ -303,26 +331,17 @@ __device__ __forceinline__ float table_pow(const Tables& tab) {
 }
 
 // f16 pair table: word e COPIES + c = the two centroids of entry e (bit 2p + i = plane p of
-// code i) divided by cpow, as an f16 pair; copy c read by lanes l % COPIES == c.
+// code i) divided by cpow, as an f16 pair; copy c read by lanes l % COPIES == c. Entries here,
+// copies by pair_replicate after a barrier.
 template <int BITS, int COPIES>
-__device__ __forceinline__ void fill_pair_table_f16(const Tables& tab, float inv_cpow, uint32_t* lut,
-                                                    int tid) {
+__device__ __forceinline__ void pair_entries_f16(const Tables& tab, float inv_cpow, uint32_t* lut,
+                                                 int tid) {
   constexpr int NPAIR = 1 << (2 * BITS);
-  for (int i = tid; i < NPAIR * COPIES; i += kScoreThreads) {
-    const int e = i / COPIES;
-    uint32_t ca = 0, cb = 0;
-#pragma unroll
-    for (int p = 0; p < BITS; ++p) {
-      ca |= ((e >> (2 * p)) & 1u) << p;
-      cb |= ((e >> (2 * p + 1)) & 1u) << p;
-    }
-    float va = 0.0f, vb = 0.0f;
-#pragma unroll
-    for (int k = 0; k < (1 << BITS); ++k) {
-      va = (uint32_t)k == ca ? tab.c[k] : va;
-      vb = (uint32_t)k == cb ? tab.c[k] : vb;
-    }
-    lut[i] = f16_bits(va * inv_cpow) | (f16_bits(vb * inv_cpow) << 16);
+  for (int e = tid; e < NPAIR; e += kScoreThreads) {
+    uint32_t ca, cb;
+    pair_codes<BITS, COPIES>(e, ca, cb);
+    lut[e * COPIES] = f16_bits(centroid_of<BITS>(tab, ca) * inv_cpow) |
+                      (f16_bits(centroid_of<BITS>(tab, cb) * inv_cpow) << 16);
   }
 }
 
@@ -361,13 +380,16 @@ __device__ __forceinline__ uint32_t planes_sel2(int oct) {
 }
 
 // Raw logits (divided by the head's and the table's powers of two) of one 16-token record tile:
-// acc[k] for head 4 oct + k and token tok. mulc is the pair-gathering multiplier of
-// pair_index, held in a register so that the compiler keeps it a 24-bit multiply.
+// acc[k] for head 4 oct + k and token tok. For b = 2, 3 the lane's plane bytes sit side by side
+// in one word y (byte p = plane p of its 8 coordinates); the pair index of coordinates 2 pr,
+// 2 pr + 1 is sum_p 4^p (plane-p bit pair), one byte dot product of the masked word with the
+// weights (1, 4, 16), which for odd pr comes out times 4 and is scaled into the table address.
 template <int M, int BITS, int COPIES>
 __device__ __forceinline__ floatx4_t tile_dots_f16(const uint32_t* w, const uint32_t* lut, int lane,
                                                    int oct, uint32_t sel01, uint32_t sel2,
-                                                   uint32_t mulc, const uint4 (&qa_hi)[M / 32],
+                                                   const uint4 (&qa_hi)[M / 32],
                                                    const uint4 (&qa_lo)[M / 32]) {
+  static_assert(COPIES == 32 || BITS > 3, "pair-table address shifts assume 32 copies");
   floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* lc = lut + (lane & (COPIES - 1));
 #pragma unroll
@@ -377,12 +399,14 @@ __device__ __forceinline__ floatx4_t tile_dots_f16(const uint32_t* w, const uint
     if constexpr (BITS == 2 || BITS == 3) {
       uint32_t y = __builtin_amdgcn_perm(wk[1], wk[0], sel01);
       if constexpr (BITS == 3) y = __builtin_amdgcn_perm(wk[2], y, sel2);
-      const uint32_t mask = BITS == 3 ? 0x030303u : 0x0303u;
+      const uint32_t y2 = y >> 4;
+      constexpr uint32_t mask = BITS == 3 ? 0x030303u : 0x0303u;
+      constexpr uint32_t wts = BITS == 3 ? 0x100401u : 0x0401u;
 #pragma unroll
       for (int pr = 0; pr < 4; ++pr) {
-        const uint32_t idx = __builtin_amdgcn_ubfe(__umul24(y & (mask << (2 * pr)), mulc),
-                                                   16 + 2 * pr, 2 * BITS);
-        z[pr] = lc[idx * COPIES];
+        const uint32_t src = pr < 2 ? y : y2;
+        const uint32_t d = __builtin_amdgcn_udot4(src & (mask << (2 * (pr & 1))), wts, 0u, false);
+        z[pr] = lc[d << ((pr & 1) ? 3 : 5)];
       }
     } else {
 #pragma unroll
@@ -454,12 +478,19 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
   };
   int bi = PCA ? basis_of_row(a.pca, rowbase + t_begin) : 0;
   uint32_t ring[PF][SW];
-#pragma unroll
-  for (int r = 0; r < PF; ++r)
-    if (r < n_steps) load_step(r, ring[r]);
   const float cpow = table_pow<BITS>(a.tab);
-  fill_pair_table_f16<BITS, COPIES>(a.tab, 1.0f / cpow, lut, tid);
-  prepare_queries<D, M, PCA>(a, b, kv, G, bi, qs, qmu, qT, part, qpow);
+  prepare_queries<D, M, PCA>(a, b, kv, G, bi, qs, qmu, qT, part, qpow, [&](int phase) {
+    if (phase == 0) {
+      // the first steps' record loads go out behind the prologue's own loads, which the
+      // prologue then waits for alone
+#pragma unroll
+      for (int r = 0; r < PF; ++r)
+        if (r < n_steps) load_step(r, ring[r]);
+      pair_entries_f16<BITS, COPIES>(a.tab, 1.0f / cpow, lut, tid);
+    } else {
+      pair_replicate<(1 << (2 * BITS)), COPIES>(lut, tid);
+    }
+  });
   uint4 qa_hi[KS], qa_lo[KS];  // A operand: head tok, coordinates 32 ks + 8 oct .. + 7
   float qm[4], qsc[4];         // q . mu and the product's scale of heads 4 oct + k
   auto operands = [&]() {
@@ -472,8 +503,6 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
   };
   operands();
   const uint32_t sel01 = planes_sel01(oct), sel2 = planes_sel2(oct);
-  uint32_t mulc = BITS == 3 ? 0x10410u : 0x10400u;
-  asm volatile("" : "+s"(mulc));
   int bnext = bi;
   for (int64_t g0 = 0; g0 < n_steps; g0 += PF) {
 #pragma unroll
@@ -506,8 +535,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
         uint32_t w[NWT];
 #pragma unroll
         for (int k = 0; k < NWT; ++k) w[k] = stage[(16 * tt + tok) * NWT + k];
-        const floatx4_t acc = tile_dots_f16<M, BITS, COPIES>(w, lut, lane, oct, sel01, sel2, mulc,
-                                                             qa_hi, qa_lo);
+        const floatx4_t acc = tile_dots_f16<M, BITS, COPIES>(w, lut, lane, oct, sel01, sel2, qa_hi,
+                                                             qa_lo);
         const float nrm = __uint_as_float(w[NWC]);
         const bool tv = t0 + 16 * tt + tok < t_end;
 #pragma unroll
@@ -570,8 +599,6 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
   const int64_t t_begin = (blockIdx.x % a.chunks) * a.chunk;
   const int64_t t_end = t_begin + a.chunk < k.T ? t_begin + a.chunk : k.T;
   const int64_t rowbase = b * k.rec_sb + kv * k.rec_sh;
-  fill_pair_table<BK, CK>(k.tab, lutk, tid);
-  fill_pair_table<BV, CV>(a.tv, lutv, tid);
   const uint32_t* krec32 = reinterpret_cast<const uint32_t*>(k.rec);
   const uint32_t* vrec32 = reinterpret_cast<const uint32_t*>(a.vrec);
   uint4 qa_hi[KS], qa_lo[KS];
@@ -613,7 +640,16 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
     const int bi = PCA ? basis_of_row(k.pca, rowbase + s0) : 0;
     if (bi != cur) {  // block-uniform
       __syncthreads();
-      prepare_queries<D, M, PCA>(k, b, kv, G, bi, qs, qmu, qT, part, qpow);
+      prepare_queries<D, M, PCA>(k, b, kv, G, bi, qs, qmu, qT, part, qpow, [&](int phase) {
+        if (cur >= 0) return;  // the pair tables are filled with the first basis
+        if (phase == 0) {
+          pair_entries<BK, CK>(k.tab, lutk, tid);
+          pair_entries<BV, CV>(a.tv, lutv, tid);
+        } else {
+          pair_replicate<2 * (1 << (2 * BK)), CK>(lutk, tid);
+          pair_replicate<2 * NPV, CV>(lutv, tid);
+        }
+      });
       query_operands<M>(qs, qmu, tok, oct, qa_hi, qa_lo, qm);
       cur = bi;
     }
