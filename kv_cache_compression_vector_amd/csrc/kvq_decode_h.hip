@@ -46,21 +46,24 @@ __device__ __forceinline__ uint32_t gather_bytes(const uint32_t* w, int sh) {
   return y;
 }
 
-template <int BITS>
-__device__ __forceinline__ uint32_t pair_of(uint32_t y, int pr) {
+// Word offset (index times C) in the pair table of the coordinates at bits pr, pr + 1 of the
+// plane bytes y (byte p = plane p). For b = 2, 3 the index sum_p 4^p (plane-p bit pair) is one
+// byte dot product of the masked bytes with the weights (1, 4, 16); at pr = 2 it comes out times
+// 4, which the shift into the table offset absorbs.
+template <int BITS, int C>
+__device__ __forceinline__ uint32_t pair_word(uint32_t y, int pr) {
   if constexpr (BITS == 1) {
-    return (y >> pr) & 3u;
-  } else if constexpr (BITS == 2 || BITS == 3) {
-    // y = a + b 2^8 (+ c 2^16), a, b, c < 4 after the mask: y (2^16 + 2^10 (+ 2^4)) holds
-    // a + 4 b (+ 16 c) in bits 16.. and nothing else reaches or carries into those bits
-    const uint32_t mask = (BITS == 3 ? 0x030303u : 0x0303u) << pr;
-    const uint32_t prod = __umul24(y & mask, BITS == 3 ? 0x10410u : 0x10400u);
-    return __builtin_amdgcn_ubfe(prod, 16 + pr, 2 * BITS);
+    return ((y >> pr) & 3u) * C;
+  } else if constexpr ((BITS == 2 || BITS == 3) && C == 32) {
+    constexpr uint32_t mask = BITS == 3 ? 0x030303u : 0x0303u;
+    constexpr uint32_t wts = BITS == 3 ? 0x100401u : 0x0401u;
+    const uint32_t d = __builtin_amdgcn_udot4(y & (mask << pr), wts, 0u, false);  // idx 4^(pr/2)
+    return d << (5 - pr);
   } else {
     uint32_t idx = 0;
 #pragma unroll
     for (int p = 0; p < BITS; ++p) idx |= ((y >> (8 * p + pr)) & 3u) << (2 * p);
-    return idx;
+    return idx * C;
   }
 }
 
@@ -110,6 +113,9 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
   constexpr int RCH = M / 8;
   __shared__ uint4 stage[BF16 ? kDhWaves * 16 * kDhVT * RCH : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int RPK = 64 / RCH;  // rows per whole-row store instruction
+  const int64_t lane_off = (int64_t)(lane / RCH) * a.ld + 8 * (lane % RCH);
+  uint16_t* const ylast = static_cast<uint16_t*>(a.y) + (a.n - 1) * a.ld + 8 * (lane % RCH);
   const int n16 = lane & 15, q = lane >> 4;
   fill_pairs<BITS, C>(a.tab, lut, tid, 64 * kDhWaves);
   // A operands (H_32, permuted) of the two output tiles: row m -> b' = 8 (m/4) + 4t + m % 4,
@@ -185,9 +191,9 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
           const uint32_t yb = gather_bytes<BITS>(w[vt], ((2 * q + half) * (M / 8)) % 32 + 4 * ab);
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            const uint32_t idx = pair_of<BITS>(yb, 2 * s);
-            hi[2 * half + s] = lut[idx * C + (lane & (C - 1))];
-            lo[2 * half + s] = lut[(NPAIR + idx) * C + (lane & (C - 1))];
+            const uint32_t off = pair_word<BITS, C>(yb, 2 * s) + (lane & (C - 1));
+            hi[2 * half + s] = lut[off];
+            lo[2 * half + s] = lut[NPAIR * C + off];
           }
         }
         const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -255,12 +261,13 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
         const int id = 64 * k + lane, row = id / RCH, ch = id % RCH;
         out[k] = stage[(wave * 16 * kDhVT + row) * RCH + (ch ^ (row & (RCH - 1)))];
       }
+      const int64_t v0 = st * 16 * kDhVT;  // the step's first row
+      uint16_t* const yp = static_cast<uint16_t*>(a.y) + v0 * a.ld + lane_off;
 #pragma unroll
       for (int k = 0; k < CH; ++k) {
-        const int id = 64 * k + lane, row = id / RCH, ch = id % RCH;
-        int64_t v = st * 16 * kDhVT + row;
-        v = v < a.n ? v : a.n - 1;  // rows past the end hold the last row's own bytes
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + v * a.ld + 8 * ch) = out[k];
+        // row v0 + RPK k + lane / RCH; rows past the end hold the last row's own bytes
+        const bool in = v0 + RPK * k + lane / RCH < a.n;
+        *reinterpret_cast<uint4*>(in ? yp + RPK * k * a.ld : ylast) = out[k];
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -299,6 +306,9 @@ __global__ __launch_bounds__(64 * kDpWaves) void k_decode_pca_h(DecodeArgs a, in
   __shared__ __attribute__((aligned(16))) float s_mu[D];
   __shared__ uint4 stage[BF16 ? kDpWaves * 16 * RCH : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int RPK = 64 / RCH;  // rows per whole-row store instruction
+  const int64_t lane_off = (int64_t)(lane / RCH) * a.ld + 8 * (lane % RCH);
+  uint16_t* const ylast = static_cast<uint16_t*>(a.y) + (a.n - 1) * a.ld + 8 * (lane % RCH);
   const int n16 = lane & 15, q = lane >> 4;
   fill_pairs<BITS, C>(a.tab, lut, tid, 64 * kDpWaves);
   uint4 Ah[2];  // H_32 fragments, as in k_decode_h
@@ -393,9 +403,9 @@ __global__ __launch_bounds__(64 * kDpWaves) void k_decode_pca_h(DecodeArgs a, in
           const uint32_t yb = gather_bytes<BITS>(w[vt], ((2 * q + half) * (R / 8)) % 32 + 4 * ab);
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            const uint32_t idx = pair_of<BITS>(yb, 2 * s);
-            hi[2 * half + s] = lut[idx * C + (lane & (C - 1))];
-            lo[2 * half + s] = lut[(NPAIR + idx) * C + (lane & (C - 1))];
+            const uint32_t off = pair_word<BITS, C>(yb, 2 * s) + (lane & (C - 1));
+            hi[2 * half + s] = lut[off];
+            lo[2 * half + s] = lut[NPAIR * C + off];
           }
         }
         const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -477,12 +487,13 @@ __global__ __launch_bounds__(64 * kDpWaves) void k_decode_pca_h(DecodeArgs a, in
           const int id = 64 * k + lane, row = id / RCH, ch = id % RCH;
           out[k] = stage[(wave * 16 + row) * RCH + (ch ^ (row & (RCH - 1)))];
         }
+        const int64_t v0 = tile * kDpRows + 32 * wave + 16 * vt;  // the 16 rows' first
+        uint16_t* const yp = static_cast<uint16_t*>(a.y) + v0 * a.ld + lane_off;
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
-          const int id = 64 * k + lane, row = id / RCH, ch = id % RCH;
-          int64_t vr = tile * kDpRows + 32 * wave + 16 * vt + row;
-          vr = vr < a.n ? vr : a.n - 1;  // rows past the end hold the last row's own bytes
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + vr * a.ld + 8 * ch) = out[k];
+          // row v0 + RPK k + lane / RCH; rows past the end hold the last row's own bytes
+          const bool in = v0 + RPK * k + lane / RCH < a.n;
+          *reinterpret_cast<uint4*>(in ? yp + RPK * k * a.ld : ylast) = out[k];
         }
         __builtin_amdgcn_wave_barrier();
       }

@@ -78,11 +78,14 @@ void k_encode_mx(EncodeArgs a, int64_t tiles_per_block) {
   auto load_tile = [&](int64_t tile, uint4 (&in)[PER]) {
     const int64_t rw = tile * TILE + ROWS * wave;
     const int l = opaque_lane();
+    // piece k of lane l is chunk l % RCH of row rw + (64 / RCH) k + l / RCH: a uniform row base
+    // plus the lane's offset, and the last row's chunk for rows past the end
+    const uint16_t* xp = a.x + (rw + l / RCH) * a.ld + 8 * (l % RCH);
+    const uint16_t* xlast = a.x + (a.n - 1) * a.ld + 8 * (l % RCH);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int id = k * 64 + l, p = id / RCH, ch = id % RCH;
-      const int64_t row = rw + p < a.n ? rw + p : a.n - 1;
-      in[k] = ld_stream(reinterpret_cast<const uint4*>(a.x + row * a.ld) + ch);
+      const bool inr = rw + (64 / RCH) * k + l / RCH < a.n;
+      in[k] = ld_stream(inr ? xp + (64 / RCH) * k * a.ld : xlast);
     }
   };
   uint4 nxt[PER];
