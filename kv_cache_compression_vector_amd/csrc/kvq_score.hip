@@ -6,13 +6,14 @@
 // a projection, x^ = mu + B v^ gives q.x^ = q.mu + (n/r) sum_i q''_i z^_i, q'' = H_r(s (.) B^T q).
 // The query heads that share a KV head (GQA) are scored together so each record is read once.
 //
-// Work split: the products run on MFMA (v_mfma_f32_16x16x32_bf16) as S^T = Q' Z^T for tiles of
-// 16 heads (G <= 8 used) x 16 tokens x 32 coordinates. A = the rotated queries, split into bf16
-// hi + lo once per block; B = the dequantised keys: each lane expands 8 coordinates of one token
-// through a 2^(2b)-entry LDS table indexed by the bit pairs of two coordinates, whose entries are
-// the two centroids' bf16 hi pair and lo pair, i.e. MFMA operand words. hi*hi + hi*lo + lo*hi
-// keep ~2^-16 relative accuracy per product with f32 accumulation. A block takes a run of tokens
-// of one (batch, KV head), so the query preparation is paid once per run.
+// Work split: the products run on MFMA (v_mfma_f32_16x16x32_f16) as S^T = Q' Z^T for tiles of
+// 16 heads (G <= 8 used) x 16 tokens x 32 coordinates. A = the rotated queries, scaled per head by
+// a power of two into the f16 range and split into f16 hi + lo once per block; B = the
+// dequantised keys: each lane expands 8 coordinates of one token through a 2^(2b)-entry LDS
+// table indexed by the bit pairs of two coordinates, whose entries are the two centroids as an
+// f16 pair (scaled by a power of two per table), i.e. MFMA operand words. hi*c + lo*c carry the
+// query to ~2^-22 and the centroid to 2^-11, products exact in the f32 accumulator. A block
+// takes a run of tokens of one (batch, KV head), so the query preparation is paid once per run.
 #include "kvq_device.h"
 #include "kvq_kernels.h"
 
@@ -252,56 +253,6 @@ __device__ __forceinline__ void pair_replicate(uint32_t* lut, int tid) {
 // Copies per pair table: one per lane of a half-wave up to 3 bits (16 KB at 3 bits), 4 at 4 bits.
 template <int BITS>
 constexpr int pair_copies() { return BITS <= 3 ? 32 : 4; }
-
-// The MFMA A operand of the rotated queries (head tok, coordinates 32 ks + 8 oct + [0, 8)) as bf16
-// hi and lo halves, and q . mu of heads 4 oct + [0, 4), from what prepare_queries left in LDS.
-template <int M>
-__device__ __forceinline__ void query_operands(const float* qs, const float* qmu, int tok, int oct,
-                                               uint4 (&qa_hi)[M / 32], uint4 (&qa_lo)[M / 32],
-                                               float (&qm)[4]) {
-  constexpr int H = kScoreHeads;
-#pragma unroll
-  for (int ks = 0; ks < M / 32; ++ks) {
-    uint32_t hi[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = tok < H ? qs[tok * M + 32 * ks + 8 * oct + e] : 0.0f;
-      split_bf16(x, hi[e], lo[e]);
-    }
-    qa_hi[ks] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                           hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-    qa_lo[ks] = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                           lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) qm[k] = 4 * oct + k < H ? qmu[4 * oct + k] : 0.0f;
-}
-
-// Raw logits of one 16-token record tile against the rotated queries: acc[k] = q . k^ for head
-// 4 oct + k and the tile's token tok, before the norm scale and q . mu.
-template <int M, int BITS, int COPIES>
-__device__ __forceinline__ floatx4_t tile_dots(const uint32_t* w, const uint32_t* lut, int lane,
-                                               int oct, const uint4 (&qa_hi)[M / 32],
-                                               const uint4 (&qa_lo)[M / 32]) {
-  constexpr int NPAIR = 1 << (2 * BITS);
-  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < M / 32; ++ks) {
-    uint32_t zh[4], zl[4];
-#pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {
-      const uint32_t idx = pair_index<BITS>(w + ks * BITS, 8 * oct, 2 * pr);
-      zh[pr] = lut[idx * COPIES + (lane & (COPIES - 1))];
-      zl[pr] = lut[(NPAIR + idx) * COPIES + (lane & (COPIES - 1))];
-    }
-    const uint4 bh = make_uint4(zh[0], zh[1], zh[2], zh[3]);
-    const uint4 blo = make_uint4(zl[0], zl[1], zl[2], zl[3]);
-    acc = mfma16(qa_hi[ks], bh, acc);
-    acc = mfma16(qa_hi[ks], blo, acc);
-    acc = mfma16(qa_lo[ks], bh, acc);
-  }
-  return acc;
-}
 
 // ---- f16 products for the score kernel -------------------------------------------------
 // The score multiplies each rotated query, scaled per head by a power of two into the f16
@@ -583,7 +534,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) float qs[H * M];
   __shared__ float qmu[H];
   __shared__ float qpow[H];
-  __shared__ uint32_t lutk[2 * (1 << (2 * BK)) * CK];
+  __shared__ uint32_t lutk[(1 << (2 * BK)) * CK];  // f16 centroid pairs of the K codec
   __shared__ uint32_t lutv[2 * NPV * CV];
   __shared__ __attribute__((aligned(16))) float qT[PCA ? D * H : 1];
   __shared__ __attribute__((aligned(16))) float part[PCA ? proj_slices<D, M>() * H * M + H * D / 2 : 1];
@@ -602,7 +553,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
   const uint32_t* krec32 = reinterpret_cast<const uint32_t*>(k.rec);
   const uint32_t* vrec32 = reinterpret_cast<const uint32_t*>(a.vrec);
   uint4 qa_hi[KS], qa_lo[KS];
-  float qm[4], mrun[4], lrun[4];  // softmax state of heads 4 oct + kk
+  float qm[4], qsc[4], mrun[4], lrun[4];  // q . mu, product scale, softmax state of heads 4 oct + kk
+  const float cpow = table_pow<BK>(k.tab);
+  const uint32_t sel01 = planes_sel01(oct), sel2 = planes_sel2(oct);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     mrun[kk] = -INFINITY;
@@ -643,14 +596,19 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
       prepare_queries<D, M, PCA>(k, b, kv, G, bi, qs, qmu, qT, part, qpow, [&](int phase) {
         if (cur >= 0) return;  // the pair tables are filled with the first basis
         if (phase == 0) {
-          pair_entries<BK, CK>(k.tab, lutk, tid);
+          pair_entries_f16<BK, CK>(k.tab, 1.0f / cpow, lutk, tid);
           pair_entries<BV, CV>(a.tv, lutv, tid);
         } else {
-          pair_replicate<2 * (1 << (2 * BK)), CK>(lutk, tid);
+          pair_replicate<(1 << (2 * BK)), CK>(lutk, tid);
           pair_replicate<2 * NPV, CV>(lutv, tid);
         }
       });
-      query_operands<M>(qs, qmu, tok, oct, qa_hi, qa_lo, qm);
+      query_operands_f16<M>(qs, qpow, tok, oct, qa_hi, qa_lo);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        qm[kk] = 4 * oct + kk < H ? qmu[4 * oct + kk] : 0.0f;
+        qsc[kk] = 4 * oct + kk < H ? qpow[4 * oct + kk] * cpow * k.tab.inv_m : 0.0f;
+      }
       cur = bi;
     }
     for (int u = 0; u < kUnits; ++u) {
@@ -675,12 +633,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
       float lg[2][4];
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
-        const floatx4_t d = tile_dots<M, BK, CK>(wk[tile], lutk, lane, oct, qa_hi, qa_lo);
+        const floatx4_t d = tile_dots_f16<M, BK, CK>(wk[tile], lutk, lane, oct, sel01, sel2, qa_hi,
+                                                     qa_lo);
         const int64_t t = t0 + 16 * tile + tok;
-        const float ns = __uint_as_float(wk[tile][NWK - 1]) * k.tab.inv_m;
+        const float nk = __uint_as_float(wk[tile][NWK - 1]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          float x = fmaf(d[kk], ns, qm[kk]) * a.scale;
+          float x = fmaf(d[kk], nk * qsc[kk], qm[kk]) * a.scale;
           if (a.softcap > 0.0f) x = a.softcap * tanhf(x / a.softcap);
           lg[tile][kk] = (t < t_end && 4 * oct + kk < G) ? x : -INFINITY;
         }
