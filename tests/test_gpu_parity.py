@@ -151,6 +151,42 @@ def test_score_packed_parity(D, bits, G):
     assert np.all(err <= bound), f"score error {err.max():.3g} (bound min {bound.min():.3g})"
 
 
+@pytest.mark.parametrize("cscale", [2.0 ** -30, 1.0, 2.0 ** 30])
+def test_score_packed_query_and_table_scales(cscale):
+    """The score's f16 products hold each query head and the centroid table scaled by powers of
+    two: heads 2^40, 2^-40, zero and unit in one GQA group, and tables scaled by 2^-30 .. 2^30,
+    stay within the normwise bound of the oracle's score."""
+    D, bits, G, B, Hkv, T = 128, 3, 4, 1, 2, 300
+    Hq = Hkv * G
+    cent = np.array([-2.2, -1.3, -0.7, -0.2, 0.25, 0.8, 1.4, 2.1], np.float64) * cscale
+    codec = kvq.Codec(D, bits, seed=23, centroids=cent.astype(np.float32))
+    k = _rows(B * Hkv * T, D, seed=33)
+    rec = kvq.encode(codec, k)
+    q = _rows(B * Hq, D, seed=43).view(B, Hq, D)
+    head_scale = torch.tensor([2.0 ** 40, 2.0 ** -40, 0.0, 1.0] * Hkv, device=DEV)
+    q = (q.float() * head_scale[None, :, None]).to(torch.bfloat16)
+    say(f"score scales D={D} b={bits} G={G} table x{cscale:g}")
+    s = kvq.score_packed(codec, q, rec, Hkv, T, rec_sb=Hkv * T, rec_sh=T)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    rec_h = rec.cpu().numpy().reshape(B, Hkv, T, -1)
+    q_h = bf16_host(q)
+    oc = oracle_codec_like(codec)
+    qq = np.repeat(q_h[:, :, None, :], T, axis=2)
+    rr = rec_h[:, np.arange(Hq) // G]
+    ref = oracle.score(oc, qq.reshape(-1, D), rr.reshape(-1, rr.shape[-1])).reshape(B, Hq, T)
+    sgn = oracle.signs(codec.seed, D).astype(np.float64)
+    qv = (q_h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    qp = oracle.fwht_rows(qv * sgn)
+    codes, norms = unpack_records(rr.reshape(-1, rr.shape[-1]), D, bits)
+    zh = oc.centroids.astype(np.float64)[codes].reshape(B, Hq, T, D)
+    scale = norms.reshape(B, Hq, T) / D * np.abs(qp[:, :, None, :] * zh).sum(-1)
+    err = np.abs(s - ref)
+    bound = 1e-3 * np.maximum(np.abs(ref), scale)
+    assert np.all(err <= bound), f"score error {err.max():.3g} (bound min {bound.min():.3g})"
+    assert np.all(s[:, 2::G] == 0.0), "a zero query head scores zero"
+
+
 @pytest.mark.parametrize("D,bits,T_", [(128, 2, 2.0), (64, 3, 1.5), (256, 2, 2.5), (128, 4, 2.0)])
 def test_outlier_parity(D, bits, T_):
     n = 3000 + 13
