@@ -68,12 +68,13 @@ __device__ __forceinline__ uint32_t pair_word(uint32_t y, int pr) {
 }
 
 // Pair table: entry e (bit 2p + i = plane p of code i) = the two centroids as a bf16 hi pair
-// (lut[e C + c]) and lo pair (lut[(NPAIR + e) C + c]), copy c read by lanes l % C == c.
+// (lut[e C + c]) and lo pair (lut[(NPAIR + e) C + c]), copy c read by lanes l % C == c. Filled
+// in two phases around a block barrier: pair_entries forms each entry once (copy 0) and
+// pair_copies replicates it, consecutive threads writing consecutive words.
 template <int BITS, int C>
-__device__ __forceinline__ void fill_pairs(const Tables& tab, uint32_t* lut, int tid, int nthr) {
+__device__ __forceinline__ void pair_entries(const Tables& tab, uint32_t* lut, int tid, int nthr) {
   constexpr int NPAIR = 1 << (2 * BITS);
-  for (int i = tid; i < NPAIR * C; i += nthr) {
-    const int e = i / C;
+  for (int e = tid; e < NPAIR; e += nthr) {
     uint32_t ca = 0, cb = 0;
 #pragma unroll
     for (int p = 0; p < BITS; ++p) {
@@ -89,9 +90,16 @@ __device__ __forceinline__ void fill_pairs(const Tables& tab, uint32_t* lut, int
     const uint32_t ha = f32_to_bf16_rne(va), hb = f32_to_bf16_rne(vb);
     const uint32_t la = f32_to_bf16_rne(va - __uint_as_float(ha << 16));
     const uint32_t lb = f32_to_bf16_rne(vb - __uint_as_float(hb << 16));
-    lut[i] = ha | (hb << 16);
-    lut[NPAIR * C + i] = la | (lb << 16);
+    lut[e * C] = ha | (hb << 16);
+    lut[(NPAIR + e) * C] = la | (lb << 16);
   }
+}
+
+template <int BITS, int C>
+__device__ __forceinline__ void pair_copies(uint32_t* lut, int tid, int nthr) {
+  constexpr int WORDS = 2 * (1 << (2 * BITS)) * C;
+  for (int i = tid; i < WORDS; i += nthr)
+    if (i % C != 0) lut[i] = lut[i - i % C];
 }
 
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
   const int64_t lane_off = (int64_t)(lane / RCH) * a.ld + 8 * (lane % RCH);
   uint16_t* const ylast = static_cast<uint16_t*>(a.y) + (a.n - 1) * a.ld + 8 * (lane % RCH);
   const int n16 = lane & 15, q = lane >> 4;
-  fill_pairs<BITS, C>(a.tab, lut, tid, 64 * kDhWaves);
+  pair_entries<BITS, C>(a.tab, lut, tid, 64 * kDhWaves);
   // A operands (H_32, permuted) of the two output tiles: row m -> b' = 8 (m/4) + 4t + m % 4,
   // column k = 8q + e -> b = 8 (e % 4) + 2q + e / 4
   uint4 A[2];
@@ -150,6 +158,8 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
       sg[ap][h] = BF16 ? ((s0 << 15) | (s1 << 31)) : (s0 | (s1 << 1));
     }
   }
+  __syncthreads();
+  pair_copies<BITS, C>(lut, tid, 64 * kDhWaves);
   __syncthreads();
   const uint32_t* rec32 = reinterpret_cast<const uint32_t*>(a.rec);
   const int64_t n_steps = (a.n + 16 * kDhVT - 1) / (16 * kDhVT);
@@ -310,7 +320,7 @@ __global__ __launch_bounds__(64 * kDpWaves) void k_decode_pca_h(DecodeArgs a, in
   const int64_t lane_off = (int64_t)(lane / RCH) * a.ld + 8 * (lane % RCH);
   uint16_t* const ylast = static_cast<uint16_t*>(a.y) + (a.n - 1) * a.ld + 8 * (lane % RCH);
   const int n16 = lane & 15, q = lane >> 4;
-  fill_pairs<BITS, C>(a.tab, lut, tid, 64 * kDpWaves);
+  pair_entries<BITS, C>(a.tab, lut, tid, 64 * kDpWaves);  // copies with the first basis
   uint4 Ah[2];  // H_32 fragments, as in k_decode_h
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -369,6 +379,7 @@ __global__ __launch_bounds__(64 * kDpWaves) void k_decode_pca_h(DecodeArgs a, in
     bi = bi < 0 ? 0 : (bi >= a.pca.count ? a.pca.count - 1 : bi);
     if (bi != cur) {
       __syncthreads();
+      if (cur < 0) pair_copies<BITS, C>(lut, tid, 64 * kDpWaves);
       const uint4* Bk = reinterpret_cast<const uint4*>(a.pca.basis + (int64_t)bi * D * R);
       for (int e = tid; e < D * HCH; e += 64 * kDpWaves) {
         const uint4 w = Bk[e];
