@@ -282,17 +282,22 @@ __device__ __forceinline__ float table_pow(const Tables& tab) {
 }
 
 // f16 pair table: word e COPIES + c = the two centroids of entry e (bit 2p + i = plane p of
-// code i) divided by cpow, as an f16 pair; copy c read by lanes l % COPIES == c. Entries here,
+// code i) divided by cpow, as an f16 pair; copy c read by lanes l % COPIES == c. With LO, words
+// (NPAIR + e) COPIES + c hold the pair's f16 remainders (centroid to ~2^-22). Entries here,
 // copies by pair_replicate after a barrier.
-template <int BITS, int COPIES>
+template <int BITS, int COPIES, bool LO>
 __device__ __forceinline__ void pair_entries_f16(const Tables& tab, float inv_cpow, uint32_t* lut,
                                                  int tid) {
   constexpr int NPAIR = 1 << (2 * BITS);
   for (int e = tid; e < NPAIR; e += kScoreThreads) {
     uint32_t ca, cb;
     pair_codes<BITS, COPIES>(e, ca, cb);
-    lut[e * COPIES] = f16_bits(centroid_of<BITS>(tab, ca) * inv_cpow) |
-                      (f16_bits(centroid_of<BITS>(tab, cb) * inv_cpow) << 16);
+    const float va = centroid_of<BITS>(tab, ca) * inv_cpow, vb = centroid_of<BITS>(tab, cb) * inv_cpow;
+    const _Float16 ha = (_Float16)va, hb = (_Float16)vb;
+    lut[e * COPIES] = (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+    if constexpr (LO)
+      lut[(NPAIR + e) * COPIES] = f16_bits(va - (float)ha) | (f16_bits(vb - (float)hb) << 16);
   }
 }
 
@@ -335,7 +340,7 @@ __device__ __forceinline__ uint32_t planes_sel2(int oct) {
 // in one word y (byte p = plane p of its 8 coordinates); the pair index of coordinates 2 pr,
 // 2 pr + 1 is sum_p 4^p (plane-p bit pair), one byte dot product of the masked word with the
 // weights (1, 4, 16), which for odd pr comes out times 4 and is scaled into the table address.
-template <int M, int BITS, int COPIES>
+template <int M, int BITS, int COPIES, bool LO>
 __device__ __forceinline__ floatx4_t tile_dots_f16(const uint32_t* w, const uint32_t* lut, int lane,
                                                    int oct, uint32_t sel01, uint32_t sel2,
                                                    const uint4 (&qa_hi)[M / 32],
@@ -346,7 +351,7 @@ __device__ __forceinline__ floatx4_t tile_dots_f16(const uint32_t* w, const uint
 #pragma unroll
   for (int ks = 0; ks < M / 32; ++ks) {
     const uint32_t* wk = w + ks * BITS;
-    uint32_t z[4];
+    uint32_t z[4], zl[4];
     if constexpr (BITS == 2 || BITS == 3) {
       uint32_t y = __builtin_amdgcn_perm(wk[1], wk[0], sel01);
       if constexpr (BITS == 3) y = __builtin_amdgcn_perm(wk[2], y, sel2);
@@ -357,15 +362,22 @@ __device__ __forceinline__ floatx4_t tile_dots_f16(const uint32_t* w, const uint
       for (int pr = 0; pr < 4; ++pr) {
         const uint32_t src = pr < 2 ? y : y2;
         const uint32_t d = __builtin_amdgcn_udot4(src & (mask << (2 * (pr & 1))), wts, 0u, false);
-        z[pr] = lc[d << ((pr & 1) ? 3 : 5)];
+        const uint32_t off = d << ((pr & 1) ? 3 : 5);
+        z[pr] = lc[off];
+        if constexpr (LO) zl[pr] = lc[(1 << (2 * BITS)) * COPIES + off];
       }
     } else {
 #pragma unroll
-      for (int pr = 0; pr < 4; ++pr) z[pr] = lc[pair_index<BITS>(wk, 8 * oct, 2 * pr) * COPIES];
+      for (int pr = 0; pr < 4; ++pr) {
+        const uint32_t off = pair_index<BITS>(wk, 8 * oct, 2 * pr) * COPIES;
+        z[pr] = lc[off];
+        if constexpr (LO) zl[pr] = lc[(1 << (2 * BITS)) * COPIES + off];
+      }
     }
     const uint4 bz = make_uint4(z[0], z[1], z[2], z[3]);
     acc = mfma16h(qa_hi[ks], bz, acc);
     acc = mfma16h(qa_lo[ks], bz, acc);
+    if constexpr (LO) acc = mfma16h(qa_hi[ks], make_uint4(zl[0], zl[1], zl[2], zl[3]), acc);
   }
   return acc;
 }
@@ -437,7 +449,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
 #pragma unroll
       for (int r = 0; r < PF; ++r)
         if (r < n_steps) load_step(r, ring[r]);
-      pair_entries_f16<BITS, COPIES>(a.tab, 1.0f / cpow, lut, tid);
+      pair_entries_f16<BITS, COPIES, false>(a.tab, 1.0f / cpow, lut, tid);
     } else {
       pair_replicate<(1 << (2 * BITS)), COPIES>(lut, tid);
     }
@@ -486,8 +498,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
         uint32_t w[NWT];
 #pragma unroll
         for (int k = 0; k < NWT; ++k) w[k] = stage[(16 * tt + tok) * NWT + k];
-        const floatx4_t acc = tile_dots_f16<M, BITS, COPIES>(w, lut, lane, oct, sel01, sel2, qa_hi,
-                                                             qa_lo);
+        const floatx4_t acc =
+            tile_dots_f16<M, BITS, COPIES, false>(w, lut, lane, oct, sel01, sel2, qa_hi, qa_lo);
         const float nrm = __uint_as_float(w[NWC]);
         const bool tv = t0 + 16 * tt + tok < t_end;
 #pragma unroll
@@ -534,7 +546,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) float qs[H * M];
   __shared__ float qmu[H];
   __shared__ float qpow[H];
-  __shared__ uint32_t lutk[(1 << (2 * BK)) * CK];  // f16 centroid pairs of the K codec
+  __shared__ uint32_t lutk[2 * (1 << (2 * BK)) * CK];  // f16 centroid pairs (hi | lo) of the K codec
   __shared__ uint32_t lutv[2 * NPV * CV];
   __shared__ __attribute__((aligned(16))) float qT[PCA ? D * H : 1];
   __shared__ __attribute__((aligned(16))) float part[PCA ? proj_slices<D, M>() * H * M + H * D / 2 : 1];
@@ -596,10 +608,10 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
       prepare_queries<D, M, PCA>(k, b, kv, G, bi, qs, qmu, qT, part, qpow, [&](int phase) {
         if (cur >= 0) return;  // the pair tables are filled with the first basis
         if (phase == 0) {
-          pair_entries_f16<BK, CK>(k.tab, 1.0f / cpow, lutk, tid);
+          pair_entries_f16<BK, CK, true>(k.tab, 1.0f / cpow, lutk, tid);
           pair_entries<BV, CV>(a.tv, lutv, tid);
         } else {
-          pair_replicate<(1 << (2 * BK)), CK>(lutk, tid);
+          pair_replicate<2 * (1 << (2 * BK)), CK>(lutk, tid);
           pair_replicate<2 * NPV, CV>(lutv, tid);
         }
       });
@@ -633,8 +645,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
       float lg[2][4];
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
-        const floatx4_t d = tile_dots_f16<M, BK, CK>(wk[tile], lutk, lane, oct, sel01, sel2, qa_hi,
-                                                     qa_lo);
+        const floatx4_t d =
+            tile_dots_f16<M, BK, CK, true>(wk[tile], lutk, lane, oct, sel01, sel2, qa_hi, qa_lo);
         const int64_t t = t0 + 16 * tile + tok;
         const float nk = __uint_as_float(wk[tile][NWK - 1]);
 #pragma unroll
