@@ -192,7 +192,10 @@ kvq_status kvq_decode(const kvq_codec* codec, const void* records_dev, int64_t n
  * records_dev: record (b, kv, t) at index b*rec_sb + kv*rec_sh + t.
  * scores_dev: f32, score (b, h, t) at scores_dev + b*s_sb + h*s_sh + t.
  * Hq must be a multiple of Hkv (query heads h*Hkv/Hq share kv head). Outlier lists are not
- * consulted (score requires codec->outlier_T == 0). */
+ * consulted (score requires codec->outlier_T == 0).
+ * Accuracy: the products are formed in f16 with the query held to ~2^-22 and each centroid to
+ * 2^-11 (both scaled by powers of two into the f16 range), so |error| <= ~5e-4 *
+ * (n_t/m) sum_i |q'_i z^_{t,i}|, under the 1e-3 normwise bar on scores. */
 kvq_status kvq_score_packed(const kvq_codec* codec, const void* q_dev, int32_t B, int32_t Hq,
                             int64_t q_sb, int64_t q_sh, const void* records_dev, int32_t Hkv,
                             int64_t T, int64_t rec_sb, int64_t rec_sh, float* scores_dev,
