@@ -70,6 +70,41 @@ __device__ __forceinline__ void chunk_sign_masks(const Tables& tab, int c, uint3
 // Partner value across lanes: lane ^ mask within the wave.
 __device__ __forceinline__ float lane_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// lane ^ MASK for a compile-time MASK. Inside a row of 16 lanes the exchange is a DPP move:
+// quad permutes [1,0,3,2] (xor 1) and [2,3,0,1] (xor 2), the row rotation by 8 (xor 8), and for
+// xor 4 the half-row mirror (xor 7) followed by the quad permute [3,2,1,0] (xor 3). Wider masks
+// use the lane-permute path.
+template <int MASK>
+__device__ __forceinline__ float lane_xor_c(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (MASK == 1) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+  } else if constexpr (MASK == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+  } else if constexpr (MASK == 4) {
+    const int m = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);
+    return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true));
+  } else if constexpr (MASK == 8) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true));
+  } else {
+    return __shfl_xor(v, MASK, 64);
+  }
+}
+
+// Cross-lane butterfly stages MASK, 2 MASK, .. < LPV of fwht_vector.
+template <int MASK, int LPV>
+__device__ __forceinline__ void fwht_lane_stages(float (&v)[8], int c) {
+  if constexpr (MASK < LPV) {
+    const bool upper = (c & MASK) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = lane_xor_c<MASK>(v[j]);
+      v[j] = upper ? (p - v[j]) : (v[j] + p);
+    }
+    fwht_lane_stages<2 * MASK, LPV>(v, c);
+  }
+}
+
 // Unnormalised Walsh-Hadamard transform (Sylvester order) of the M coordinates held by the
 // LPV lanes of a vector: coordinate bits 0..2 are the slot index inside the lane, bits 3.. are
 // the lane index c. The element whose butterfly bit is 0 receives a + b, the other a - b.
@@ -84,15 +119,7 @@ __device__ __forceinline__ void fwht_vector(float (&v)[8], int c) {
         v[j] = a + b;
         v[j + h] = a - b;
       }
-#pragma unroll
-  for (int m = 1; m < LPV; m <<= 1) {
-    const bool upper = (c & m) != 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = lane_xor(v[j], m);
-      v[j] = upper ? (p - v[j]) : (v[j] + p);
-    }
-  }
+  fwht_lane_stages<1, LPV>(v, c);
 }
 
 // Sum over the LPV lanes of one vector (all of them receive the total).
