@@ -65,10 +65,7 @@ void k_encode(EncodeArgs a) {
     const int64_t vec = it * L::VPW + vw;
     const bool valid = vec < a.n;
     const int64_t vec0 = it * L::VPW;
-    stage_rows_in<M>([&](int j) {  // rows past the end repeat the last row (results unused)
-      const int64_t r = vec0 + j < a.n ? vec0 + j : a.n - 1;
-      return a.x + r * a.ld;
-    }, tile);
+    stage_rows_linear<M>(a.x, a.ld, vec0, a.n, tile);  // rows past the end repeat the last row
     float v[L::K];
     const float ss = load_part<L::K>(tile + lane * St::S, part_signs<M>(a.tab, s_sign, q), v);
     const float n = sqrtf(part_sum<L::Q>(ss));
@@ -114,10 +111,7 @@ __device__ __forceinline__ float rotate_owned(const EncodeArgs& a, const uint32_
   using St = Stage<L::K>;
   const int lane = threadIdx.x & 63;
   const int64_t vec0 = it * L::VPW;
-  stage_rows_in<M>([&](int j) {  // rows past the end repeat the last row (results unused)
-    const int64_t r = vec0 + j < a.n ? vec0 + j : a.n - 1;
-    return a.x + r * a.ld;
-  }, tile);
+  stage_rows_linear<M>(a.x, a.ld, vec0, a.n, tile);  // rows past the end repeat the last row
   const float ss = load_part<L::K>(tile + lane * St::S, part_signs<M>(a.tab, s_sign, q), v);
   const float n = sqrtf(part_sum<L::Q>(ss));
   fwht_regs<L::K, 8>(v);
@@ -360,9 +354,12 @@ void k_evict(EvictArgs a) {
     const EvictCache& ec = a.c[k];
     const int64_t r0 = g0 - ec.row_begin, r = r0 + vw;
     stage_rows_in<M>([&](int j) {
+      // ring slot tail_head + rr < 2 tail_cap (both terms are below tail_cap): one conditional
+      // subtract wraps it; caches hold Hadamard records, so rows are M = head_dim elements
       const int64_t rr = r0 + j;
-      return rr < ec.tail_len ? ec.tail + ((ec.tail_head + rr) % ec.tail_cap) * a.D
-                              : ec.fresh + (rr - ec.tail_len) * a.D;
+      const int64_t slot = ec.tail_head + rr;
+      return rr < ec.tail_len ? ec.tail + (slot >= ec.tail_cap ? slot - ec.tail_cap : slot) * M
+                              : ec.fresh + (rr - ec.tail_len) * M;
     }, tile);
     float v[L::K];
     const float ss = load_part<L::K>(tile + lane * St::S, part_signs<M>(a.tab, s_sign, q), v);

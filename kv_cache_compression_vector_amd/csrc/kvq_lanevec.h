@@ -123,6 +123,34 @@ __device__ __forceinline__ void stage_rows_in(RowFn row_of, uint4* tile) {
   __builtin_amdgcn_wave_barrier();
 }
 
+// stage_rows_in for the rows x + (vec0 + j) ld, rows >= n repeating the last row. Part k of the
+// lane is a fixed row and column offset plus k (64 / (CH Q)) rows, so every load adds a uniform
+// stride to the lane's first row instead of forming a 64-bit row product.
+template <int M>
+__device__ __forceinline__ void stage_rows_linear(const uint16_t* __restrict__ x, int64_t ld,
+                                                  int64_t vec0, int64_t n, uint4* tile) {
+  using L = LV<M>;
+  using St = Stage<L::K>;
+  constexpr int CH = St::CH, JK = 64 / (CH * L::Q);  // vectors advanced per load
+  static_assert(64 % CH == 0 && (64 / CH) % L::Q == 0, "row parts per load");
+  const int lane = threadIdx.x & 63;
+  const int j0 = (lane / CH) / L::Q, col = ((lane / CH) % L::Q) * L::K + 8 * (lane % CH);
+  const uint16_t* first = x + (vec0 + j0) * ld + col;
+  const uint16_t* last = x + (n - 1) * ld + col;
+  uint4 r[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const bool in = vec0 + j0 + JK * k < n;
+    r[k] = ld_stream(in ? first + JK * k * ld : last);
+  }
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int id = k * 64 + lane, p = id / CH, c = id % CH;
+    tile[p * St::S + c] = r[k];
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Coalesced store of the wave's tile (bf16 row parts) to rows vec0 .. (rows >= n skipped).
 template <int M>
 __device__ __forceinline__ void stage_rows_out(uint16_t* __restrict__ y, int64_t ld, int64_t vec0,
