@@ -98,6 +98,41 @@ def test_pca_many_bases_and_score():
                     assert np.all(err <= bound), f"score l={l} h={h} b={bb} g={g}: {err.max():.3g}"
 
 
+def test_pca_score_bases_change_inside_a_block_run():
+    """Bases change every 256 rows, inside the token run that one score block takes: with 128
+    (batch, KV head) pairs of 2048 tokens each block takes at least two 256-token segments, so
+    the block prepares its queries again for every new basis."""
+    D, r, bits, B, H, T, G, NB = 128, 64, 3, 64, 2, 2048, 6, 5
+    mu, b = _bases(D, r, NB, seed=11)
+    basis = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(DEV).contiguous()
+    mean = torch.from_numpy(mu).to(DEV).contiguous()
+    index_h = (np.arange(B * H * T // 256) * 3 % NB).astype(np.int32)  # neighbours differ
+    codec = kvq.Codec(D, bits, seed=42, proj_rank=r, basis=basis, mean=mean,
+                      basis_index=torch.from_numpy(index_h).to(DEV), basis_block_rows=256)
+    x = synth.iid_normal((B * H * T, D), seed=21, device=DEV)
+    say(f"pca score, bases every 256 rows: B={B} H={H} T={T} G={G}")
+    rec = kvq.encode(codec, x)
+    q = synth.iid_normal((B, H * G, D), seed=22, device=DEV)
+    s = kvq.score_packed(codec, q, rec, Hkv=H, T=T, rec_sb=H * T, rec_sh=T)
+    torch.cuda.synchronize()
+    recn, sn, qh = rec.cpu().numpy(), s.cpu().numpy(), bf16_host(q)
+    for bb, h in [(0, 0), (31, 1), (63, 1)]:
+        for blk in range(T // 256):
+            row0 = (bb * H + h) * T + 256 * blk
+            k = int(index_h[row0 // 256])
+            oc = _oracle_codec(D, r, bits, 42, mu[k], b[k])
+            recs = recn[row0: row0 + 256]
+            ynorm = np.linalg.norm(oracle.decode(oc, recs), axis=1)
+            for g in range(G):
+                hq = h * G + g
+                sref = oracle.score(oc, np.repeat(qh[bb, hq][None], 256, 0), recs)
+                got = sn[bb, hq, 256 * blk: 256 * (blk + 1)]
+                qn = np.linalg.norm((qh[bb, hq].astype(np.uint32) << 16).view(np.float32))
+                bound = 1e-3 * np.maximum(np.abs(sref), qn * ynorm)
+                err = np.abs(got - sref)
+                assert np.all(err <= bound), f"b={bb} h={h} block {blk} g={g}: {err.max():.3g}"
+
+
 def test_pca_refusals():
     D, r = 128, 64
     basis = torch.zeros(D, r, dtype=torch.bfloat16, device=DEV)
