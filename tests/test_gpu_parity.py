@@ -239,19 +239,17 @@ def test_outlier_capacity_overflow_reports_and_truncates():
     assert torch.isfinite(y).all()
 
 
-def test_append_evict_matches_oracle_model():
-    D, bits, window, margin = 128, 3, 200, 16
+def _append_evict_against_model(window, margin, tail_cap, t_news, n_caches=3, seed=1):
+    D, bits = 128, 3
     codec = kvq.Codec(D, bits, seed=77)
-    n_caches = 3
-    caches = [kvq.Cache(codec, packed_cap=4096, tail_cap=1500, window=window, margin=margin,
+    caches = [kvq.Cache(codec, packed_cap=4096, tail_cap=tail_cap, window=window, margin=margin,
                         device=DEV) for _ in range(n_caches)]
     models = [oracle.CacheModel(oracle_codec_like(codec), window, margin) for _ in range(n_caches)]
     appended = [np.zeros((0, D), np.uint16) for _ in range(n_caches)]
-    seed = 1
-    for t_new in [700, 1, 1, 129, 0, 1, 300, 5, 0, 1]:
+    for t_new in t_news:
         rows = [_rows(max(t_new, 1), D, seed=seed + k) for k in range(n_caches)]
         seed += 10
-        say(f"append t_new={t_new}")
+        say(f"append t_new={t_new} (tail_cap={tail_cap}, window={window})")
         ev = kvq.append_evict_chunk(codec, caches, rows if t_new else None, t_new)
         for k in range(n_caches):
             host = bf16_host(rows[k][:t_new]) if t_new else np.zeros((0, D), np.uint16)
@@ -266,6 +264,19 @@ def test_append_evict_matches_oracle_model():
                 got = c.packed[: c.packed_len].cpu().numpy()
                 ref = oracle.encode(oracle_codec_like(codec), appended[k][: c.packed_len])
                 compare_codes(got, ref, D, bits, f"evict cache {k}")
+    return caches
+
+
+def test_append_evict_matches_oracle_model():
+    _append_evict_against_model(200, 16, 1500, [700, 1, 1, 129, 0, 1, 300, 5, 0, 1])
+
+
+def test_append_evict_tail_ring_wraps():
+    """A 480-row tail ring whose head passes its end several times: the evicted chunks read
+    rows across the wrap."""
+    t_news = [150, 1, 130, 64, 1, 1, 120, 37, 0, 150, 1, 90, 149, 1, 77, 150, 3, 140, 1, 66]
+    caches = _append_evict_against_model(160, 16, 480, t_news, seed=501)
+    assert all(c.packed_len > 480 for c in caches)  # more rows left the ring than it holds: it wrapped
 
 
 def test_config1_full_roundtrip():
