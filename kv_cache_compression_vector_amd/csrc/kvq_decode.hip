@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
       o.y = f32_to_bf16_rne(zh[2]) | (f32_to_bf16_rne(zh[3]) << 16);
       o.z = f32_to_bf16_rne(zh[4]) | (f32_to_bf16_rne(zh[5]) << 16);
       o.w = f32_to_bf16_rne(zh[6]) | (f32_to_bf16_rne(zh[7]) << 16);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + vec * a.ld + 8 * c) = o;
+      st_stream(static_cast<uint16_t*>(a.y) + vec * a.ld + 8 * c, o);  // rows are written once
     } else {
       float* yr = static_cast<float*>(a.y) + vec * a.ld + 8 * c;
       *reinterpret_cast<float4*>(yr) = make_float4(zh[0], zh[1], zh[2], zh[3]);

@@ -262,7 +262,8 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
       }
     }
     if constexpr (BF16) {
-      // whole rows: each instruction writes 64 consecutive 16-byte chunks of the step's rows
+      // whole rows: each instruction writes 64 consecutive 16-byte chunks of the step's rows,
+      // as streaming (nontemporal) stores: the rows are not read again by this kernel
       __builtin_amdgcn_wave_barrier();
       constexpr int CH = 16 * kDhVT * RCH / 64;
       uint4 out[CH];
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
       for (int k = 0; k < CH; ++k) {
         // row v0 + RPK k + lane / RCH; rows past the end hold the last row's own bytes
         const bool in = v0 + RPK * k + lane / RCH < a.n;
-        *reinterpret_cast<uint4*>(in ? yp + RPK * k * a.ld : ylast) = out[k];
+        st_stream(in ? yp + RPK * k * a.ld : ylast, out[k]);
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -489,7 +490,8 @@ __global__ __launch_bounds__(64 * kDpWaves) void k_decode_pca_h(DecodeArgs a, in
         }
       }
       if constexpr (BF16) {
-        // the 16 rows leave whole: each instruction writes 64 consecutive 16-byte chunks
+        // the 16 rows leave whole: each instruction writes 64 consecutive 16-byte chunks, as
+        // streaming (nontemporal) stores
         __builtin_amdgcn_wave_barrier();
         constexpr int CH = 16 * RCH / 64;
         uint4 out[CH];
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(64 * kDpWaves) void k_decode_pca_h(DecodeArgs a, in
         for (int k = 0; k < CH; ++k) {
           // row v0 + RPK k + lane / RCH; rows past the end hold the last row's own bytes
           const bool in = v0 + RPK * k + lane / RCH < a.n;
-          *reinterpret_cast<uint4*>(in ? yp + RPK * k * a.ld : ylast) = out[k];
+          st_stream(in ? yp + RPK * k * a.ld : ylast, out[k]);
         }
         __builtin_amdgcn_wave_barrier();
       }

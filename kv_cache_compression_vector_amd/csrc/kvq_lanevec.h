@@ -33,18 +33,6 @@ __host__ __device__ constexpr int coord_at(int pos, int M) { return 8 * (pos % (
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// Streaming 16-byte load / store (data touched once).
-__device__ __forceinline__ uint4 ld_stream(const void* p) {
-  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void st_stream(void* p, uint4 v) {
-  const u32x4_t x = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(x, static_cast<u32x4_t*>(p));
-}
-
 // Two f32 -> packed bf16 (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_t v = {lo, hi};
