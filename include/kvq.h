@@ -103,8 +103,12 @@ typedef struct kvq_codec {
                                     many rows (a multiple of 256); block k uses basis
                                     basis_index_dev[k]. For the packed score the row of record
                                     (b, kv, t) is b*rec_sb + kv*rec_sh + t.                     */
-  const int32_t* basis_index_dev;   /* PCA with basis_count > 1: int32 per block, < basis_count;
-                                       the caller guarantees it covers every block touched      */
+  const int32_t* basis_index_dev;   /* PCA with basis_count > 1: int32 per block, in
+                                       [0, basis_count); the caller guarantees it covers every
+                                       block touched. The host never reads it (reading would
+                                       need a synchronisation), so the kernels clamp an entry
+                                       outside the range into it: a negative entry selects basis
+                                       0, an entry >= basis_count selects basis basis_count - 1. */
   const uint16_t* unbasis_dev;   /* projection codecs only: bf16 [basis_count][D][r], the decode
                                     basis C (same layout and indexing as basis_dev). Decode gives
                                     x^ = mu + C v^, the packed score and attention use C^T q. NULL:
@@ -151,7 +155,9 @@ typedef struct kvq_cache {
  * [arc PR #98, "Eviction is chunked, on purpose": EVICT_CHUNK = 128]. */
 #define KVQ_EVICT_CHUNK 128
 
-/* Bytes of one record for this codec: m*b/8 + 4. Returns 0 for an invalid codec. */
+/* Bytes of one record for this codec: m*b/8 + 4 (b bit-planes of m codes, then the f32 norm:
+ * 260 B at head_dim 512 and 4 bits, the packed row of arc PR #98's "What landed" bytes table,
+ * against 1,026 B for bf16). Returns 0 for an invalid codec. */
 size_t kvq_record_bytes(const kvq_codec* codec);
 
 /* Workspace bytes kvq_encode needs for n vectors when codec->outlier_T > 0 (0 otherwise): the
@@ -228,7 +234,11 @@ kvq_status kvq_attend_packed(const kvq_codec* kcodec, const kvq_codec* vcodec, c
 
 /* Build an empty cache over caller-owned buffers: packed_dev holds packed_cap records,
  * tail_dev holds tail_cap bf16 rows of head_dim. window >= 0, margin >= 0. Host only.
- * Outlier lists are not supported in caches (codec->outlier_T must be 0). */
+ * Outlier lists are not supported in caches (codec->outlier_T must be 0).
+ * The cache is the two-region layout of arc PR #98, "What landed": a dense bf16 tail of the
+ * newest rows in front of a packed region of records, sized by the caller. The struct records a
+ * fingerprint of the codec, so a cache this library did not build, or built for another codec,
+ * is refused by every later call (KVQ_E_CACHE) [arc PR #98, "Refuse what we can't serve"]. */
 kvq_status kvq_cache_init(const kvq_codec* codec, kvq_cache* cache, void* packed_dev,
                           int64_t packed_cap, void* tail_dev, int64_t tail_cap, int32_t window,
                           int32_t margin);
@@ -244,8 +254,18 @@ kvq_status kvq_append_evict_chunk(const kvq_codec* codec, kvq_cache* const* cach
                                   int32_t n_caches, const void* const* new_rows_dev,
                                   int64_t t_new, void* stream, int64_t* evicted_host);
 
-/* Message for the last error on this thread ("" if none). */
+/* Message for the last error on this thread ("" if none): the failing call's argument and
+ * value, e.g. "ld_x=100 is not a multiple of 8 elements". Errors are typed statuses with a
+ * named cause, never a silent fallback [kakeyaturbo PR #15, "M2" commit: validation at the
+ * boundary with typed errors; arc PR #98, "Query strides": validate, name and refuse]. The
+ * pointer stays valid until the next call on the same thread. */
 const char* kvq_last_error(void);
+
+/* Streaming copy of `bytes` (a multiple of 16; both pointers 16-byte aligned) from src_dev to
+ * dst_dev on `stream`: the plain copy kernel a measurement times next to the codec kernels, so
+ * that its bandwidth figures can be checked against what a trivial kernel reaches on the same
+ * device in the same run. Not part of the codec. */
+kvq_status kvq_stream_copy(void* dst_dev, const void* src_dev, int64_t bytes, void* stream);
 
 /* ABI version of this header; record format version. */
 #define KVQ_ABI_VERSION 1

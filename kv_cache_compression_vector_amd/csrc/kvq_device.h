@@ -167,4 +167,51 @@ __host__ __device__ constexpr uint64_t low_mask(int bits) {
   return bits >= 64 ? ~0ull : ((1ull << bits) - 1ull);
 }
 
+// ---- Norms over the whole bf16 range ----------------------------------------------------------
+// An f32 sum of squares overflows once a row's largest magnitude passes about 2^60 and loses its
+// relative precision (then flushes to zero) below about 2^-60, while bf16 rows reach 2^+-127. The
+// kernels form the plain sum first; in the rare wave where some vector's sum lies outside
+// [2^-100, 2^100) every lane forms its vector's sum again over values multiplied by 2^-e, e the
+// exponent of the vector's largest magnitude (a power of two: exact), and that vector's norm is
+// sqrt(sum) 2^e. The branch is wave-uniform, so the cross-lane reductions inside it see every lane.
+
+__device__ __forceinline__ bool ss_out_of_range(float ss) { return !(ss >= 0x1p-100f && ss < 0x1p100f); }
+
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
+
+// 2^e as an f32, e in [-126, 127].
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// Exponent e of the largest magnitude, from its f32 bit pattern (sign cleared), clamped to
+// [-126, 126] so that both 2^e and 2^-e are normal f32 values; 0 for a zero vector.
+__device__ __forceinline__ int max_exp_of_bits(uint32_t mag_bits) {
+  const int E = (int)(mag_bits >> 23);
+  const int e = E == 0 ? -126 : E - 127;
+  return e > 126 ? 126 : e;
+}
+
+// Largest bf16 magnitude of the 8 coordinates in a 16-byte chunk, as f32 bits.
+__device__ __forceinline__ uint32_t chunk_max_mag_bits(const uint4& c) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    m = m > (w[k] & 0x7FFFu) ? m : (w[k] & 0x7FFFu);
+    m = m > ((w[k] >> 16) & 0x7FFFu) ? m : ((w[k] >> 16) & 0x7FFFu);
+  }
+  return m << 16;
+}
+
+// Sum of squares of the 8 bf16 coordinates of a chunk, each multiplied by sc first.
+__device__ __forceinline__ float chunk_scaled_ss(const uint4& c, float sc, float acc) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = bf16lo_to_f32(w[k]) * sc, b = bf16hi_to_f32(w[k]) * sc;
+    acc = fmaf(a, a, acc);
+    acc = fmaf(b, b, acc);
+  }
+  return acc;
+}
+
 }  // namespace kvq

@@ -42,7 +42,7 @@ __device__ __forceinline__ float chosen_centroid(float u, const Quant<BITS, SYM>
 // A rule whose denominator is not positive keeps the norm.
 __device__ __forceinline__ float rule_scale(int rule, float n, float zu, float zz, int m) {
   if (rule == 1 && zz > 0.0f) return n * sqrtf((float)m / zz);
-  if (rule == 2 && zu > 0.0f) return n * n * (float)m / zu;
+  if (rule == 2 && zu > 0.0f) return n * (n * (float)m / zu);
   if (rule == 3 && zz > 0.0f) return zu / zz;
   return n;
 }
@@ -68,7 +68,7 @@ void k_encode(EncodeArgs a) {
     stage_rows_linear<M>(a.x, a.ld, vec0, a.n, tile);  // rows past the end repeat the last row
     float v[L::K];
     const float ss = load_part<L::K>(tile + lane * St::S, part_signs<M>(a.tab, s_sign, q), v);
-    const float n = sqrtf(part_sum<L::Q>(ss));
+    const float n = safe_norm_lv<L::K, L::Q>(part_sum<L::Q>(ss), tile + lane * St::S);
     fwht_regs<L::K, 8>(v);
     fwht_cross<L::Q, L::K>(v, q);
     float stored = n;
@@ -113,7 +113,7 @@ __device__ __forceinline__ float rotate_owned(const EncodeArgs& a, const uint32_
   const int64_t vec0 = it * L::VPW;
   stage_rows_linear<M>(a.x, a.ld, vec0, a.n, tile);  // rows past the end repeat the last row
   const float ss = load_part<L::K>(tile + lane * St::S, part_signs<M>(a.tab, s_sign, q), v);
-  const float n = sqrtf(part_sum<L::Q>(ss));
+  const float n = safe_norm_lv<L::K, L::Q>(part_sum<L::Q>(ss), tile + lane * St::S);
   fwht_regs<L::K, 8>(v);
   fwht_cross<L::Q, L::K>(v, q);
   return n;
@@ -363,7 +363,7 @@ void k_evict(EvictArgs a) {
     }, tile);
     float v[L::K];
     const float ss = load_part<L::K>(tile + lane * St::S, part_signs<M>(a.tab, s_sign, q), v);
-    const float n = sqrtf(part_sum<L::Q>(ss));
+    const float n = safe_norm_lv<L::K, L::Q>(part_sum<L::Q>(ss), tile + lane * St::S);
     fwht_regs<L::K, 8>(v);
     fwht_cross<L::Q, L::K>(v, q);
     quantize_store_lv<M, BITS, SYM>(v, n, n, true, q, a.tab,

@@ -123,7 +123,28 @@ void k_encode_mx(EncodeArgs a, int64_t tiles_per_block) {
       }
       ss += __shfl_xor(ss, 16, 64);
       ss += __shfl_xor(ss, 32, 64);
-      const float nr = sqrtf(ss);
+      float nr = sqrtf(ss);
+      const bool bad = ss_out_of_range(ss);
+      if (wave_any(bad)) {  // rescaled sum of squares (kvq_device.h), wave-uniform
+        uint32_t mb = 0;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint32_t m = chunk_max_mag_bits(A[rt][ks]);
+          mb = mb > m ? mb : m;
+        }
+        uint32_t o = (uint32_t)__shfl_xor((int)mb, 16, 64);
+        mb = mb > o ? mb : o;
+        o = (uint32_t)__shfl_xor((int)mb, 32, 64);
+        mb = mb > o ? mb : o;
+        const int ex = max_exp_of_bits(mb);
+        const float sc = pow2f(-ex);
+        float s2 = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s2 = chunk_scaled_ss(A[rt][ks], sc, s2);
+        s2 += __shfl_xor(s2, 16, 64);
+        s2 += __shfl_xor(s2, 32, 64);
+        nr = bad ? sqrtf(s2) * pow2f(ex) : nr;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) nC[rt][i] = __shfl(nr, 4 * grp + i, 64);
     }

@@ -227,6 +227,14 @@ int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
 
 const char* kvq_last_error(void) { return g_last_error.c_str(); }
 
+kvq_status kvq_stream_copy(void* dst_dev, const void* src_dev, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(KVQ_E_ARG, "bytes=%lld must be a non-negative multiple of 16", (long long)bytes);
+  if (bytes == 0) return ok();
+  if (!dst_dev || !src_dev) return fail(KVQ_E_NULL, "dst_dev or src_dev is NULL");
+  if (!aligned(dst_dev, 16) || !aligned(src_dev, 16)) return fail(KVQ_E_STRIDE, "copy pointers must be 16-byte aligned");
+  return from_hip(kvq::launch_stream_copy(dst_dev, src_dev, bytes, static_cast<hipStream_t>(stream)), "stream_copy");
+}
+
 size_t kvq_record_bytes(const kvq_codec* codec) {
   Resolved r;
   if (resolve_codec(codec, r) != KVQ_OK) return 0;

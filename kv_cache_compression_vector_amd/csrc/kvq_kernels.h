@@ -134,5 +134,6 @@ hipError_t launch_attend(int D, int mk, bool proj, int bk, int bv, const AttendA
 hipError_t launch_evict(int m, int bits, bool sym, const EvictArgs& a, hipStream_t st);
 hipError_t launch_tail_copy(const TailCopyArgs& a, hipStream_t st);
 hipError_t launch_clear_u32(uint32_t* p, int64_t n_words, hipStream_t st);
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t st);
 
 }  // namespace kvq

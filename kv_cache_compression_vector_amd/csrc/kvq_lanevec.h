@@ -243,6 +243,70 @@ __device__ __forceinline__ float part_sum(float x) {
   return x;
 }
 
+template <int Q>
+__device__ __forceinline__ uint32_t part_max_u32(uint32_t x) {
+  if constexpr (Q >= 2) {
+    const uint32_t y = __float_as_uint(quad_xor<1>(__uint_as_float(x)));
+    x = x > y ? x : y;
+  }
+  if constexpr (Q >= 4) {
+    const uint32_t y = __float_as_uint(quad_xor<2>(__uint_as_float(x)));
+    x = x > y ? x : y;
+  }
+  return x;
+}
+
+// Norm of a vector whose lane part's raw bf16 chunks sit at `row` (K/8 chunks, LDS), given the
+// plain f32 sum of squares already summed over the vector's Q lanes; rescaled (see
+// ss_out_of_range) where that sum left the f32 range. Call from wave-uniform control flow.
+template <int K, int Q>
+__device__ __forceinline__ float safe_norm_lv(float ss, const uint4* row) {
+  const bool bad = ss_out_of_range(ss);
+  float n = sqrtf(ss);
+  if (wave_any(bad)) {
+    uint32_t mb = 0;
+#pragma unroll
+    for (int c = 0; c < K / 8; ++c) {
+      const uint32_t m = chunk_max_mag_bits(row[c]);
+      mb = mb > m ? mb : m;
+    }
+    const int e = max_exp_of_bits(part_max_u32<Q>(mb));
+    const float sc = pow2f(-e);
+    float s2 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < K / 8; ++c) s2 = chunk_scaled_ss(row[c], sc, s2);
+    const float n2 = sqrtf(part_sum<Q>(s2)) * pow2f(e);
+    n = bad ? n2 : n;
+  }
+  return n;
+}
+
+// The same for a vector held as f32 coordinates (K per lane, Q lanes; projection outputs).
+template <int K, int Q>
+__device__ __forceinline__ float safe_norm_f32(float ss, const float (&v)[K]) {
+  const bool bad = ss_out_of_range(ss);
+  float n = sqrtf(ss);
+  if (wave_any(bad)) {
+    uint32_t mb = 0;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const uint32_t m = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+      mb = mb > m ? mb : m;
+    }
+    const int e = max_exp_of_bits(part_max_u32<Q>(mb));
+    const float sc = pow2f(-e);
+    float s2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const float a = v[i] * sc;
+      s2 = fmaf(a, a, s2);
+    }
+    const float n2 = sqrtf(part_sum<Q>(s2)) * pow2f(e);
+    n = bad ? n2 : n;
+  }
+  return n;
+}
+
 __device__ __forceinline__ uint32_t shift_in(uint32_t w, bool bit) { return w + w + (bit ? 1u : 0u); }
 
 // (acc << 1) | sign bit of x: one v_alignbit_b32.

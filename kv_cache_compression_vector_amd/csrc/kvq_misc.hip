@@ -1,4 +1,5 @@
-// kvq_misc.hip — small helper kernels: tail-ring append and word clearing.
+// kvq_misc.hip — small helper kernels: tail-ring append, word clearing, and a streaming copy
+// (the bandwidth control a measurement runs next to the codec kernels).
 #include "kvq_device.h"
 #include "kvq_kernels.h"
 
@@ -24,6 +25,35 @@ __global__ __launch_bounds__(256) void k_tail_copy(TailCopyArgs a) {
 __global__ __launch_bounds__(256) void k_clear_u32(uint32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     p[i] = 0u;
+}
+
+// Streaming copy of n16 16-byte words: each thread moves 4 words per pass, all four loads
+// issued before the stores, grid-stride over the array.
+__global__ __launch_bounds__(256) void k_stream_copy(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                                     int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < n16; i += stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i + 256 * k < n16) v[k] = ld_stream(src + i + 256 * k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i + 256 * k < n16) st_stream(dst + i + 256 * k, v[k]);
+  }
+}
+
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  if (n16 <= 0) return hipSuccess;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int64_t blocks = (n16 + 1023) / 1024;
+  if (blocks > (int64_t)cus * 8) blocks = (int64_t)cus * 8;
+  hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), n16);
+  return hipGetLastError();
 }
 
 hipError_t launch_tail_copy(const TailCopyArgs& a, hipStream_t st) {

@@ -163,7 +163,7 @@ void k_encode_pca(EncodeArgs a, int64_t tiles_per_block) {
       for (int e = 0; e < 4; ++e) ss = fmaf(v[4 * c + e], v[4 * c + e], ss);
     }
     __builtin_amdgcn_wave_barrier();
-    const float n = sqrtf(ss);
+    const float n = safe_norm_f32<R, 1>(ss, v);
     fwht_regs<R>(v);
     quantize_store_lv<R, BITS, SYM>(v, n, n, vec < a.n, 0, a.tab,
                                     reinterpret_cast<uint32_t*>(a.rec) + vec * NWT);
@@ -316,7 +316,7 @@ void k_encode_pq(EncodeArgs a, int64_t tiles_per_block) {
     __builtin_amdgcn_wave_barrier();
     phase_fence();
     ss += quad_xor<1>(ss);
-    const float n = sqrtf(ss);
+    const float n = safe_norm_f32<32, 2>(ss, v);
     fwht_regs<32>(v);          // index bits 0, 1, 3, 4, 5 (local bits 0 .. 4)
     fwht_cross<2, 32>(v, q);   // index bit 2, across the pair
     // quantise word group q: bit t of each plane word is local coordinate 4 (t mod 8) + t / 8

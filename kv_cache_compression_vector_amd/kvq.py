@@ -87,10 +87,12 @@ def lib() -> ctypes.CDLL:
         L.kvq_attend_packed.argtypes = [PC, PC, P, I32, I32, I64, I64, P, P, I32, I64, I64, I64,
                                         ctypes.c_float, ctypes.c_float, P, I64, I64, P,
                                         ctypes.c_size_t, P]
+        L.kvq_stream_copy.argtypes = [P, P, I64, P]
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_abi_version.restype = ctypes.c_int32
         for name in ("kvq_codec_tables", "kvq_encode", "kvq_decode", "kvq_score_packed",
-                     "kvq_attend_packed", "kvq_cache_init", "kvq_append_evict_chunk"):
+                     "kvq_attend_packed", "kvq_cache_init", "kvq_append_evict_chunk",
+                     "kvq_stream_copy"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -291,3 +293,10 @@ def append_evict_chunk(codec: Codec, caches: list[Cache], new_rows: list[torch.T
     dev = caches[0].tail if n else None
     _check(lib().kvq_append_evict_chunk(codec.ref, arr, n, rows, t_new, _stream(dev), ev))
     return list(ev)
+
+
+def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """The library's streaming copy kernel (a bandwidth control): dst <- src, same byte size."""
+    nb = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() == nb and src.is_contiguous() and dst.is_contiguous()
+    _check(lib().kvq_stream_copy(_ptr(dst), _ptr(src), nb, _stream(src)))

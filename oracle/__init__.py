@@ -176,8 +176,9 @@ class Codec:
 
 def encode(cd: Codec, x_bf16: np.ndarray, ol_cap: int | None = None) -> dict:
     """Encode rows of x (uint16 bf16 bits, shape [n, D]). Returns a dict with records
-    ([n, rec_bytes] u8), codes and flags ([n, m] u8), z ([n, m] f64), norms ([n] f64) and, when
-    T > 0, the outlier CSR (offsets [n+1] u32, idx u8, val u16 bf16 bits, total)."""
+    ([n, rec_bytes] u8), codes and flags ([n, m] u8), z ([n, m] f64), norms ([n] f64), the f32
+    decision thresholds and, when T > 0, the outlier CSR (offsets [n+1] u32, idx u8, val u16
+    bf16 bits, total)."""
     x = np.ascontiguousarray(x_bf16, np.uint16).reshape(-1, cd.D)
     n = x.shape[0]
     rec = np.zeros((n, cd.rec_bytes), np.uint8)
@@ -185,7 +186,8 @@ def encode(cd: Codec, x_bf16: np.ndarray, ol_cap: int | None = None) -> dict:
     flags = np.zeros((n, cd.m), np.uint8)
     z = np.zeros((n, cd.m), np.float64)
     norms = np.zeros(n, np.float64)
-    out = dict(records=rec, codes=codes, flags=flags, z=z, norms=norms)
+    out = dict(records=rec, codes=codes, flags=flags, z=z, norms=norms,
+               thresholds=thresholds(cd.centroids))
     c = cd._c()
     if cd.T > 0:
         cap = n * cd.m if ol_cap is None else ol_cap

@@ -10,7 +10,8 @@ import torch
 
 import oracle
 from kv_cache_compression_vector_amd import kvq, synth
-from tests.gpu_helpers import (bf16_host, compare_codes, compare_decoded, oracle_codec_like, say,
+from tests.gpu_helpers import (bf16_host, check_scores, compare_codes, compare_decoded,
+                               compare_outlier_lists, oracle_codec_like, say, score_scale,
                                unpack_records)
 
 pytestmark = pytest.mark.gpu
@@ -101,15 +102,11 @@ def test_heavy_tailed_v_with_outliers_full_size():
     mism, flagged = compare_codes(got, ref, D, bits, "heavy-tailed codes")
     idx = ol.idx[:total].cpu().numpy()
     val = ol.val[:total].cpu().numpy().view(np.uint16)
-    near_t = ((ref["flags"] & oracle.FLAG_NEAR_T) != 0).any(1)
-    roff = ref["offsets"].astype(np.int64)
+    differing = compare_outlier_lists(off, idx, val, ref, rows, "heavy-tailed outliers")
+    say(f"  {len(rows)} sampled vectors' lists: {differing} differ, each only at near-T coordinates")
     sub_off, sub_idx, sub_val = [0], [np.zeros(0, np.uint8)], [np.zeros(0, np.uint16)]
     for k, v in enumerate(rows):
         gi, gv = idx[off[v]:off[v + 1]], val[off[v]:off[v + 1]]
-        if not near_t[k]:
-            np.testing.assert_array_equal(gi, ref["idx"][roff[k]:roff[k + 1]])
-            dv = gv.astype(np.int32) - ref["val"][roff[k]:roff[k + 1]].astype(np.int32)
-            assert np.all(np.abs(dv) <= 1), f"row {v}: outlier values beyond 1 bf16 ulp"
         sub_idx.append(gi)
         sub_val.append(gv)
         sub_off.append(sub_off[-1] + len(gi))
@@ -155,11 +152,8 @@ def test_long_context_score_full_size():
     sref = oracle.score(oc, qh, recs)
     sg = s[torch.from_numpy(bs).to(DEV), torch.from_numpy(hs).to(DEV),
            torch.from_numpy(ts).to(DEV)].cpu().numpy().astype(np.float64)
-    yref = oracle.decode(oc, recs)
-    bound = 1e-3 * np.maximum(np.abs(sref), np.linalg.norm(_f64(qh), axis=1) * np.linalg.norm(yref, axis=1))
-    err = np.abs(sg - sref)
-    say(f"  {len(bs)} sampled scores, worst err/bound {float(np.max(err / bound)):.3f}")
-    assert np.all(err <= bound)
+    worst = check_scores(sg, sref, score_scale(oc, qh, recs), "long-context scores")
+    say(f"  {len(bs)} sampled scores, worst err/bound {worst:.3f}")
 
 
 def test_qwen2_shaped_cache_full_size():
@@ -233,8 +227,5 @@ def test_qwen2_shaped_cache_full_size():
         sel = kb == k
         ock = oracle_codec_like(ck, basis_host=bhost[k], mean_host=mhost[k])
         sref = oracle.score(ock, qh[sel], recs[sel])
-        yr = oracle.decode(ock, recs[sel])
-        bound = 1e-3 * np.maximum(np.abs(sref), np.linalg.norm(_f64(qh[sel]), axis=1) *
-                                  np.linalg.norm(yr, axis=1))
-        assert np.all(np.abs(sg[sel] - sref) <= bound), f"scores, basis {k}"
+        check_scores(sg[sel], sref, score_scale(ock, qh[sel], recs[sel]), f"scores, basis {k}")
     say(f"  {len(rows)} sampled rows per stream and {len(bb)} sampled scores agree")

@@ -10,7 +10,8 @@ import torch
 
 import oracle
 from kv_cache_compression_vector_amd import kvq, synth
-from tests.gpu_helpers import (bf16_host, compare_codes, compare_decoded, oracle_codec_like, say,
+from tests.gpu_helpers import (bf16_host, check_scores, compare_codes, compare_decoded,
+                               compare_outlier_lists, oracle_codec_like, say, score_scale,
                                unpack_records)
 
 pytestmark = pytest.mark.gpu
@@ -211,13 +212,8 @@ def test_outlier_parity(D, bits, T_):
     assert total == off[-1] and abs(int(off[-1]) - ref["total"]) <= near_t.sum()
     rate = ref["total"] / (n * D)
     say(f"  outliers {total} (oracle {ref['total']}), rate {rate:.4f}")
-    for v in np.nonzero(per_vec_ok)[0][:400]:
-        gi = idx[off[v]:off[v + 1]]
-        ri = ref["idx"][roff[v]:roff[v + 1]]
-        np.testing.assert_array_equal(gi, ri)
-        gv = val[off[v]:off[v + 1]].astype(np.int32)
-        rv = ref["val"][roff[v]:roff[v + 1]].astype(np.int32)
-        assert np.all(np.abs(gv - rv) <= 1), "outlier values beyond 1 bf16 ulp"
+    differing = compare_outlier_lists(off, idx, val, ref, None, "outlier lists")
+    say(f"  lists of all {n} vectors compared: {differing} differ, only at near-T coordinates")
     # decode with the side list: GPU vs oracle on the GPU's own records and list
     y = kvq.decode(codec, rec, outliers=ol)
     yref = oracle.decode(oracle_codec_like(codec), recn, off, idx[:total], val[:total])

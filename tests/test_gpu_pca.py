@@ -6,7 +6,8 @@ import torch
 
 import oracle
 from kv_cache_compression_vector_amd import kvq, synth
-from tests.gpu_helpers import (bf16_host, compare_codes, compare_decoded, say, unpack_records)
+from tests.gpu_helpers import (bf16_host, check_scores, compare_codes, compare_decoded, say,
+                               score_scale, unpack_records)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -90,12 +91,10 @@ def test_pca_many_bases_and_score():
             for bb in range(B):
                 for g in range(G):
                     hq = h * G + g
-                    sref = oracle.score(oc, np.repeat(qh[l, bb, hq][None], T, 0), rh[l, bb, h])
-                    err = np.abs(sn[l * B + bb, hq] - sref)
-                    # normwise bound through Cauchy-Schwarz on the decoded keys
-                    qn = np.linalg.norm((qh[l, bb, hq].astype(np.uint32) << 16).view(np.float32))
-                    bound = 1e-3 * np.maximum(np.abs(sref), qn * np.linalg.norm(yref.reshape(B, T, D)[bb], axis=1))
-                    assert np.all(err <= bound), f"score l={l} h={h} b={bb} g={g}: {err.max():.3g}"
+                    qq = np.repeat(qh[l, bb, hq][None], T, 0)
+                    sref = oracle.score(oc, qq, rh[l, bb, h])
+                    check_scores(sn[l * B + bb, hq], sref, score_scale(oc, qq, rh[l, bb, h]),
+                                 f"score l={l} h={h} b={bb} g={g}")
 
 
 def test_pca_score_bases_change_inside_a_block_run():
@@ -122,15 +121,12 @@ def test_pca_score_bases_change_inside_a_block_run():
             k = int(index_h[row0 // 256])
             oc = _oracle_codec(D, r, bits, 42, mu[k], b[k])
             recs = recn[row0: row0 + 256]
-            ynorm = np.linalg.norm(oracle.decode(oc, recs), axis=1)
             for g in range(G):
                 hq = h * G + g
-                sref = oracle.score(oc, np.repeat(qh[bb, hq][None], 256, 0), recs)
+                qq = np.repeat(qh[bb, hq][None], 256, 0)
+                sref = oracle.score(oc, qq, recs)
                 got = sn[bb, hq, 256 * blk: 256 * (blk + 1)]
-                qn = np.linalg.norm((qh[bb, hq].astype(np.uint32) << 16).view(np.float32))
-                bound = 1e-3 * np.maximum(np.abs(sref), qn * ynorm)
-                err = np.abs(got - sref)
-                assert np.all(err <= bound), f"b={bb} h={h} block {blk} g={g}: {err.max():.3g}"
+                check_scores(got, sref, score_scale(oc, qq, recs), f"b={bb} h={h} block {blk} g={g}")
 
 
 def test_pca_refusals():

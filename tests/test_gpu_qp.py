@@ -8,7 +8,8 @@ import torch
 
 import oracle
 from kv_cache_compression_vector_amd import kvq, synth
-from tests.gpu_helpers import bf16_host, compare_codes, compare_decoded, oracle_codec_like, say
+from tests.gpu_helpers import (bf16_host, check_scores, compare_codes, compare_decoded,
+                               oracle_codec_like, say, score_scale)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -65,11 +66,9 @@ def test_qp_encode_decode_score(D, r, bits):
     torch.cuda.synchronize()
     qh = bf16_host(q).reshape(3, D)
     for h in range(3):
-        sref = oracle.score(oc, np.repeat(qh[h][None], n, 0), recn)
-        qn = np.linalg.norm((qh[h].astype(np.uint32) << 16).view(np.float32))
-        bound = 1e-3 * np.maximum(np.abs(sref), qn * nrm)
-        err = np.abs(s[0, h].cpu().numpy() - sref)
-        assert np.all(err <= bound), f"score head {h}: {err.max():.3g}"
+        qq = np.repeat(qh[h][None], n, 0)
+        sref = oracle.score(oc, qq, recn)
+        check_scores(s[0, h].cpu().numpy(), sref, score_scale(oc, qq, recn), f"score head {h}")
 
 
 def test_qp_several_bases_and_attention():
