@@ -29,7 +29,8 @@
  *
  * Conventions for every call below.
  *  - Pointers named *_dev are device memory (HIP), *_host host memory. The caller owns all of
- *    them; the library allocates nothing and keeps no device state.
+ *    them; the library allocates nothing and keeps no device state, except the static scratch
+ *    array of kvq_attend_packed_static (one per device).
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously;
  *    argument errors are detected on the host before anything is enqueued and nothing is then
  *    launched. A launch failure maps to KVQ_E_DEVICE.
@@ -231,6 +232,25 @@ kvq_status kvq_attend_packed(const kvq_codec* kcodec, const kvq_codec* vcodec, c
                              int64_t rec_sb, int64_t rec_sh, float softmax_scale, float softcap,
                              float* out_dev, int64_t o_sb, int64_t o_sh, void* workspace_dev,
                              size_t workspace_bytes, void* stream);
+
+/* kvq_attend_packed without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The per-block partials go to a static device array of KVQ_STATIC_SCRATCH_BYTES (16 MiB), one
+ * per device, held from the first call on that device until the process ends; the call itself
+ * allocates nothing and frees nothing. A call whose partials need more
+ * (kvq_attend_workspace_bytes(vcodec, B, Hkv, T) > KVQ_STATIC_SCRATCH_BYTES, e.g. B*Hkv > 992 at
+ * head_dim 128) returns KVQ_E_CAPACITY before anything is launched. Every other argument, the
+ * result and the errors are those of kvq_attend_packed. All calls on one device share that
+ * device's array, and the array keeps the last call's contents (every partial a call reads is
+ * written by the same call first): calls that overlap on one device, on different streams or
+ * from different threads, race and give undefined results. */
+#define KVQ_STATIC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_attend_packed_static(const kvq_codec* kcodec, const kvq_codec* vcodec,
+                                    const void* q_dev, int32_t B, int32_t Hq, int64_t q_sb,
+                                    int64_t q_sh, const void* krec_dev, const void* vrec_dev,
+                                    int32_t Hkv, int64_t T, int64_t rec_sb, int64_t rec_sh,
+                                    float softmax_scale, float softcap, float* out_dev,
+                                    int64_t o_sb, int64_t o_sh, void* stream);
 
 /* Build an empty cache over caller-owned buffers: packed_dev holds packed_cap records,
  * tail_dev holds tail_cap bf16 rows of head_dim. window >= 0, margin >= 0. Host only.

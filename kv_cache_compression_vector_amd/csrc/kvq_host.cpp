@@ -219,6 +219,40 @@ constexpr uint64_t kCacheMagic = 0x4b56514341434845ull;  // "KVQCACHE"
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Device address of the static scratch array on the current device (see below), looked up once
+// per device with that device current.
+kvq_status static_scratch_address(void** out);
+
+}  // namespace
+
+// ---- Static scratch of the allocation-free attention entry point ----------------------------
+// One array per device, held until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: every use goes through the address hipGetSymbolAddress returns
+// for the current device.
+static __device__ __align__(256) unsigned char scratch[KVQ_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};
+
+kvq_status static_scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(KVQ_E_DEVICE, "device %d outside 0..63", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(KVQ_E_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -481,6 +515,30 @@ kvq_status kvq_attend_packed(const kvq_codec* kcodec, const kvq_codec* vcodec, c
   a.softcap = softcap;
   return from_hip(kvq::launch_attend(rk.D, rk.m, rk.pca, rk.bits, rv.bits, a, static_cast<hipStream_t>(stream)),
                   "attend_packed");
+}
+
+kvq_status kvq_attend_packed_static(const kvq_codec* kcodec, const kvq_codec* vcodec,
+                                    const void* q_dev, int32_t B, int32_t Hq, int64_t q_sb,
+                                    int64_t q_sh, const void* krec_dev, const void* vrec_dev,
+                                    int32_t Hkv, int64_t T, int64_t rec_sb, int64_t rec_sh,
+                                    float softmax_scale, float softcap, float* out_dev,
+                                    int64_t o_sb, int64_t o_sh, void* stream) {
+  Resolved rv;
+  kvq_status st = resolve_codec(vcodec, rv);
+  if (st != KVQ_OK) return st;
+  if (B > 0 && Hkv > 0 && T > 0) {
+    const size_t need = kvq_attend_workspace_bytes(vcodec, B, Hkv, T);
+    if (need > (size_t)KVQ_STATIC_SCRATCH_BYTES)
+      return fail(KVQ_E_CAPACITY, "B=%d Hkv=%d T=%lld needs %zu bytes of partials; the static scratch "
+                  "holds %zu (use kvq_attend_packed with a caller workspace)", B, Hkv, (long long)T,
+                  need, (size_t)KVQ_STATIC_SCRATCH_BYTES);
+  }
+  void* ws = nullptr;
+  st = static_scratch_address(&ws);
+  if (st != KVQ_OK) return st;
+  return kvq_attend_packed(kcodec, vcodec, q_dev, B, Hq, q_sb, q_sh, krec_dev, vrec_dev, Hkv, T,
+                           rec_sb, rec_sh, softmax_scale, softcap, out_dev, o_sb, o_sh, ws,
+                           (size_t)KVQ_STATIC_SCRATCH_BYTES, stream);
 }
 
 kvq_status kvq_cache_init(const kvq_codec* codec, kvq_cache* cache, void* packed_dev,

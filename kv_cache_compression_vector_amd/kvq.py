@@ -87,12 +87,14 @@ def lib() -> ctypes.CDLL:
         L.kvq_attend_packed.argtypes = [PC, PC, P, I32, I32, I64, I64, P, P, I32, I64, I64, I64,
                                         ctypes.c_float, ctypes.c_float, P, I64, I64, P,
                                         ctypes.c_size_t, P]
+        L.kvq_attend_packed_static.argtypes = [PC, PC, P, I32, I32, I64, I64, P, P, I32, I64, I64,
+                                               I64, ctypes.c_float, ctypes.c_float, P, I64, I64, P]
         L.kvq_stream_copy.argtypes = [P, P, I64, P]
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_abi_version.restype = ctypes.c_int32
         for name in ("kvq_codec_tables", "kvq_encode", "kvq_decode", "kvq_score_packed",
                      "kvq_attend_packed", "kvq_cache_init", "kvq_append_evict_chunk",
-                     "kvq_stream_copy"):
+                     "kvq_stream_copy", "kvq_attend_packed_static"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -244,6 +246,25 @@ def attend_packed(kcodec: Codec, vcodec: Codec, q: torch.Tensor, krecords: torch
                                    q.stride(1), _ptr(krecords), _ptr(vrecords), Hkv, T, rec_sb,
                                    rec_sh, softmax_scale, softcap, _ptr(out), out.stride(0),
                                    out.stride(1), _ptr(workspace), workspace.numel(), _stream(q)))
+    return out
+
+
+STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def attend_packed_static(kcodec: Codec, vcodec: Codec, q: torch.Tensor, krecords: torch.Tensor,
+                         vrecords: torch.Tensor, Hkv: int, T: int, rec_sb: int, rec_sh: int,
+                         softmax_scale: float, softcap: float = 0.0,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """attend_packed through the allocation-free entry point (partials in the library's static
+    device scratch). Pass `out` to allocate nothing here either."""
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    _check(lib().kvq_attend_packed_static(kcodec.ref, vcodec.ref, _ptr(q), B, Hq, q.stride(0),
+                                          q.stride(1), _ptr(krecords), _ptr(vrecords), Hkv, T,
+                                          rec_sb, rec_sh, softmax_scale, softcap, _ptr(out),
+                                          out.stride(0), out.stride(1), _stream(q)))
     return out
 
 
