@@ -1,20 +1,19 @@
 // kvq_encode_mx.hip — Hadamard-path encode with the rotation on the matrix cores (m <= 128).
 //
 // u = H_m (s (.) x) [kakeyaturbo PR #15, "M4 Phase A": rotate = H.D.x; "M4 Phase B": the rotation
-// as a dense product on the tensor cores] is formed as U = X Bm with Bm = diag(s) H_m (entries
-// +-1, exact in bf16; x is bf16, so every product is exact and sums in f32). The in-register
+// as a dense product on the tensor cores] is formed on v_mfma_f32_16x16x32_bf16 from +-1 operands
+// (exact in bf16; x is bf16, so every product is exact and sums in f32). The in-register
 // butterfly would cost log2(m) adds per coordinate on the vector ALUs, which bind first on this
 // chip; the product costs them nothing.
 //
-// Output columns are permuted: lane column c of n-tile nt receives coordinate
-// j = pi^-1(NT c + nt), pi the record's plane position, so each lane holds NT consecutive plane
-// positions of each of its rows. The quantiser (kvq_lanevec.h) then builds NT-bit fields per
-// plane in registers, and LPW = 32/NT lanes OR their fields into a record word over DPP.
+// m = 128 (k_encode_t128): the transposed product U^T = Bm^T X^T, arranged so that each lane ends
+// with one whole record word group of one vector (no cross-lane packing), and the rotation held
+// as 16 register fragments (see below). m = 64 (k_encode_mx): U = X Bm with the output columns
+// permuted so each lane holds NT consecutive plane positions of each of its rows; the quantiser
+// builds NT-bit fields per plane and LPW = 32/NT lanes OR them into a record word over DPP.
 //
-// Per wave: 16-row tiles staged through a swizzled LDS region with 1 KB-contiguous loads, the
-// next tile's loads in flight while the current one computes. A block of 8 waves shares the
-// staged rotation, so two blocks (16 waves) fit a CU: enough bytes in flight to stream HBM.
-// Norms come from bf16 dot products of the staged rows.
+// Rows arrive through swizzled LDS with 1 KB-contiguous loads, the next tile's loads in flight
+// while the current one computes. Norms come from bf16 dot products of the staged rows.
 #include "kvq_device.h"
 #include "kvq_kernels.h"
 #include "kvq_lanevec.h"
@@ -209,6 +208,220 @@ void k_encode_mx(EncodeArgs a, int64_t tiles_per_block) {
   }
 }
 
+// ---- m = 128: the transposed product --------------------------------------------------------
+// U^T = Bm^T X^T with A = Bm^T (16 output coordinates x 32 inputs) and B = X^T (32 inputs x 16
+// vectors): the accumulator of lane l = 16 grp + c holds vector c, rows m = 4 grp + i of the
+// m-tile. Row m of m-tile mt is assigned plane position P = 32 grp + 4 mt + i, so lane (grp, c)
+// ends with exactly the 32 plane positions of record word group grp of vector c: its b plane
+// words need no other lane, and its norm is the one its own group already summed.
+//
+// Structure of the operand. With j = coord_at(P) = 32 (mt % 4) + 8 i + 2 grp + (mt >> 2) and an
+// input index k = 32 ks + kappa (kappa < 32), popcount(k & j) splits into popcount(ks & (mt % 4))
+// and popcount(kappa & (8 i + 2 grp + (mt >> 2))): the fragment (mt, ks) of Bm^T is
+// (-1)^popcount(ks & (mt % 4)) F(mt >> 2, ks), with F holding s_k and the second factor. The whole
+// 128 x 128 rotation is the 8 fragments F and their negations, kept in registers.
+
+// F(h, ks) for lane l: row m = l % 16, inputs k = 32 ks + kappa, kappa = 8 (l / 16) + e.
+__device__ __forceinline__ uint4 t128_fragment(const Tables& tab, int h, int ks, int l) {
+  const int m = l & 15, jl = 8 * (m & 3) + 2 * (m >> 2) + h;
+  uint32_t w[4];
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int kappa = 8 * (l >> 4) + 2 * hh + q, k = 32 * ks + kappa;
+      const uint32_t s = (tab.sign_pairs[k >> 1] >> (16 * (k & 1))) & 0x8000u;  // s_k = -1
+      const uint32_t par = (uint32_t)(__builtin_popcount(kappa & jl) & 1) << 15;
+      v |= (0x3F80u | (s ^ par)) << (16 * q);
+    }
+    w[hh] = v;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+constexpr int kT128Waves = 4;   // waves per block
+constexpr int kT128Rows = 16;   // vectors per wave tile
+
+// Block b takes the block tiles b, b + G, b + 2G, ... (G = the grid): at any moment the resident
+// blocks stream through one window of the rows.
+template <int BITS, bool SYM>
+__global__ __launch_bounds__(64 * kT128Waves) __attribute__((amdgpu_waves_per_eu(3)))
+void k_encode_t128(EncodeArgs a) {
+  constexpr int M = 128, KS = 4, RCH = M / 8, ROWS = kT128Rows;
+  constexpr int NWC = (M / 32) * BITS, NWT = NWC + 1, TILE = kT128Waves * ROWS;
+  __shared__ uint4 s_reg[kT128Waves * ROWS * RCH];
+  const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
+  const int c = ln & 15, grp = ln >> 4;
+  uint4 F[2][KS], FN[2][KS];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      F[h][ks] = t128_fragment(a.tab, h, ks, ln);
+      FN[h][ks] = make_uint4(F[h][ks].x ^ 0x80008000u, F[h][ks].y ^ 0x80008000u,
+                             F[h][ks].z ^ 0x80008000u, F[h][ks].w ^ 0x80008000u);
+    }
+  uint4* reg = s_reg + wave * ROWS * RCH;
+  uint32_t* rec_lds = reinterpret_cast<uint32_t*>(reg);
+  // LDS places (uint4) of the 4 staged pieces (row 4 k + grp, chunk c) and of the 4 operand
+  // chunks (row c, chunk 4 ks + grp): swizzled so 16 lanes of one row or one chunk column hit
+  // distinct banks
+  int woff[4], roff[KS];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) woff[k] = swz<RCH>(4 * k + grp, c);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = swz<RCH>(c, 4 * ks + grp);
+  const int64_t n_tiles = (a.n + TILE - 1) / TILE;
+  const int64_t G = gridDim.x;
+  const int64_t lane_off = (int64_t)grp * a.ld + 8 * c;
+  // piece k of the lane: row rw + 4 k + grp, chunk c (1 KB contiguous per instruction); rows past
+  // the end repeat the last row
+  auto load_tile = [&](int64_t tile, uint4 (&in)[4]) {
+    const int64_t rw = tile * TILE + ROWS * wave;
+    if (rw + ROWS <= a.n) {  // wave-uniform
+      const uint16_t* xp = a.x + rw * a.ld + lane_off;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) in[k] = ld_stream(xp + 4 * k * a.ld);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        int64_t row = rw + 4 * k + grp;
+        row = row < a.n ? row : a.n - 1;
+        in[k] = ld_stream(a.x + row * a.ld + 8 * c);
+      }
+    }
+  };
+  uint4 nxt[4];
+  if ((int64_t)blockIdx.x < n_tiles) load_tile(blockIdx.x, nxt);
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += G) {
+    const int64_t rw0 = tile * TILE + ROWS * wave;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) reg[woff[k]] = nxt[k];
+    if (tile + G < n_tiles) load_tile(tile + G, nxt);  // in flight while this tile computes
+    __builtin_amdgcn_wave_barrier();
+    uint4 X[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) X[ks] = reg[roff[ks]];
+    __builtin_amdgcn_wave_barrier();
+    // norm of vector c: this lane's 32 coordinates, summed over the 4 groups
+    float ss = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t w[4] = {X[ks].x, X[ks].y, X[ks].z, X[ks].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]),
+                                             __builtin_bit_cast(bf16x2_t, w[e]), ss, false);
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    float n = __builtin_amdgcn_sqrtf(ss);
+    const bool bad = ss_out_of_range(ss);
+    if (wave_any(bad)) {  // rescaled sum of squares (kvq_device.h), wave-uniform
+      uint32_t mb = 0;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t m = chunk_max_mag_bits(X[ks]);
+        mb = mb > m ? mb : m;
+      }
+      uint32_t o = (uint32_t)__shfl_xor((int)mb, 16, 64);
+      mb = mb > o ? mb : o;
+      o = (uint32_t)__shfl_xor((int)mb, 32, 64);
+      mb = mb > o ? mb : o;
+      const int ex = max_exp_of_bits(mb);
+      const float sc = pow2f(-ex);
+      float s2 = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s2 = chunk_scaled_ss(X[ks], sc, s2);
+      s2 += __shfl_xor(s2, 16, 64);
+      s2 += __shfl_xor(s2, 32, 64);
+      n = bad ? __builtin_amdgcn_sqrtf(s2) * pow2f(ex) : n;
+    }
+    // rotation and quantiser, one m-tile at a time: plane bits t = 4 mt + i, pushed from t = 31
+    const Quant<BITS, SYM> q(a.tab, n);
+    QuantAcc<BITS, SYM> qa;
+#pragma unroll
+    for (int mt = 7; mt >= 0; --mt) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bool neg = __builtin_popcount(ks & (mt & 3)) & 1;  // compile-time
+        acc = mfma_bf16(neg ? FN[mt >> 2][ks] : F[mt >> 2][ks], X[ks], acc);
+      }
+#pragma unroll
+      for (int i = 3; i >= 0; --i) qa.push(acc[i], q);
+    }
+    uint32_t pl[BITS];
+    qa.planes(q, 0xFFFFFFFFu, pl);
+    // the tile's records, staged in the (now free) region: lane (grp, c) writes words
+    // grp * b .. grp * b + b - 1 of record c; group 0 writes the norm
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) rec_lds[c * NWT + grp * BITS + p] = pl[p];
+    if (grp == 0) rec_lds[c * NWT + NWC] = __float_as_uint(n);
+    __builtin_amdgcn_wave_barrier();
+    // the wave tile's records are contiguous in memory: coalesced 16-byte stores
+    {
+      constexpr int CH = ROWS * NWT / 4;  // 16-byte pieces (ROWS * NWT is a multiple of 4)
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(a.rec) + rw0 * NWT);
+      const uint4* src = reinterpret_cast<const uint4*>(rec_lds);
+      if (rw0 + ROWS <= a.n) {  // wave-uniform
+#pragma unroll
+        for (int k = 0; k < (CH + 63) / 64; ++k) {
+          const int id = k * 64 + ln;
+          if (id < CH) st_stream(dst + id, src[id]);
+        }
+      } else if (rw0 < a.n) {
+        const int valid_w = (int)(a.n - rw0) * NWT;  // words of whole valid records
+#pragma unroll
+        for (int k = 0; k < (CH + 63) / 64; ++k) {
+          const int id = k * 64 + ln;
+          if (4 * id + 4 <= valid_w) st_stream(dst + id, src[id]);
+        }
+        const int tw = valid_w % 4, w0 = valid_w - tw;  // a partial last piece, word by word
+        if (ln < tw) reinterpret_cast<uint32_t*>(a.rec)[rw0 * NWT + w0 + ln] = rec_lds[w0 + ln];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int BITS, bool SYM>
+static hipError_t launch_t128(const EncodeArgs& a, hipStream_t st) {
+  constexpr int TILE = kT128Waves * kT128Rows;
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_encode_t128<BITS, SYM>, 64 * kT128Waves, 0) !=
+            hipSuccess || nb <= 0)
+      nb = 1;
+    per_cu = nb;
+  }
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t tiles = (a.n + TILE - 1) / TILE;
+  const int64_t resident = (int64_t)per_cu * cus;
+  const int64_t blocks = tiles < resident ? tiles : resident;
+  hipLaunchKernelGGL((k_encode_t128<BITS, SYM>), dim3((unsigned)blocks), dim3(64 * kT128Waves), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+static hipError_t launch_t128_b(int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
+  switch (bits * 2 + (sym ? 1 : 0)) {
+    case 2: return launch_t128<1, false>(a, st);
+    case 3: return launch_t128<1, true>(a, st);
+    case 4: return launch_t128<2, false>(a, st);
+    case 5: return launch_t128<2, true>(a, st);
+    case 6: return launch_t128<3, false>(a, st);
+    case 7: return launch_t128<3, true>(a, st);
+    case 8: return launch_t128<4, false>(a, st);
+    case 9: return launch_t128<4, true>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int M, int BITS, bool SYM>
 static hipError_t launch_mx_t(const EncodeArgs& a, hipStream_t st) {
   constexpr int TILE = MX<M>::WAVES * MX<M>::ROWS;
@@ -241,7 +454,7 @@ bool encode_mx_supported(int m) { return m == 64 || m == 128; }
 hipError_t launch_encode_mx(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
   if (m == 64) return launch_mx_m<64>(bits, sym, a, st);
-  if (m == 128) return launch_mx_m<128>(bits, sym, a, st);
+  if (m == 128) return launch_t128_b(bits, sym, a, st);
   return hipErrorInvalidValue;
 }
 
