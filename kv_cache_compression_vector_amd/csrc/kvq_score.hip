@@ -397,8 +397,7 @@ struct ScoreSteps {
 };
 
 template <int D, int M, int BITS, bool PCA>
-__global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t chunk,
-                                                         int64_t chunks_per_pair) {
+__global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t chunks_per_pair) {
   constexpr int H = kScoreHeads;
   constexpr int KS = M / 32;              // MFMA k-steps (one 32-coordinate word group each)
   constexpr int NWC = KS * BITS, NWT = NWC + 1;
@@ -423,14 +422,19 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
   const int64_t pair = blockIdx.x / chunks_per_pair;
   const int b = (int)(pair / a.Hkv), kv = (int)(pair % a.Hkv);
   const int G = a.Hq / a.Hkv;
-  const int64_t t_begin = (blockIdx.x % chunks_per_pair) * chunk;
-  const int64_t t_end = t_begin + chunk < a.T ? t_begin + chunk : a.T;
+  // the block's 256-token segments of its (batch, KV head): j, j + cpp, j + 2 cpp, ...: the
+  // blocks of a pair advance through its records side by side
+  const int64_t cpp = chunks_per_pair, jseg = blockIdx.x % chunks_per_pair;
+  const int64_t segs = (a.T + kScoreSegment - 1) / kScoreSegment;
+  const int64_t my_segs = jseg < segs ? (segs - jseg + cpp - 1) / cpp : 0;
+  const int64_t t_end = a.T;
+  auto seg_t0 = [&](int64_t k) { return kScoreSegment * (jseg + cpp * k); };
   const int64_t rowbase = b * a.rec_sb + kv * a.rec_sh;
-  const int64_t n_steps = ((t_end - t_begin + kScoreSegment - 1) / kScoreSegment) * SPS;
+  const int64_t n_steps = my_segs * SPS;
   const uint32_t* rec32 = reinterpret_cast<const uint32_t*>(a.rec);
   // first token of step g of this wave
   auto step_t0 = [&](int64_t g) {
-    return t_begin + kScoreSegment * (g / SPS) + 64 * wave + 16 * TPS * (g % SPS);
+    return seg_t0(g / SPS) + 64 * wave + 16 * TPS * (g % SPS);
   };
   auto load_step = [&](int64_t g, uint32_t (&buf)[SW]) {
     const int64_t t0 = step_t0(g), left = t_end - t0;
@@ -439,7 +443,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
 #pragma unroll
     for (int i = 0; i < SW; ++i) buf[i] = lane + 64 * i < lim ? src[64 * i] : 0u;
   };
-  int bi = PCA ? basis_of_row(a.pca, rowbase + t_begin) : 0;
+  int bi = PCA ? basis_of_row(a.pca, rowbase + (my_segs > 0 ? seg_t0(0) : 0)) : 0;
   uint32_t ring[PF][SW];
   const float cpow = table_pow<BITS>(a.tab);
   prepare_queries<D, M, PCA>(a, b, kv, G, bi, qs, qmu, qT, part, qpow, [&](int phase) {
@@ -481,8 +485,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
             bi = bnext;
           }
           // the next segment's basis, looked up one segment ahead
-          const int64_t sn = t_begin + kScoreSegment * (g / SPS + 1);
-          bnext = sn < t_end ? basis_of_row(a.pca, rowbase + sn) : bi;
+          bnext = g / SPS + 1 < my_segs ? basis_of_row(a.pca, rowbase + seg_t0(g / SPS + 1)) : bi;
         }
       }
       // this step's records to the wave's LDS slice, then the slot refills
@@ -877,9 +880,11 @@ static int device_cus() {
   return cus[dev];
 }
 
-// Launch: one round of resident blocks. Each (batch, KV head) pair is split into as many token
-// chunks (multiples of the 256-token segment) as the chip holds blocks per pair, so every
-// block pays the query preparation once over the longest possible run of tokens.
+// Launch: one round of resident blocks. Each (batch, KV head) pair gets as many blocks as the
+// chip holds blocks per pair; block j of a pair takes the pair's 256-token segments j, j + cpp,
+// ..., so every block pays the query preparation once, and the blocks of a pair read its records
+// side by side (a narrow window of addresses at any moment streams faster on this chip than as
+// many separate contiguous runs).
 template <int D, int M, int BITS, bool PCA>
 static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t st) {
   static int per_cu = 0;
@@ -895,12 +900,11 @@ static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t st) {
   int64_t cpp = ((int64_t)per_cu * device_cus()) / pairs;
   if (cpp > segs) cpp = segs;
   if (cpp < 1) cpp = 1;
-  const int64_t chunk = ((segs + cpp - 1) / cpp) * kScoreSegment;
-  const int64_t chunks = (a.T + chunk - 1) / chunk;
+  const int64_t chunks = cpp;
   const int64_t blocks = chunks * pairs;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_score<D, M, BITS, PCA>), dim3((unsigned)blocks), dim3(kScoreThreads), 0, st,
-                     a, chunk, chunks);
+                     a, chunks);
   return hipGetLastError();
 }
 
