@@ -274,6 +274,19 @@ kvq_status kvq_append_evict_chunk(const kvq_codec* codec, kvq_cache* const* cach
                                   int32_t n_caches, const void* const* new_rows_dev,
                                   int64_t t_new, void* stream, int64_t* evicted_host);
 
+/* Roll a cache back to its first new_len tokens (0 <= new_len <= packed_len + tail_len), e.g.
+ * after rejected speculative tokens. Truncation maps onto both regions [arc PR #98, "What
+ * landed": the cache reports its length in tokens and maps truncation onto both time bases]:
+ *  - new_len >= packed_len: the dense tail keeps its oldest new_len - packed_len rows;
+ *  - new_len < packed_len: the packed region keeps its first new_len records and the tail
+ *    empties (the rolled-back tokens are gone from both regions; rows a caller needs dense again
+ *    come from kvq_decode of the kept records).
+ * The retention floor keeps `margin` dense rows beyond the window after every append, so a
+ * rollback of at most margin + 1 tokens never reaches the packed region [arc PR #98, "Mutation
+ * runs": the rollback margin]. Host only: lengths change, no device memory is touched and
+ * nothing is enqueued. A cache not built for `codec` is refused (KVQ_E_CACHE). */
+kvq_status kvq_cache_truncate(const kvq_codec* codec, kvq_cache* cache, int64_t new_len);
+
 /* Message for the last error on this thread ("" if none): the failing call's argument and
  * value, e.g. "ld_x=100 is not a multiple of 8 elements". Errors are typed statuses with a
  * named cause, never a silent fallback [kakeyaturbo PR #15, "M2" commit: validation at the

@@ -570,6 +570,26 @@ kvq_status kvq_cache_init(const kvq_codec* codec, kvq_cache* cache, void* packed
   return ok();
 }
 
+kvq_status kvq_cache_truncate(const kvq_codec* codec, kvq_cache* cache, int64_t new_len) {
+  Resolved r;
+  kvq_status st = resolve_codec(codec, r);
+  if (st != KVQ_OK) return st;
+  if (!cache) return fail(KVQ_E_NULL, "cache is NULL");
+  if (cache->magic != kCacheMagic) return fail(KVQ_E_CACHE, "cache was not built by kvq_cache_init");
+  if (cache->codec_key != codec_key(codec, r)) return fail(KVQ_E_CACHE, "cache was built for another codec");
+  const int64_t len = cache->packed_len + cache->tail_len;
+  if (new_len < 0 || new_len > len)
+    return fail(KVQ_E_ARG, "new_len=%lld outside [0, %lld] (packed %lld + dense %lld)", (long long)new_len,
+                (long long)len, (long long)cache->packed_len, (long long)cache->tail_len);
+  if (new_len >= cache->packed_len) {
+    cache->tail_len = new_len - cache->packed_len;
+  } else {
+    cache->packed_len = new_len;
+    cache->tail_len = 0;
+  }
+  return ok();
+}
+
 kvq_status kvq_append_evict_chunk(const kvq_codec* codec, kvq_cache* const* caches,
                                   int32_t n_caches, const void* const* new_rows_dev,
                                   int64_t t_new, void* stream, int64_t* evicted_host) {

@@ -90,11 +90,12 @@ def lib() -> ctypes.CDLL:
         L.kvq_attend_packed_static.argtypes = [PC, PC, P, I32, I32, I64, I64, P, P, I32, I64, I64,
                                                I64, ctypes.c_float, ctypes.c_float, P, I64, I64, P]
         L.kvq_stream_copy.argtypes = [P, P, I64, P]
+        L.kvq_cache_truncate.argtypes = [PC, ctypes.POINTER(_Cache), I64]
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_abi_version.restype = ctypes.c_int32
         for name in ("kvq_codec_tables", "kvq_encode", "kvq_decode", "kvq_score_packed",
                      "kvq_attend_packed", "kvq_cache_init", "kvq_append_evict_chunk",
-                     "kvq_stream_copy", "kvq_attend_packed_static"):
+                     "kvq_stream_copy", "kvq_attend_packed_static", "kvq_cache_truncate"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -292,6 +293,13 @@ class Cache:
     @property
     def tail_head(self):
         return self._s.tail_head
+
+    def __len__(self):
+        return self._s.packed_len + self._s.tail_len
+
+    def truncate(self, new_len: int) -> None:
+        """Roll back to the first new_len tokens (host-side lengths only)."""
+        _check(lib().kvq_cache_truncate(self.codec.ref, ctypes.byref(self._s), new_len))
 
     def tail_rows(self) -> torch.Tensor:
         """Dense rows in order, oldest first (a copy)."""

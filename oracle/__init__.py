@@ -278,6 +278,25 @@ class CacheModel:
         self.tail: list[np.ndarray] = []       # oldest first, each [D] uint16
         self.packed: list[np.ndarray] = []     # records, oldest first
 
+    def __len__(self) -> int:
+        """Length in tokens: packed records plus dense rows [arc PR #98, "What landed"]."""
+        return len(self.packed) + len(self.tail)
+
+    def truncate(self, new_len: int) -> None:
+        """Roll the cache back to its first new_len tokens. Truncation maps onto both regions
+        [arc PR #98, "What landed": the cache reports its length in tokens and maps truncation
+        onto both time bases]: a length inside the dense tail drops its newest rows; a length
+        inside the packed region drops the records past it and empties the tail (the tokens
+        between are gone from both regions; a caller that needs them dense again decodes
+        records, the dequantizing path a deep rollback can ask for)."""
+        if not 0 <= new_len <= len(self):
+            raise ValueError(f"new_len={new_len} outside [0, {len(self)}]")
+        if new_len >= len(self.packed):
+            del self.tail[new_len - len(self.packed):]
+        else:
+            del self.packed[new_len:]
+            self.tail = []
+
     def append_evict(self, rows_bf16: np.ndarray) -> int:
         rows = np.ascontiguousarray(rows_bf16, np.uint16).reshape(-1, self.cd.D)
         t_new = rows.shape[0]

@@ -341,3 +341,53 @@ def test_scale_rules_parity(rule, D, bits, custom):
     else:
         r = ((xf - y) * y).sum(1).abs()
         assert torch.all(r <= 1e-4 * xf.norm(dim=1) * y.norm(dim=1))
+
+
+def test_truncate_and_reappend_match_the_model():
+    """Appends, shallow rollbacks (inside the dense tail), a deep rollback into the packed region
+    and appends after them, on two caches at once, against the oracle's cache model: lengths,
+    evicted chunks, dense rows bit-identical, packed records against the oracle's encode of the
+    kept history."""
+    D, bits, window, margin = 128, 3, 160, 16
+    codec = kvq.Codec(D, bits, seed=77)
+    n_caches = 2
+    caches = [kvq.Cache(codec, packed_cap=4096, tail_cap=1200, window=window, margin=margin,
+                        device=DEV) for _ in range(n_caches)]
+    oc = oracle_codec_like(codec)
+    models = [oracle.CacheModel(oc, window, margin) for _ in range(n_caches)]
+    hist = [np.zeros((0, D), np.uint16) for _ in range(n_caches)]
+    ops = [("a", 700), ("t", 5), ("a", 1), ("a", 1), ("t", 17), ("a", 129), ("a", 0),
+           ("deep", 200), ("a", 300), ("t", 3), ("a", 1), ("a", 0), ("deep", 1), ("a", 450)]
+    seed = 900
+    for op, v in ops:
+        if op == "a":
+            rows = [_rows(max(v, 1), D, seed=seed + k) for k in range(n_caches)]
+            seed += 10
+            say(f"append t_new={v}")
+            ev = kvq.append_evict_chunk(codec, caches, rows if v else None, v)
+            for k in range(n_caches):
+                host = bf16_host(rows[k][:v]) if v else np.zeros((0, D), np.uint16)
+                hist[k] = np.concatenate([hist[k], host])
+                assert ev[k] == models[k].append_evict(host)
+        else:
+            for k in range(n_caches):
+                c = caches[k]
+                new_len = len(c) - v if op == "t" else c.packed_len - v
+                say(f"truncate cache {k} to {new_len} ({op}, packed {c.packed_len}, dense {c.tail_len})")
+                c.truncate(new_len)
+                models[k].truncate(new_len)
+                hist[k] = hist[k][:new_len]
+        torch.cuda.synchronize()
+        for k in range(n_caches):
+            c, mdl = caches[k], models[k]
+            assert c.tail_len == len(mdl.tail) and c.packed_len == len(mdl.packed)
+            assert len(c) == len(hist[k])
+            if c.tail_len:
+                np.testing.assert_array_equal(bf16_host(c.tail_rows()), np.stack(mdl.tail))
+            if c.packed_len:
+                got = c.packed[: c.packed_len].cpu().numpy()
+                compare_codes(got, oracle.encode(oc, hist[k][: c.packed_len]), D, bits,
+                              f"cache {k} after {op} {v}")
+    with pytest.raises(kvq.KvqError) as e:
+        caches[0].truncate(len(caches[0]) + 1)
+    assert e.value.name == "KVQ_E_ARG"

@@ -655,3 +655,96 @@ def test_retention_floor_terms_each_bind():
     assert oracle.retention_floor(1024, 100, 16) == 1123     # t_new - 1 binds
     assert oracle.retention_floor(1024, 0, 16) == 1040       # flush: window + margin
     assert oracle.retention_floor(1024, 17, 16) == 1040      # max() ties
+
+
+# --- Rollback / truncation of the two-region cache [arc PR #98, "What landed": truncation maps
+# onto both time bases; "Mutation runs": the rollback margin]. The pins compare the model with the
+# plain append history (an independent list) and with the encode of its prefix.
+
+def _cache_with_history(D, window, margin, t_news, seed):
+    cd = oracle.Codec(D, 3, seed=3)
+    model = oracle.CacheModel(cd, window, margin)
+    rng = np.random.default_rng(seed)
+    hist = []
+    for t_new in t_news:
+        rows = _bf16(rng.normal(size=(t_new, D)))
+        hist.extend(list(rows))
+        model.append_evict(rows)
+    return cd, model, hist, rng
+
+
+def test_truncate_inside_the_dense_tail_drops_the_newest_rows():
+    D, window, margin = 64, 48, 16
+    cd, model, hist, _ = _cache_with_history(D, window, margin, [400, 1, 1, 7], seed=21)
+    n_packed, L = len(model.packed), len(model)
+    assert L == len(hist) and len(model.tail) > 20
+    packed_before = [r.copy() for r in model.packed]
+    model.truncate(L - 13)
+    assert len(model) == L - 13 and len(model.packed) == n_packed
+    np.testing.assert_array_equal(np.stack(model.tail), np.stack(hist[n_packed:L - 13]))
+    np.testing.assert_array_equal(np.stack(model.packed), np.stack(packed_before))
+    model.truncate(L - 13)   # idempotent at the current length
+    assert len(model) == L - 13
+    model.truncate(n_packed)  # exactly the packed length: the tail empties, nothing packed goes
+    assert len(model.tail) == 0 and len(model.packed) == n_packed
+
+
+def test_truncate_into_the_packed_region_keeps_the_encoded_prefix():
+    D, window, margin = 64, 48, 16
+    cd, model, hist, _ = _cache_with_history(D, window, margin, [700, 0], seed=22)
+    assert len(model.packed) >= 3 * oracle.EVICT_CHUNK
+    new_len = len(model.packed) - 150          # not a chunk boundary
+    model.truncate(new_len)
+    assert len(model) == new_len and len(model.tail) == 0
+    np.testing.assert_array_equal(np.stack(model.packed), oracle.encode_records(cd, np.stack(hist[:new_len])))
+    model.truncate(0)
+    assert len(model) == 0
+    with pytest.raises(ValueError):
+        model.truncate(1)
+
+
+def test_reappend_after_rollback_keeps_the_reachable_span_dense():
+    """Rollbacks of at most margin + 1 tokens between appends: after every append the span a
+    query can reach (its t_new rows and the window - 1 before them) lies in the dense tail, the
+    tail equals the history past the packed region, and the packed region is the encode of the
+    history's prefix."""
+    D, window, margin = 32, 40, 16
+    cd = oracle.Codec(D, 2, seed=9)
+    model = oracle.CacheModel(cd, window, margin)
+    rng = np.random.default_rng(23)
+    hist = []
+    for step in range(300):
+        t_new = int(rng.choice([1, 1, 1, 2, 5, 33]))
+        rows = _bf16(rng.normal(size=(t_new, D)))
+        hist.extend(list(rows))
+        model.append_evict(rows)
+        assert len(model.tail) >= min(len(hist), t_new + window - 1)
+        n_packed = len(model.packed)
+        np.testing.assert_array_equal(np.stack(model.tail), np.stack(hist[n_packed:]))
+        if step % 3 == 2:  # speculative tokens rejected
+            r = int(rng.integers(0, min(margin + 1, len(model.tail)) + 1))
+            model.truncate(len(model) - r)
+            del hist[len(hist) - r:]
+            assert len(model.packed) == n_packed  # a shallow rollback never reaches the records
+    np.testing.assert_array_equal(np.stack(model.packed),
+                                  oracle.encode_records(cd, np.stack(hist[:len(model.packed)])))
+
+
+def test_a_rollback_past_the_margin_can_leave_the_window_short():
+    """The margin term binds: from a tail at exactly window + margin rows, rolling back
+    margin + 2 tokens and appending one token leaves fewer dense rows than the window reaches."""
+    D, window, margin = 32, 40, 16
+    cd = oracle.Codec(D, 2, seed=9)
+    model = oracle.CacheModel(cd, window, margin)
+    rng = np.random.default_rng(24)
+    model.append_evict(_bf16(rng.normal(size=(window + margin + 128, D))))
+    model.append_evict(np.zeros((0, D), np.uint16))          # flush: exactly the floor remains
+    assert len(model.tail) == window + margin
+    safe = oracle.CacheModel(cd, window, margin)
+    safe.packed, safe.tail = list(model.packed), list(model.tail)
+    safe.truncate(len(safe) - (margin + 1))
+    safe.append_evict(_bf16(rng.normal(size=(1, D))))
+    assert len(safe.tail) >= window                           # still dense
+    model.truncate(len(model) - (margin + 2))
+    model.append_evict(_bf16(rng.normal(size=(1, D))))
+    assert len(model.tail) == window - 1                      # one reachable row is packed
