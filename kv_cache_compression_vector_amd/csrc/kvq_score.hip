@@ -382,6 +382,69 @@ __device__ __forceinline__ floatx4_t tile_dots_f16(const uint32_t* w, const uint
   return acc;
 }
 
+// ---- The packed score's tile: both query halves in one product --------------------------
+// Row m of the A operand holds head h = m / 4 + 4 ((m % 4) / 2) as its f16 hi half (m even) or lo
+// half (m odd), divided by the head's power of two. The accumulator of lane (oct, tok) then holds
+// head oct's hi and lo partial sums in acc[0], acc[1] and head oct + 4's in acc[2], acc[3]: one
+// product per k-step instead of two, and at up to 4 heads per KV head every lane owns one score.
+template <int M>
+__device__ __forceinline__ void query_rows_f16(const float* qs, const float* qpow, int m, int oct,
+                                               uint4 (&qa)[M / 32]) {
+  const int h = (m >> 2) + 4 * ((m & 3) >> 1);
+  const bool lo = m & 1;
+  const float inv = 1.0f / qpow[h];
+#pragma unroll
+  for (int ks = 0; ks < M / 32; ++ks) {
+    uint32_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = qs[h * M + 32 * ks + 8 * oct + e] * inv;
+      const _Float16 xh = (_Float16)x;
+      v[e] = lo ? f16_bits(x - (float)xh) : (uint32_t)__builtin_bit_cast(uint16_t, xh);
+    }
+    qa[ks] = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                        v[6] | (v[7] << 16));
+  }
+}
+
+// Raw logits of one 16-token record tile against the query rows above (divided by the heads' and
+// the table's powers of two). The pair table has one copy: entry e (bit 2p + i = plane p of code
+// i) is word e. For b = 2, 3 the entry's byte address 4 e is one byte dot product of the masked
+// plane bytes with weights (4, 16, 64) (coordinates at bits 0, 1 of each byte) or (1, 4, 16)
+// (bits 2, 3, whose bytes already carry a factor 4); the table's own address folds into the load.
+template <int M, int BITS>
+__device__ __forceinline__ floatx4_t tile_dots_rows(const uint32_t* w, const uint32_t* lut, int oct,
+                                                    uint32_t sel01, uint32_t sel2,
+                                                    const uint4 (&qa)[M / 32]) {
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const char* lb = reinterpret_cast<const char*>(lut);
+#pragma unroll
+  for (int ks = 0; ks < M / 32; ++ks) {
+    const uint32_t* wk = w + ks * BITS;
+    uint32_t z[4];
+    if constexpr (BITS == 2 || BITS == 3) {
+      uint32_t y = __builtin_amdgcn_perm(wk[1], wk[0], sel01);
+      if constexpr (BITS == 3) y = __builtin_amdgcn_perm(wk[2], y, sel2);
+      const uint32_t y2 = y >> 4;
+      constexpr uint32_t mask = BITS == 3 ? 0x030303u : 0x0303u;
+      constexpr uint32_t w_even = BITS == 3 ? 0x401004u : 0x1004u;
+      constexpr uint32_t w_odd = BITS == 3 ? 0x100401u : 0x0401u;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const uint32_t src = pr < 2 ? y : y2;
+        const uint32_t d = (pr & 1) ? __builtin_amdgcn_udot4(src & (mask << 2), w_odd, 0u, false)
+                                    : __builtin_amdgcn_udot4(src & mask, w_even, 0u, false);
+        z[pr] = *reinterpret_cast<const uint32_t*>(lb + d);
+      }
+    } else {
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) z[pr] = lut[pair_index<BITS>(wk, 8 * oct, 2 * pr)];
+    }
+    acc = mfma16h(qa[ks], make_uint4(z[0], z[1], z[2], z[3]), acc);
+  }
+  return acc;
+}
+
 // Steps of the score loop. A wave takes the 64 consecutive tokens s0 + 64 wave + [0, 64) of each
 // 256-token segment, in steps of TPS 16-token tiles. A step's records are one contiguous byte
 // range: they leave memory as dword loads spread over the wave's lanes (SW per lane, no lane
@@ -401,13 +464,12 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
   constexpr int H = kScoreHeads;
   constexpr int KS = M / 32;              // MFMA k-steps (one 32-coordinate word group each)
   constexpr int NWC = KS * BITS, NWT = NWC + 1;
-  constexpr int COPIES = pair_copies<BITS>();
   using St = ScoreSteps<NWT>;
   constexpr int TPS = St::TPS, SW = St::SW, PF = St::PF, SPS = St::SPS, WORDS = St::WORDS;
   __shared__ __attribute__((aligned(16))) float qs[H * M];
   __shared__ float qmu[H];
   __shared__ float qpow[H];
-  __shared__ uint32_t lut[(1 << (2 * BITS)) * COPIES];  // [entry][copy]: f16 centroid pairs
+  __shared__ uint32_t lut[1 << (2 * BITS)];  // entry e: f16 centroid pair
   // the projection's staging (queries, partial sums) and the loop's record staging share LDS:
   // the former is live only inside prepare_queries, between barriers, before a step's records
   // are staged
@@ -453,19 +515,17 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
 #pragma unroll
       for (int r = 0; r < PF; ++r)
         if (r < n_steps) load_step(r, ring[r]);
-      pair_entries_f16<BITS, COPIES, false>(a.tab, 1.0f / cpow, lut, tid);
-    } else {
-      pair_replicate<(1 << (2 * BITS)), COPIES>(lut, tid);
+      pair_entries_f16<BITS, 1, false>(a.tab, 1.0f / cpow, lut, tid);
     }
   });
-  uint4 qa_hi[KS], qa_lo[KS];  // A operand: head tok, coordinates 32 ks + 8 oct .. + 7
-  float qm[4], qsc[4];         // q . mu and the product's scale of heads 4 oct + k
+  uint4 qa[KS];     // A operand: row tok (a head's hi or lo half), coordinates 32 ks + 8 oct .. + 7
+  float qm[2], qsc[2];  // q . mu and the product's scale of heads oct and oct + 4
   auto operands = [&]() {
-    query_operands_f16<M>(qs, qpow, tok, oct, qa_hi, qa_lo);
+    query_rows_f16<M>(qs, qpow, tok, oct, qa);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      qm[k] = 4 * oct + k < H ? qmu[4 * oct + k] : 0.0f;
-      qsc[k] = 4 * oct + k < H ? qpow[4 * oct + k] * cpow * a.tab.inv_m : 0.0f;
+    for (int k = 0; k < 2; ++k) {
+      qm[k] = qmu[oct + 4 * k];
+      qsc[k] = qpow[oct + 4 * k] * cpow * a.tab.inv_m;
     }
   };
   operands();
@@ -501,15 +561,12 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
         uint32_t w[NWT];
 #pragma unroll
         for (int k = 0; k < NWT; ++k) w[k] = stage[(16 * tt + tok) * NWT + k];
-        const floatx4_t acc =
-            tile_dots_f16<M, BITS, COPIES, false>(w, lut, lane, oct, sel01, sel2, qa_hi, qa_lo);
+        const floatx4_t acc = tile_dots_rows<M, BITS>(w, lut, oct, sel01, sel2, qa);
         const float nrm = __uint_as_float(w[NWC]);
         const bool tv = t0 + 16 * tt + tok < t_end;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int h = 4 * oct + k;
-          if (tv && h < G) srow[(int64_t)h * a.s_sh + 16 * tt] = fmaf(acc[k], nrm * qsc[k], qm[k]);
-        }
+        if (tv && oct < G) srow[(int64_t)oct * a.s_sh + 16 * tt] = fmaf(acc[0] + acc[1], nrm * qsc[0], qm[0]);
+        if (tv && oct + 4 < G)
+          srow[(int64_t)(oct + 4) * a.s_sh + 16 * tt] = fmaf(acc[2] + acc[3], nrm * qsc[1], qm[1]);
       }
       __builtin_amdgcn_wave_barrier();
     }
