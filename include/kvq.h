@@ -182,6 +182,23 @@ kvq_status kvq_encode(const kvq_codec* codec, const void* x_dev, int64_t n, int6
                       void* records_dev, const kvq_outliers* ol, int64_t* ol_total_host,
                       void* stream);
 
+/* Lloyd-Max table refitted to the codec's own rotated, normalised coordinates z = H (s (.) x) /
+ * ||x|| of n calibration rows x_dev (bf16 [n][ld_x]) [kakeyaturbo PR #15, calibration-artefacts
+ * commit: the table refitted to post-rotation residuals lowers the MSE below the Gaussian
+ * table's; larql PR #196, turbo-quant commit: Lloyd's conditions]. Starting from the codec's
+ * table (Gaussian or custom), each of `iters` passes puts every coordinate in its cell of the
+ * current table (the quantiser's decision, the f32 thresholds of the table), sums z and counts
+ * per cell on the GPU (one kernel; partial sums per block in the caller's workspace of
+ * kvq_fit_workspace_bytes(codec, n) bytes), and moves each centroid to its cell's mean (f64 sum
+ * on the host, rounded to f32); an empty cell keeps its centroid. Writes the 2^b f32 centroids to
+ * centroids_host: a table for the codec's centroids_host. Hadamard codecs (proj_rank 0); the
+ * codec's outlier threshold and scale rule play no part. Synchronises the stream once per pass.
+ * Returns KVQ_E_CENTROIDS if the result is not strictly ascending. */
+size_t kvq_fit_workspace_bytes(const kvq_codec* codec, int64_t n);
+kvq_status kvq_fit_table(const kvq_codec* codec, const void* x_dev, int64_t n, int64_t ld_x,
+                         int32_t iters, float* centroids_host, void* workspace_dev,
+                         size_t workspace_bytes, void* stream);
+
 /* Decode n records into y_dev [n][ld_y] of dtype y_dtype (bf16: round to nearest even).
  * x^ = mu + B (n/m) s (.) H_m z^, with z^_i = centroid[code_i] or the outlier value.
  * ol: NULL, or the side list kvq_encode wrote for these records.

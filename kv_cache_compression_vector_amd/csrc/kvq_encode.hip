@@ -408,6 +408,120 @@ hipError_t launch_evict(int m, int bits, bool sym, const EvictArgs& a, hipStream
 }
 
 // ------------------------------------------------------------------------------------------
+// Lloyd-Max refit [kakeyaturbo PR #15, calibration-artefacts commit: the table refitted to the
+// codec's own post-rotation coordinates]. One pass: per block, the sum and the count of the
+// rotated, normalised coordinates z = u / n falling in each cell of the current table, the cell
+// decided as the quantiser decides it (u > n t_k); the host sums the blocks' partials in f64 and
+// moves each centroid to its cell's mean.
+
+template <int M, int BITS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LV<M>::WAVES)))
+void k_fit_cells(EncodeArgs a, float* part_sum, uint32_t* part_cnt) {
+  using L = LV<M>;
+  using St = Stage<L::K>;
+  constexpr int NL = 1 << BITS;
+  __shared__ __attribute__((aligned(16))) uint32_t s_sign[LV<M>::Q > 1 ? M / 2 : 4];
+  __shared__ uint4 s_tile[4 * St::WORDS];
+  __shared__ float s_sum[4][NL];
+  __shared__ uint32_t s_cnt[4][NL];
+  build_sign_table<M>(a.tab, s_sign);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane % L::Q, vw = lane / L::Q;
+  uint4* tile = s_tile + wave * St::WORDS;
+  float sum[NL];
+  uint32_t cnt[NL];
+#pragma unroll
+  for (int c = 0; c < NL; ++c) {
+    sum[c] = 0.0f;
+    cnt[c] = 0u;
+  }
+  const int64_t n_iter = (a.n + L::VPW - 1) / L::VPW;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < n_iter; it += (int64_t)gridDim.x * 4) {
+    const bool valid = it * L::VPW + vw < a.n;
+    float v[L::K];
+    const float n = rotate_owned<M>(a, s_sign, it, tile, q, v);
+    const float rn = n > 0.0f ? 1.0f / n : 0.0f;
+    // a zero vector has u = 0 and z = 0: its compares are 0 > t_k
+    float thr[NL - 1];
+#pragma unroll
+    for (int k = 0; k < NL - 1; ++k) thr[k] = n > 0.0f ? n * a.tab.t[k] : (a.tab.t[k] < 0.0f ? -1.0f : 1.0f);
+#pragma unroll
+    for (int i = 0; i < L::K; ++i) {
+      int code = 0;
+#pragma unroll
+      for (int k = 0; k < NL - 1; ++k) code += v[i] > thr[k] ? 1 : 0;
+      const float z = v[i] * rn;
+#pragma unroll
+      for (int c = 0; c < NL; ++c) {
+        const bool hit = valid && code == c;
+        sum[c] += hit ? z : 0.0f;
+        cnt[c] += hit ? 1u : 0u;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NL; ++c) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      sum[c] += __shfl_xor(sum[c], m, 64);
+      cnt[c] += (uint32_t)__shfl_xor((int)cnt[c], m, 64);
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      s_sum[wave][c] = sum[c];
+      s_cnt[wave][c] = cnt[c];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < NL) {
+    const int c = threadIdx.x;
+    part_sum[(int64_t)blockIdx.x * NL + c] = s_sum[0][c] + s_sum[1][c] + s_sum[2][c] + s_sum[3][c];
+    part_cnt[(int64_t)blockIdx.x * NL + c] = s_cnt[0][c] + s_cnt[1][c] + s_cnt[2][c] + s_cnt[3][c];
+  }
+}
+
+int64_t fit_blocks(int m, int64_t n) {
+  const int vpw = m > 128 ? 64 / (m / 128) : 64;  // vectors per wave (LV<m>::VPW)
+  const int64_t n_iter = (n + vpw - 1) / vpw;
+  int64_t blocks = (n_iter + 3) / 4;
+  if (blocks > 4096) blocks = 4096;
+  return blocks < 1 ? 1 : blocks;
+}
+
+template <int M, int BITS>
+static hipError_t launch_fit_t(const EncodeArgs& a, float* part_sum, uint32_t* part_cnt, hipStream_t st) {
+  const int64_t blocks = fit_blocks(M, a.n);
+  hipLaunchKernelGGL((k_fit_cells<M, BITS>), dim3((unsigned)blocks), dim3(256), 0, st, a, part_sum, part_cnt);
+  return hipGetLastError();
+}
+
+template <int M>
+static hipError_t launch_fit_m(int bits, const EncodeArgs& a, float* ps, uint32_t* pc, hipStream_t st) {
+  switch (bits) {
+    case 1: return launch_fit_t<M, 1>(a, ps, pc, st);
+    case 2: return launch_fit_t<M, 2>(a, ps, pc, st);
+    case 3: return launch_fit_t<M, 3>(a, ps, pc, st);
+    case 4: return launch_fit_t<M, 4>(a, ps, pc, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fit_cells(int m, int bits, const EncodeArgs& a, float* part_sum, uint32_t* part_cnt,
+                            hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  switch (m) {
+    case 64: return launch_fit_m<64>(bits, a, part_sum, part_cnt, st);
+    case 128: return launch_fit_m<128>(bits, a, part_sum, part_cnt, st);
+    case 256: return launch_fit_m<256>(bits, a, part_sum, part_cnt, st);
+    case 512: return launch_fit_m<512>(bits, a, part_sum, part_cnt, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------------------------------
 // Launchers
 
 template <int M, int BITS, bool SYM>

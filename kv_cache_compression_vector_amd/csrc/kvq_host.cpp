@@ -361,6 +361,79 @@ kvq_status kvq_encode(const kvq_codec* codec, const void* x_dev, int64_t n, int6
   return ok();
 }
 
+size_t kvq_fit_workspace_bytes(const kvq_codec* codec, int64_t n) {
+  Resolved r;
+  if (resolve_codec(codec, r) != KVQ_OK || n <= 0 || r.pca) return 0;
+  return (size_t)(kvq::fit_blocks(r.m, n) * r.L * 8);
+}
+
+kvq_status kvq_fit_table(const kvq_codec* codec, const void* x_dev, int64_t n, int64_t ld_x,
+                         int32_t iters, float* centroids_host, void* workspace_dev,
+                         size_t workspace_bytes, void* stream) {
+  Resolved r;
+  kvq_status st = resolve_codec(codec, r);
+  if (st != KVQ_OK) return st;
+  if (r.pca) return fail(KVQ_E_ARG, "the refit needs a Hadamard codec (proj_rank=%u)", codec->proj_rank);
+  if (n <= 0) return fail(KVQ_E_ARG, "n=%lld: the refit needs at least one row", (long long)n);
+  if (iters < 0) return fail(KVQ_E_ARG, "iters=%d is negative", iters);
+  if (!centroids_host) return fail(KVQ_E_NULL, "centroids_host is NULL");
+  if (ld_x < r.D) return fail(KVQ_E_STRIDE, "ld_x=%lld < head_dim=%d", (long long)ld_x, r.D);
+  if (ld_x % 8) return fail(KVQ_E_STRIDE, "ld_x=%lld is not a multiple of 8 elements", (long long)ld_x);
+  if (!x_dev || !workspace_dev) return fail(KVQ_E_NULL, "x_dev or workspace_dev is NULL");
+  if (!aligned(x_dev, 16)) return fail(KVQ_E_STRIDE, "x_dev is not 16-byte aligned");
+  if (!aligned(workspace_dev, 16)) return fail(KVQ_E_STRIDE, "workspace_dev is not 16-byte aligned");
+  const int64_t blocks = kvq::fit_blocks(r.m, n);
+  if (workspace_bytes < (size_t)(blocks * r.L * 8))
+    return fail(KVQ_E_CAPACITY, "workspace_bytes=%zu, need %lld", workspace_bytes, (long long)(blocks * r.L * 8));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float table[16];
+  std::memcpy(table, r.tab.c, sizeof(float) * r.L);
+  float* part_sum = static_cast<float*>(workspace_dev);
+  uint32_t* part_cnt = reinterpret_cast<uint32_t*>(part_sum + blocks * r.L);
+  float* hs = new float[blocks * r.L];
+  uint32_t* hc = new uint32_t[blocks * r.L];
+  for (int it = 0; it < iters; ++it) {
+    kvq_codec cur = *codec;
+    cur.centroids_host = table;
+    cur.outlier_T = 0.0f;
+    Resolved rc;
+    st = resolve_codec(&cur, rc);
+    if (st != KVQ_OK) break;  // a pass that made the table non-ascending (cannot happen in exact
+                              // arithmetic: Lloyd keeps the order) is reported, not used
+    kvq::EncodeArgs a{};
+    a.tab = rc.tab;
+    a.x = static_cast<const uint16_t*>(x_dev);
+    a.ld = ld_x;
+    a.n = n;
+    hipError_t e = kvq::launch_fit_cells(r.m, r.bits, a, part_sum, part_cnt, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(hs, part_sum, sizeof(float) * blocks * r.L, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(hc, part_cnt, sizeof(uint32_t) * blocks * r.L, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      st = from_hip(e, "fit_table");
+      break;
+    }
+    for (int k = 0; k < r.L; ++k) {
+      double sum = 0.0;
+      uint64_t cnt = 0;
+      for (int64_t b = 0; b < blocks; ++b) {
+        sum += (double)hs[b * r.L + k];
+        cnt += hc[b * r.L + k];
+      }
+      if (cnt > 0) table[k] = (float)(sum / (double)cnt);  // an empty cell keeps its centroid
+    }
+  }
+  delete[] hs;
+  delete[] hc;
+  if (st != KVQ_OK) return st;
+  for (int k = 1; k < r.L; ++k)
+    if (!(table[k] > table[k - 1]))
+      return fail(KVQ_E_CENTROIDS, "refitted table not strictly ascending at %d (%g <= %g)", k,
+                  (double)table[k], (double)table[k - 1]);
+  std::memcpy(centroids_host, table, sizeof(float) * r.L);
+  return ok();
+}
+
 kvq_status kvq_decode(const kvq_codec* codec, const void* records_dev, int64_t n,
                       const kvq_outliers* ol, void* y_dev, kvq_dtype y_dtype, int64_t ld_y,
                       void* stream) {

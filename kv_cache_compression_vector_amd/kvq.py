@@ -91,11 +91,15 @@ def lib() -> ctypes.CDLL:
                                                I64, ctypes.c_float, ctypes.c_float, P, I64, I64, P]
         L.kvq_stream_copy.argtypes = [P, P, I64, P]
         L.kvq_cache_truncate.argtypes = [PC, ctypes.POINTER(_Cache), I64]
+        L.kvq_fit_workspace_bytes.argtypes = [PC, I64]
+        L.kvq_fit_workspace_bytes.restype = ctypes.c_size_t
+        L.kvq_fit_table.argtypes = [PC, P, I64, I64, I32, P, P, ctypes.c_size_t, P]
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_abi_version.restype = ctypes.c_int32
         for name in ("kvq_codec_tables", "kvq_encode", "kvq_decode", "kvq_score_packed",
                      "kvq_attend_packed", "kvq_cache_init", "kvq_append_evict_chunk",
-                     "kvq_stream_copy", "kvq_attend_packed_static", "kvq_cache_truncate"):
+                     "kvq_stream_copy", "kvq_attend_packed_static", "kvq_cache_truncate",
+                     "kvq_fit_table"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -199,6 +203,19 @@ def encode(codec: Codec, x: torch.Tensor, records: torch.Tensor | None = None,
                             outliers.ref if outliers is not None else None,
                             ctypes.byref(total) if want_total else None, _stream(x)))
     return (records, total.value) if want_total else records
+
+
+def fit_table(codec: Codec, x: torch.Tensor, iters: int) -> np.ndarray:
+    """Lloyd-Max table refitted to the codec's rotated, normalised coordinates of the rows x
+    (bf16 [n, >=D]), `iters` passes from the codec's table. Returns f32 [2^bits] (host)."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    n = x.shape[0]
+    ws = torch.empty(max(int(lib().kvq_fit_workspace_bytes(codec.ref, n)), 16), dtype=torch.uint8,
+                     device=x.device)
+    out = np.zeros(1 << codec.bits, np.float32)
+    _check(lib().kvq_fit_table(codec.ref, _ptr(x), n, x.stride(0), int(iters), out.ctypes.data,
+                               _ptr(ws), ws.numel(), _stream(x)))
+    return out
 
 
 def decode(codec: Codec, records: torch.Tensor, n: int | None = None,

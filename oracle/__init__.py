@@ -66,6 +66,9 @@ def lib():
         _lib.kvq_ref_encode.restype = I64
         _lib.kvq_ref_decode.argtypes = [ctypes.POINTER(_RefCodec), I64, P, P, P, P, I64, P]
         _lib.kvq_ref_score.argtypes = [ctypes.POINTER(_RefCodec), I64, P, P, P]
+        _lib.kvq_ref_lloyd_fit.argtypes = [P, I64, ctypes.c_int, ctypes.c_int, P]
+        _lib.kvq_ref_table_mse.argtypes = [P, I64, ctypes.c_int, P]
+        _lib.kvq_ref_table_mse.restype = ctypes.c_double
     return _lib
 
 
@@ -260,6 +263,30 @@ def attend(kc: Codec, vc: Codec, q_bf16: np.ndarray, krecs: np.ndarray, vrecs: n
     w = np.exp(logits - logits.max(axis=1, keepdims=True))
     w /= w.sum(axis=1, keepdims=True)
     return w @ V
+
+
+def lloyd_fit(z: np.ndarray, centroids: np.ndarray, iters: int) -> np.ndarray:
+    """Lloyd iterations of an f32 table on samples z (f64), from `centroids` (ascending): cells
+    by the table's f32 thresholds, centroids replaced by their cells' f64 means rounded to f32.
+    Returns the f32 table. [kakeyaturbo PR #15, calibration-artefacts commit]"""
+    z = np.ascontiguousarray(z, np.float64).reshape(-1)
+    c = np.ascontiguousarray(centroids, np.float32).copy()
+    lib().kvq_ref_lloyd_fit(_p(z), z.size, c.size, int(iters), _p(c))
+    return c
+
+
+def table_mse(z: np.ndarray, centroids: np.ndarray) -> float:
+    """Mean squared error of samples z under an f32 table (cells by its f32 thresholds)."""
+    z = np.ascontiguousarray(z, np.float64).reshape(-1)
+    c = np.ascontiguousarray(centroids, np.float32)
+    return float(lib().kvq_ref_table_mse(_p(z), z.size, c.size, _p(c)))
+
+
+def fit_table(cd: Codec, x_bf16: np.ndarray, iters: int) -> np.ndarray:
+    """A codec's table refitted to its own rotated, normalised coordinates z of the rows x
+    (the samples a calibration pass sees), starting from the codec's table."""
+    z = encode(cd, x_bf16)["z"]
+    return lloyd_fit(z, cd.centroids, iters)
 
 
 # --------------------------------------------------------------------------------------------

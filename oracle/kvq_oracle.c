@@ -376,3 +376,48 @@ void kvq_ref_score(const ref_codec* cd, int64_t n, const uint16_t* q, const uint
     out[k] = acc;
   }
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Lloyd-Max table refitted to a sample [kakeyaturbo PR #15, calibration-artefacts commit: the  */
+/* table refitted to the codec's own post-rotation coordinates, MSE below the Gaussian table's; */
+/* LARQL TQ: the same two optimality conditions with the sample's distribution in place of      */
+/* N(0,1)]. One iteration: the f32 thresholds of the current f32 table (midpoints of adjacent   */
+/* centroids, as the quantiser uses them), each sample z in the cell #{k : z > t_k}, each       */
+/* centroid replaced by the f64 mean of its cell, rounded to f32 (the stored table). An empty   */
+/* cell keeps its centroid. `iters` iterations in place on c32 (ascending, L entries).          */
+void kvq_ref_lloyd_fit(const double* z, int64_t n, int L, int iters, float* c32) {
+  float t[255];
+  double sum[256];
+  int64_t cnt[256];
+  for (int it = 0; it < iters; ++it) {
+    kvq_ref_thresholds(c32, L, t);
+    for (int k = 0; k < L; ++k) {
+      sum[k] = 0.0;
+      cnt[k] = 0;
+    }
+    for (int64_t i = 0; i < n; ++i) {
+      int code = 0;
+      for (int k = 0; k + 1 < L; ++k)
+        if (z[i] > (double)t[k]) ++code;
+      sum[code] += z[i];
+      ++cnt[code];
+    }
+    for (int k = 0; k < L; ++k)
+      if (cnt[k] > 0) c32[k] = (float)(sum[k] / (double)cnt[k]);
+  }
+}
+
+/* Mean squared quantisation error of the samples under the f32 table c32 (cells as above). */
+double kvq_ref_table_mse(const double* z, int64_t n, int L, const float* c32) {
+  float t[255];
+  kvq_ref_thresholds(c32, L, t);
+  double acc = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    int code = 0;
+    for (int k = 0; k + 1 < L; ++k)
+      if (z[i] > (double)t[k]) ++code;
+    const double d = z[i] - (double)c32[code];
+    acc += d * d;
+  }
+  return n > 0 ? acc / (double)n : 0.0;
+}

@@ -748,3 +748,54 @@ def test_a_rollback_past_the_margin_can_leave_the_window_short():
     model.truncate(len(model) - (margin + 2))
     model.append_evict(_bf16(rng.normal(size=(1, D))))
     assert len(model.tail) == window - 1                      # one reachable row is packed
+
+
+# --- Lloyd-Max refit on a sample [kakeyaturbo PR #15, calibration-artefacts commit]. Pinned by
+# the population optimum it must approach on Gaussian samples, by the monotone-distortion
+# property of Lloyd's iteration, by a direct numpy evaluation of the sample MSE, and by the
+# heavy-tailed case whose refit must beat the Gaussian table.
+
+def _np_table_mse(z, c32):
+    t = np.array([np.float32(0.5 * (float(c32[k]) + float(c32[k + 1]))) for k in range(len(c32) - 1)],
+                 np.float64)
+    code = np.searchsorted(t, z, side="left")  # #{k : z > t_k}
+    return float(np.mean((z - c32.astype(np.float64)[code]) ** 2))
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_refit_on_gaussian_samples_reproduces_the_gaussian_table(bits):
+    rng = np.random.default_rng(30 + bits)
+    z = rng.normal(size=1 << 20)
+    gauss = oracle.gaussian_table(bits)[1]
+    start = np.linspace(-2.5, 2.5, 1 << bits).astype(np.float32)   # far from the optimum
+    fit = oracle.lloyd_fit(z, start, 200)
+    assert np.all(np.diff(fit) > 0)
+    np.testing.assert_allclose(fit, gauss, atol=0.012)          # sampling error ~1/sqrt(cell size)
+    assert abs(oracle.table_mse(z, fit) - oracle.table_mse(z, gauss)) < 2e-4
+
+
+def test_table_mse_matches_a_direct_evaluation():
+    rng = np.random.default_rng(35)
+    z = np.concatenate([rng.standard_t(3, size=5000), [0.0, -0.5006, 1.05]])
+    c = oracle.gaussian_table(3)[1]
+    assert abs(oracle.table_mse(z, c) - _np_table_mse(z, c)) < 1e-12
+
+
+def test_refit_never_increases_the_sample_mse_and_beats_gaussian_on_heavy_tails():
+    """Student-t(3) rows with 3 channels of 128 scaled x16 (the heavy-tailed V workload),
+    rotated by the codec: each Lloyd pass does not raise the sample MSE, and the refit ends
+    below the Gaussian table's MSE."""
+    D, bits = 128, 2
+    rng = np.random.default_rng(36)
+    x = rng.standard_t(3, size=(4096, D))
+    x[:, rng.choice(D, 3, replace=False)] *= 16
+    cd = oracle.Codec(D, bits, seed=43)
+    z = oracle.encode(cd, _bf16(x))["z"].reshape(-1)
+    c = oracle.gaussian_table(bits)[1]
+    mse = [oracle.table_mse(z, c)]
+    for _ in range(15):
+        c = oracle.lloyd_fit(z, c, 1)
+        mse.append(oracle.table_mse(z, c))
+    assert all(b <= a + 1e-12 for a, b in zip(mse, mse[1:])), mse
+    assert mse[-1] < 0.98 * mse[0]
+    np.testing.assert_array_equal(oracle.fit_table(cd, _bf16(x), 15), c)
