@@ -56,7 +56,7 @@ typedef enum {
   KVQ_E_BITS = 3,       /* bits outside 1..4                                             */
   KVQ_E_CENTROIDS = 4,  /* custom table not strictly ascending or not finite             */
   KVQ_E_STRIDE = 5,     /* misaligned pointer or leading dimension                       */
-  KVQ_E_OUTLIER = 6,    /* outlier request invalid (T < 0, m > 256, missing buffers)     */
+  KVQ_E_OUTLIER = 6,    /* outlier request invalid (T < 0, projection codec, missing buffers) */
   KVQ_E_CAPACITY = 7,   /* a capacity is too small (outlier list, cache region, workspace) */
   KVQ_E_CACHE = 8,      /* cache struct not built by kvq_cache_init, or built for another codec */
   KVQ_E_DEVICE = 9,     /* HIP launch / runtime error                                    */
@@ -92,8 +92,8 @@ typedef struct kvq_codec {
                                  outlier list.                                               */
   uint32_t flags;             /* bits 0..1: the stored scale (KVQ_SCALE_*); other bits 0     */
   uint64_t seed;              /* seed of the +-1 sign diagonal (SplitMix64 stream)           */
-  float outlier_T;            /* 0: no side list. > 0: coordinates with |z| > T are listed
-                                 (requires m <= 256). Units: rotated, normalised (z).        */
+  float outlier_T;            /* 0: no side list. > 0: coordinates with |z| > T are listed.
+                                 Units: rotated, normalised (z).                             */
   uint32_t reserved0;         /* must be 0                                                   */
   const float* centroids_host;   /* f32[2^b] strictly ascending, or NULL = Gaussian Lloyd-Max */
   const uint16_t* basis_dev;     /* PCA only: bf16 [basis_count][D][r] row-major; column j of
@@ -129,7 +129,9 @@ typedef struct kvq_outliers {
   uint32_t* offsets_dev;   /* [n+1]: written by kvq_encode, read by kvq_decode. offsets[n] is
                               the total count, which may exceed capacity (entries past
                               capacity are not written; kvq_decode ignores them)             */
-  uint8_t* idx_dev;        /* [capacity]                                                     */
+  void* idx_dev;           /* [capacity] coordinate indices: u8 while the coded length m <= 256,
+                              u16 (little-endian) for m = 512 [kakeyaturbo PR #15, calibrated
+                              Lloyd-Max + outlier commit: u16 index]                          */
   uint16_t* val_dev;       /* [capacity]                                                     */
   int64_t capacity;        /* entries                                                        */
   void* workspace_dev;     /* encode only: scratch of kvq_encode_workspace_bytes() bytes,

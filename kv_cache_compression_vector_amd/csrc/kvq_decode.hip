@@ -124,7 +124,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
       int64_t e0 = a.ol_off[vec], e1 = a.ol_off[vec + 1];
       if (e1 > a.ol_cap) e1 = a.ol_cap;
       for (int64_t e = e0; e < e1; ++e) {
-        const int idx = a.ol_idx[e];
+        const int idx = M > 256 ? (int)static_cast<const uint16_t*>(a.ol_idx)[e]
+                                : (int)static_cast<const uint8_t*>(a.ol_idx)[e];
         const float val = __uint_as_float((uint32_t)a.ol_val[e] << 16);
 #pragma unroll
         for (int j = 0; j < 8; ++j)

@@ -9,6 +9,8 @@
 #include "kvq_kernels.h"
 #include "kvq_lanevec.h"
 
+#include <type_traits>
+
 namespace kvq {
 
 // The centroid the quantiser picks for rotated coordinate u (code = #{k : u > n t_k}), decided
@@ -119,9 +121,32 @@ __device__ __forceinline__ float rotate_owned(const EncodeArgs& a, const uint32_
   return n;
 }
 
+// Index type of an outlier entry: one byte while the coded length fits in it, two above.
+template <int M>
+using OutlierIdx = typename std::conditional<(M > 256), uint16_t, uint8_t>::type;
+
+// Value of lane part k of this lane's quad (a DPP broadcast within the quad).
+template <int K>
+__device__ __forceinline__ uint32_t quad_lane_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, K | (K << 2) | (K << 4) | (K << 6), 0xF, 0xF, true);
+}
+
+// Sum over the Q lane parts of a vector, and the sum over the parts before this one (q).
 template <int Q>
-__device__ __forceinline__ uint32_t other_part_u32(uint32_t x) {
-  return Q == 2 ? (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true) : 0u;
+__device__ __forceinline__ void part_counts(uint32_t x, int q, uint32_t& total, uint32_t& before) {
+  if constexpr (Q == 1) {
+    total = x;
+    before = 0u;
+  } else if constexpr (Q == 2) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
+    total = x + o;
+    before = q == 1 ? o : 0u;
+  } else {
+    const uint32_t c0 = quad_lane_u32<0>(x), c1 = quad_lane_u32<1>(x), c2 = quad_lane_u32<2>(x),
+                   c3 = quad_lane_u32<3>(x);
+    total = c0 + c1 + c2 + c3;
+    before = (q > 0 ? c0 : 0u) + (q > 1 ? c1 : 0u) + (q > 2 ? c2 : 0u);
+  }
 }
 
 template <int M, int BITS, bool SYM>
@@ -129,7 +154,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LV<M>::WAVE
 void k_encode_count(EncodeArgs a) {
   using L = LV<M>;
   using St = Stage<L::K>;
-  static_assert(L::Q <= 2, "outlier lists need m <= 256");
+  static_assert(L::Q <= 4, "outlier lists need m <= 512");
   constexpr int NWT = (M / 32) * BITS + 1;
   __shared__ __attribute__((aligned(16))) uint32_t s_sign[LV<M>::Q > 1 ? M / 2 : 4];
   __shared__ uint4 s_tile[4 * St::WORDS];
@@ -148,8 +173,9 @@ void k_encode_count(EncodeArgs a) {
     uint32_t cnt = 0;
 #pragma unroll
     for (int k = 0; k < L::K; ++k) cnt += is_outlier(v[k], rn, a.tab.T) ? 1u : 0u;
-    cnt += other_part_u32<L::Q>(cnt);
-    if (valid && q == 0) a.ol_off[vec] = cnt;
+    uint32_t total, before;
+    part_counts<L::Q>(cnt, q, total, before);  // every lane takes part in the DPP moves
+    if (valid && q == 0) a.ol_off[vec] = total;
     quantize_store_lv<M, BITS, SYM>(v, n, n, valid, q, a.tab,
                                     reinterpret_cast<uint32_t*>(a.rec) + vec * NWT);
   }
@@ -160,7 +186,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LV<M>::WAVE
 void k_encode_emit(EncodeArgs a) {
   using L = LV<M>;
   using St = Stage<L::K>;
-  static_assert(L::Q <= 2, "outlier lists need m <= 256");
+  static_assert(L::Q <= 4, "outlier lists need m <= 512");
   __shared__ __attribute__((aligned(16))) uint32_t s_sign[LV<M>::Q > 1 ? M / 2 : 4];
   __shared__ uint4 s_tile[4 * St::WORDS];
   build_sign_table<M>(a.tab, s_sign);
@@ -178,8 +204,8 @@ void k_encode_emit(EncodeArgs a) {
     uint32_t cnt = 0;
 #pragma unroll
     for (int k = 0; k < L::K; ++k) cnt += is_outlier(v[k], rn, a.tab.T) ? 1u : 0u;
-    const uint32_t other = other_part_u32<L::Q>(cnt);  // every lane takes part in the DPP move
-    const uint32_t before = q == 1 ? other : 0u;        // part 0's entries come first
+    uint32_t total, before;  // parts with lower coordinates come first
+    part_counts<L::Q>(cnt, q, total, before);  // every lane takes part in the DPP moves
     if (!valid) continue;
     int64_t pos = (int64_t)a.ol_off[vec] + before;
     int64_t end = a.ol_off[vec + 1];
@@ -188,7 +214,7 @@ void k_encode_emit(EncodeArgs a) {
     for (int k = 0; k < L::K; ++k) {
       if (is_outlier(v[k], rn, a.tab.T)) {
         if (pos < end) {
-          a.ol_idx[pos] = (uint8_t)(q * L::K + k);
+          static_cast<OutlierIdx<M>*>(a.ol_idx)[pos] = (OutlierIdx<M>)(q * L::K + k);
           a.ol_val[pos] = (uint16_t)f32_to_bf16_rne(v[k] * rn);
         }
         ++pos;
@@ -324,6 +350,7 @@ hipError_t launch_encode_outliers3(int m, int bits, bool sym, const EncodeArgs& 
     case 64: return launch_outliers_m<64>(bits, sym, a, part, st);
     case 128: return launch_outliers_m<128>(bits, sym, a, part, st);
     case 256: return launch_outliers_m<256>(bits, sym, a, part, st);
+    case 512: return launch_outliers_m<512>(bits, sym, a, part, st);
   }
   return hipErrorInvalidValue;
 }

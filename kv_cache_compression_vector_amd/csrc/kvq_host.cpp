@@ -165,8 +165,6 @@ kvq_status resolve_codec(const kvq_codec* cd, Resolved& r) {
   if (r.outliers && r.pca)
     return fail(KVQ_E_OUTLIER, "projection codecs carry no outlier list (proj_rank=%u, outlier_T=%g)",
                 cd->proj_rank, (double)cd->outlier_T);
-  if (r.outliers && r.m > 256)
-    return fail(KVQ_E_OUTLIER, "outlier lists need coded length <= 256 (u8 index), got m=%d", r.m);
   if (r.rule != 0 && (r.pca || r.outliers))
     return fail(KVQ_E_ARG, "scale rule %d needs a Hadamard codec without outlier list "
                 "(proj_rank=%u, outlier_T=%g)", r.rule, cd->proj_rank, (double)cd->outlier_T);

@@ -16,7 +16,7 @@ struct EncodeArgs {
   uint8_t* rec;             // records
   // outlier side list (outlier kernels only)
   uint32_t* ol_off;
-  uint8_t* ol_idx;
+  void* ol_idx;             // u8 entries for m <= 256, u16 above
   uint16_t* ol_val;
   int64_t ol_cap;
   // PCA projection (PCA kernels only)
@@ -30,7 +30,7 @@ struct DecodeArgs {
   const uint8_t* rec;
   int64_t n;
   const uint32_t* ol_off;   // nullptr = no side list
-  const uint8_t* ol_idx;
+  const void* ol_idx;       // u8 entries for m <= 256, u16 above
   const uint16_t* ol_val;
   int64_t ol_cap;
   void* y;

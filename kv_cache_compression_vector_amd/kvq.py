@@ -172,11 +172,13 @@ class Codec:
 
 
 class Outliers:
-    """Device CSR outlier list: offsets [n+1] u32, idx [cap] u8, val [cap] bf16 bits."""
+    """Device CSR outlier list: offsets [n+1] u32, idx [cap] (u8 for coded length m <= 256, u16
+    bits in an int16 tensor above), val [cap] bf16 bits."""
 
     def __init__(self, codec: Codec, n: int, capacity: int, device):
         self.offsets = torch.zeros(n + 1, dtype=torch.int32, device=device)
-        self.idx = torch.zeros(max(capacity, 1), dtype=torch.uint8, device=device)
+        self.idx = torch.zeros(max(capacity, 1), dtype=torch.uint8 if codec.m <= 256 else torch.int16,
+                               device=device)
         self.val = torch.zeros(max(capacity, 1), dtype=torch.int16, device=device)
         self.capacity = capacity
         wsb = lib().kvq_encode_workspace_bytes(codec.ref, n)

@@ -180,8 +180,8 @@ class Codec:
 def encode(cd: Codec, x_bf16: np.ndarray, ol_cap: int | None = None) -> dict:
     """Encode rows of x (uint16 bf16 bits, shape [n, D]). Returns a dict with records
     ([n, rec_bytes] u8), codes and flags ([n, m] u8), z ([n, m] f64), norms ([n] f64), the f32
-    decision thresholds and, when T > 0, the outlier CSR (offsets [n+1] u32, idx u8, val u16
-    bf16 bits, total)."""
+    decision thresholds and, when T > 0, the outlier CSR (offsets [n+1] u32, idx u8 for
+    m <= 256 and u16 above, val u16 bf16 bits, total)."""
     x = np.ascontiguousarray(x_bf16, np.uint16).reshape(-1, cd.D)
     n = x.shape[0]
     rec = np.zeros((n, cd.rec_bytes), np.uint8)
@@ -195,12 +195,13 @@ def encode(cd: Codec, x_bf16: np.ndarray, ol_cap: int | None = None) -> dict:
     if cd.T > 0:
         cap = n * cd.m if ol_cap is None else ol_cap
         off = np.zeros(n + 1, np.uint32)
-        idx = np.zeros(max(cap, 1), np.uint8)
+        idx = np.zeros(max(cap, 1), np.uint16)
         val = np.zeros(max(cap, 1), np.uint16)
         total = lib().kvq_ref_encode(ctypes.byref(c), n, _p(x), cd.D, _p(rec), _p(codes),
                                      _p(flags), _p(z), _p(norms), _p(off), _p(idx), _p(val), cap)
-        out.update(offsets=off, idx=idx[:min(total, cap)], val=val[:min(total, cap)],
-                   total=int(total))
+        idx = idx[:min(total, cap)]
+        out.update(offsets=off, idx=idx.astype(np.uint8) if cd.m <= 256 else idx,
+                   val=val[:min(total, cap)], total=int(total))
     else:
         lib().kvq_ref_encode(ctypes.byref(c), n, _p(x), cd.D, _p(rec), _p(codes), _p(flags),
                              _p(z), _p(norms), None, None, None, 0)
@@ -226,7 +227,7 @@ def decode(cd: Codec, records: np.ndarray, offsets=None, idx=None, val=None) -> 
     c = cd._c()
     if offsets is not None:
         off = np.ascontiguousarray(offsets, np.uint32)
-        ix = np.ascontiguousarray(idx, np.uint8)
+        ix = np.ascontiguousarray(np.asarray(idx).astype(np.uint16))
         vv = np.ascontiguousarray(val, np.uint16)
         lib().kvq_ref_decode(ctypes.byref(c), n, _p(rec), _p(off), _p(ix), _p(vv), len(ix), _p(y))
     else:

@@ -234,10 +234,12 @@ typedef struct {
  * Outputs (each may be NULL): records (n * record bytes), codes[n][m], flags[n][m]
  * (bit0: |z - t_k| < 1e-5 for some k; bit1: ||z| - T| < 1e-5), z[n][m] (f64 scaled rotated
  * coordinates), norms[n] (f64). Outliers (T > 0): CSR offsets[n+1], entries written while the
- * running count is below ol_cap. Returns the total outlier count. */
+ * running count is below ol_cap; an entry is the coordinate index (held as u16: the record format
+ * stores it in one byte while m <= 256 and in two above [PR15 OL: u16 index]) and the bf16 value
+ * of z. Returns the total outlier count. */
 int64_t kvq_ref_encode(const ref_codec* cd, int64_t n, const uint16_t* x, int64_t ld,
                        uint8_t* records, uint8_t* codes, uint8_t* flags, double* zout,
-                       double* norms, uint32_t* ol_off, uint8_t* ol_idx, uint16_t* ol_val,
+                       double* norms, uint32_t* ol_off, uint16_t* ol_idx, uint16_t* ol_val,
                        int64_t ol_cap) {
   const int D = cd->D, b = cd->bits, L = 1 << b;
   const int m = cd->r > 0 ? cd->r : D;
@@ -292,7 +294,7 @@ int64_t kvq_ref_encode(const ref_codec* cd, int64_t n, const uint16_t* x, int64_
       /* outlier side list, ascending coordinate within the vector [PR15 OL] */
       if (cd->T > 0.0 && fabs(z) > cd->T) {
         if (total < ol_cap) {
-          if (ol_idx) ol_idx[total] = (uint8_t)i;
+          if (ol_idx) ol_idx[total] = (uint16_t)i;
           if (ol_val) ol_val[total] = float_to_bf16_rne((float)z);
         }
         ++total;
@@ -324,7 +326,7 @@ int64_t kvq_ref_encode(const ref_codec* cd, int64_t n, const uint16_t* x, int64_
 /* Decode n records into y[n][D] (f64) [PR15 M5]: z^_i = centroid[code_i], outlier entries
  * override their coordinate, v^ = norm * s .* (H z^) / m, then x^ = mu + B v^ (PCA). */
 void kvq_ref_decode(const ref_codec* cd, int64_t n, const uint8_t* records,
-                    const uint32_t* ol_off, const uint8_t* ol_idx, const uint16_t* ol_val,
+                    const uint32_t* ol_off, const uint16_t* ol_idx, const uint16_t* ol_val,
                     int64_t ol_cap, double* y) {
   const int D = cd->D, b = cd->bits;
   const int m = cd->r > 0 ? cd->r : D;

@@ -74,7 +74,6 @@ FAKE = 1 << 40  # a 16-byte-aligned non-NULL address; never dereferenced (valida
     (dict(head_dim=64, proj_rank=128), "KVQ_E_DIM", "proj_rank=128"),
     (dict(head_dim=256, proj_rank=256), "KVQ_E_DIM", "proj_rank=256"),
     (dict(proj_rank=48), "KVQ_E_DIM", "proj_rank=48"),
-    (dict(head_dim=512, outlier_T=2.0), "KVQ_E_OUTLIER", "m=512"),
     (dict(outlier_T=-1.0), "KVQ_E_OUTLIER", "outlier_T"),
     (dict(centroids=np.array([0.0, -1.0, 1.0, 2.0], np.float32), bits=2), "KVQ_E_CENTROIDS", "ascending"),
     (dict(centroids=np.array([0.0, np.nan, 1.0, 2.0], np.float32), bits=2), "KVQ_E_CENTROIDS", "finite"),
@@ -87,6 +86,13 @@ def test_codec_refusals(kw, status, needle):
                         ctypes.c_void_p(FAKE), None, None, None)
     assert name == status and needle in msg, msg
     assert kvq.lib().kvq_record_bytes(cd.ref) == 0
+
+
+def test_outlier_lists_are_accepted_at_head_dim_512():
+    """Coded length 512 carries outlier lists with two-byte indices: the codec is valid."""
+    cd = kvq.Codec(512, 4, outlier_T=2.0)
+    assert kvq.lib().kvq_record_bytes(cd.ref) == 260
+    assert kvq.lib().kvq_encode_workspace_bytes(cd.ref, 1000) > 0
 
 
 def test_decode_basis_needs_a_projection_codec():

@@ -125,6 +125,43 @@ def test_heavy_tailed_v_with_outliers_full_size():
     assert e_with < e_without
 
 
+def test_v4_flash_geometry_outlier_lists_full_size():
+    """One V4-Flash-shaped layer (65,536 rows of head_dim 512, iid N(0,1)), 4 bits, T = 2.0: the
+    outlier lists carry u16 indices; sampled vectors' codes and lists against the oracle, CSR
+    monotone, decode with the list against the oracle on the GPU's own records and list."""
+    D, bits, T_ = 512, 4, 2.0
+    x = synth.iid_normal((65536, D), seed=1003, device=DEV)
+    n = x.shape[0]
+    codec = kvq.Codec(D, bits, seed=42, outlier_T=T_)
+    oc = oracle_codec_like(codec)
+    ol = kvq.Outliers(codec, n, capacity=n * D // 8, device=DEV)
+    say(f"v4-flash geometry outliers: n={n}, D={D}, b={bits}, T={T_}")
+    rec, total = kvq.encode(codec, x, outliers=ol, want_total=True)
+    rate = total / (n * D)
+    say(f"  outliers {total} ({100 * rate:.2f} % of coordinates)")
+    assert 0.04 < rate < 0.05
+    off = ol.offsets.cpu().numpy().view(np.uint32).astype(np.int64)
+    assert off[0] == 0 and np.all(np.diff(off) >= 0) and off[-1] == total
+    idx = ol.idx[:total].cpu().numpy().view(np.uint16)
+    val = ol.val[:total].cpu().numpy().view(np.uint16)
+    assert idx.max() > 255
+    rows = _sample(n, 1500, seed=9)
+    ref = oracle.encode(oc, bf16_host(_take(x, rows)))
+    got = _take(rec, rows).cpu().numpy()
+    compare_codes(got, ref, D, bits, "v4-flash geometry codes")
+    compare_outlier_lists(off, idx, val, ref, rows, "v4-flash geometry outliers")
+    sub_off, sub_idx, sub_val = [0], [], []
+    for v in rows:
+        sub_idx.append(idx[off[v]:off[v + 1]])
+        sub_val.append(val[off[v]:off[v + 1]])
+        sub_off.append(sub_off[-1] + off[v + 1] - off[v])
+    y = kvq.decode(codec, rec, outliers=ol)
+    yref = oracle.decode(oc, got, np.array(sub_off, np.uint32), np.concatenate(sub_idx),
+                         np.concatenate(sub_val))
+    compare_decoded(_take(y, rows).cpu().numpy(), yref, unpack_records(got, D, bits)[1],
+                    "v4-flash geometry decode")
+
+
 def test_long_context_score_full_size():
     """K [8, 8, 131072, 128] iid N(0,1) at 3 bits; q [8, 32, 128]; GQA 4:1."""
     B, Hkv, T, D, Hq, bits = 8, 8, 131072, 128, 32, 3

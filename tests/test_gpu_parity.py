@@ -188,7 +188,8 @@ def test_score_packed_query_and_table_scales(cscale):
     assert np.all(s[:, 2::G] == 0.0), "a zero query head scores zero"
 
 
-@pytest.mark.parametrize("D,bits,T_", [(128, 2, 2.0), (64, 3, 1.5), (256, 2, 2.5), (128, 4, 2.0)])
+@pytest.mark.parametrize("D,bits,T_", [(128, 2, 2.0), (64, 3, 1.5), (256, 2, 2.5), (128, 4, 2.0),
+                                       (512, 4, 2.0), (512, 2, 1.8)])
 def test_outlier_parity(D, bits, T_):
     n = 3000 + 13
     x = _rows(n, D, seed=D + bits)
@@ -202,6 +203,7 @@ def test_outlier_parity(D, bits, T_):
     compare_codes(recn, ref, D, bits, "outlier codes")
     off = ol.offsets.cpu().numpy().view(np.uint32)
     idx = ol.idx.cpu().numpy()
+    idx = idx.view(np.uint16) if D > 256 else idx   # u16 indices above 256 coordinates
     val = ol.val.cpu().numpy().view(np.uint16)
     roff = ref["offsets"]
     near_t = (ref["flags"] & oracle.FLAG_NEAR_T) != 0

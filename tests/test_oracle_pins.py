@@ -314,7 +314,7 @@ def test_outliers_infinite_threshold_is_the_plain_path():
                       big["idx"], big["val"]))
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
 def test_outliers_tiny_threshold_reconstructs_input(D):
     """T -> 0+: every nonzero coordinate is listed with its bf16 value, so decode returns x
     up to bf16 rounding of z (relative 2^-8 per coordinate)."""
@@ -340,6 +340,28 @@ def test_outlier_rate_on_gaussian_rows_and_csr_order():
         ix = out["idx"][off[row]:off[row + 1]]
         assert np.all(np.diff(ix.astype(int)) > 0)
         np.testing.assert_array_equal(ix, np.nonzero(np.abs(out["z"][row]) > 2.0)[0])
+
+
+def test_outlier_lists_at_head_dim_512_use_two_byte_indices():
+    """m = 512 (the V4-Flash geometry): indices reach 511, so the list holds u16 indices
+    [kakeyaturbo PR #15, calibrated Lloyd-Max + outlier commit: (u16 idx, f16 val)]; the entries
+    are exactly the coordinates with |z| > T in ascending order, the Gaussian tail rate holds,
+    and decoding with the list moves the listed coordinates to their bf16 values."""
+    x = _bf16(np.random.default_rng(8).normal(size=(400, 512)))
+    cd = oracle.Codec(512, 4, seed=11, T=2.0)
+    out = oracle.encode(cd, x)
+    assert out["idx"].dtype == np.uint16 and out["idx"].max() > 255
+    assert out["total"] / x.size == pytest.approx(2 * scipy.stats.norm.sf(2.0), abs=0.003)
+    off = out["offsets"]
+    for row in range(0, 400, 7):
+        ix = out["idx"][off[row]:off[row + 1]]
+        np.testing.assert_array_equal(ix, np.nonzero(np.abs(out["z"][row]) > 2.0)[0])
+    plain = oracle.decode(oracle.Codec(512, 4, seed=11), out["records"])
+    withl = oracle.decode(cd, out["records"], out["offsets"], out["idx"], out["val"])
+    xv = _bf16_to_f64(x)
+    e_plain = np.linalg.norm(xv - plain, axis=1) / np.linalg.norm(xv, axis=1)
+    e_list = np.linalg.norm(xv - withl, axis=1) / np.linalg.norm(xv, axis=1)
+    assert e_list.mean() < e_plain.mean()
 
 
 def test_outlier_capacity_truncates_entries_not_offsets():
