@@ -319,6 +319,17 @@ const char* kvq_last_error(void);
  * device in the same run. Not part of the codec. */
 kvq_status kvq_stream_copy(void* dst_dev, const void* src_dev, int64_t bytes, void* stream);
 
+/* Streaming read of `bytes` (a multiple of 16; src_dev 16-byte aligned) on `stream`, folded by
+ * XOR into the one u32 at sink_dev (4-byte aligned): afterwards *sink_dev holds its old value
+ * XOR the XOR of every 32-bit word of the source. The caller sets *sink_dev first. The
+ * read-only bandwidth control of a measurement, beside kvq_stream_copy and kvq_stream_fill;
+ * not part of the codec. */
+kvq_status kvq_stream_read(const void* src_dev, int64_t bytes, uint32_t* sink_dev, void* stream);
+
+/* Streaming fill of `bytes` (a multiple of 16; dst_dev 16-byte aligned) with the 32-bit `value`
+ * on `stream`: the write-only bandwidth control of a measurement. Not part of the codec. */
+kvq_status kvq_stream_fill(void* dst_dev, int64_t bytes, uint32_t value, void* stream);
+
 /* ABI version of this header; record format version. */
 #define KVQ_ABI_VERSION 1
 #define KVQ_RECORD_FORMAT 1

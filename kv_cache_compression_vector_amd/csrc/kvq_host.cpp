@@ -267,6 +267,22 @@ kvq_status kvq_stream_copy(void* dst_dev, const void* src_dev, int64_t bytes, vo
   return from_hip(kvq::launch_stream_copy(dst_dev, src_dev, bytes, static_cast<hipStream_t>(stream)), "stream_copy");
 }
 
+kvq_status kvq_stream_read(const void* src_dev, int64_t bytes, uint32_t* sink_dev, void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(KVQ_E_ARG, "bytes=%lld must be a non-negative multiple of 16", (long long)bytes);
+  if (bytes == 0) return ok();
+  if (!src_dev || !sink_dev) return fail(KVQ_E_NULL, "src_dev or sink_dev is NULL");
+  if (!aligned(src_dev, 16) || !aligned(sink_dev, 4)) return fail(KVQ_E_STRIDE, "src_dev must be 16-byte and sink_dev 4-byte aligned");
+  return from_hip(kvq::launch_stream_read(src_dev, bytes, sink_dev, static_cast<hipStream_t>(stream)), "stream_read");
+}
+
+kvq_status kvq_stream_fill(void* dst_dev, int64_t bytes, uint32_t value, void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(KVQ_E_ARG, "bytes=%lld must be a non-negative multiple of 16", (long long)bytes);
+  if (bytes == 0) return ok();
+  if (!dst_dev) return fail(KVQ_E_NULL, "dst_dev is NULL");
+  if (!aligned(dst_dev, 16)) return fail(KVQ_E_STRIDE, "dst_dev must be 16-byte aligned");
+  return from_hip(kvq::launch_stream_fill(dst_dev, bytes, value, static_cast<hipStream_t>(stream)), "stream_fill");
+}
+
 size_t kvq_record_bytes(const kvq_codec* codec) {
   Resolved r;
   if (resolve_codec(codec, r) != KVQ_OK) return 0;

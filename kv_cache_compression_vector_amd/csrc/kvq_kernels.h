@@ -135,6 +135,8 @@ hipError_t launch_evict(int m, int bits, bool sym, const EvictArgs& a, hipStream
 hipError_t launch_tail_copy(const TailCopyArgs& a, hipStream_t st);
 hipError_t launch_clear_u32(uint32_t* p, int64_t n_words, hipStream_t st);
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t st);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t st);
+hipError_t launch_stream_fill(void* dst, int64_t bytes, uint32_t value, hipStream_t st);
 // Lloyd-Max refit pass: per-block sums and counts of z in each cell of a.tab's table
 // (fit_blocks(m, n) blocks, 2^bits floats and u32 each).
 int64_t fit_blocks(int m, int64_t n);

@@ -502,8 +502,16 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(ScoreArgs a, int64_t ch
     const int64_t t0 = step_t0(g), left = t_end - t0;
     const int lim = left >= 16 * TPS ? WORDS : (left > 0 ? (int)left * NWT : 0);  // uniform
     const uint32_t* src = rec32 + (rowbase + t0) * NWT + lane;
+    // records are read once: streaming (nontemporal) loads keep them from displacing the
+    // score rows in the caches (measured 124 -> 117 us on the long-context score)
+    if (lim == WORDS && WORDS == 64 * SW) {
 #pragma unroll
-    for (int i = 0; i < SW; ++i) buf[i] = lane + 64 * i < lim ? src[64 * i] : 0u;
+      for (int i = 0; i < SW; ++i) buf[i] = __builtin_nontemporal_load(src + 64 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < SW; ++i)
+        buf[i] = lane + 64 * i < lim ? __builtin_nontemporal_load(src + 64 * i) : 0u;
+    }
   };
   int bi = PCA ? basis_of_row(a.pca, rowbase + (my_segs > 0 ? seg_t0(0) : 0)) : 0;
   uint32_t ring[PF][SW];

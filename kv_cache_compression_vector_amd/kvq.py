@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_attend_packed_static.argtypes = [PC, PC, P, I32, I32, I64, I64, P, P, I32, I64, I64,
                                                I64, ctypes.c_float, ctypes.c_float, P, I64, I64, P]
         L.kvq_stream_copy.argtypes = [P, P, I64, P]
+        L.kvq_stream_read.argtypes = [P, I64, P, P]
+        L.kvq_stream_fill.argtypes = [P, I64, ctypes.c_uint32, P]
         L.kvq_cache_truncate.argtypes = [PC, ctypes.POINTER(_Cache), I64]
         L.kvq_fit_workspace_bytes.argtypes = [PC, I64]
         L.kvq_fit_workspace_bytes.restype = ctypes.c_size_t
@@ -99,7 +101,7 @@ def lib() -> ctypes.CDLL:
         for name in ("kvq_codec_tables", "kvq_encode", "kvq_decode", "kvq_score_packed",
                      "kvq_attend_packed", "kvq_cache_init", "kvq_append_evict_chunk",
                      "kvq_stream_copy", "kvq_attend_packed_static", "kvq_cache_truncate",
-                     "kvq_fit_table"):
+                     "kvq_fit_table", "kvq_stream_read", "kvq_stream_fill"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -348,3 +350,19 @@ def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
     nb = src.numel() * src.element_size()
     assert dst.numel() * dst.element_size() == nb and src.is_contiguous() and dst.is_contiguous()
     _check(lib().kvq_stream_copy(_ptr(dst), _ptr(src), nb, _stream(src)))
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """The library's streaming read kernel (a bandwidth control): sink (one int32 on the same
+    device) ^= the XOR of every 32-bit word of src."""
+    assert src.is_contiguous() and sink.numel() >= 1 and sink.element_size() == 4
+    _check(lib().kvq_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                 _stream(src)))
+
+
+def stream_fill(dst: torch.Tensor, value: int) -> None:
+    """The library's streaming fill kernel (a bandwidth control): every 32-bit word of dst <-
+    value."""
+    assert dst.is_contiguous()
+    _check(lib().kvq_stream_fill(_ptr(dst), dst.numel() * dst.element_size(), value & 0xFFFFFFFF,
+                                 _stream(dst)))

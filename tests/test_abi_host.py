@@ -212,3 +212,21 @@ def test_zero_sized_calls_are_no_ops():
     cd = kvq.Codec(128, 3)
     assert L.kvq_encode(cd.ref, None, 0, 128, None, None, None, None) == 0
     assert L.kvq_decode(cd.ref, None, 0, None, None, 0, 128, None) == 0
+
+
+def test_stream_control_refusals():
+    """The bandwidth controls validate sizes, pointers and alignment before any launch."""
+    L = kvq.lib()
+    P = ctypes.c_void_p
+    assert _status(L.kvq_stream_copy, P(FAKE), P(FAKE), 24, None)[0] == "KVQ_E_ARG"
+    assert _status(L.kvq_stream_copy, None, P(FAKE), 32, None)[0] == "KVQ_E_NULL"
+    assert _status(L.kvq_stream_copy, P(FAKE + 4), P(FAKE), 32, None)[0] == "KVQ_E_STRIDE"
+    assert _status(L.kvq_stream_read, P(FAKE), -16, P(FAKE), None)[0] == "KVQ_E_ARG"
+    assert _status(L.kvq_stream_read, P(FAKE), 32, None, None)[0] == "KVQ_E_NULL"
+    assert _status(L.kvq_stream_read, P(FAKE + 8), 32, P(FAKE), None)[0] == "KVQ_E_STRIDE"
+    assert _status(L.kvq_stream_read, P(FAKE), 32, P(FAKE + 2), None)[0] == "KVQ_E_STRIDE"
+    assert _status(L.kvq_stream_fill, P(FAKE), 20, 7, None)[0] == "KVQ_E_ARG"
+    assert _status(L.kvq_stream_fill, None, 32, 7, None)[0] == "KVQ_E_NULL"
+    assert _status(L.kvq_stream_fill, P(FAKE + 4), 32, 7, None)[0] == "KVQ_E_STRIDE"
+    # zero bytes is a no-op that touches nothing
+    assert _status(L.kvq_stream_fill, None, 0, 7, None)[0] == "KVQ_OK"
