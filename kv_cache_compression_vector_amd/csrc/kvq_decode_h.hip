@@ -528,13 +528,30 @@ static int dh_device_cus() {
   return cus[dev];
 }
 
+// Blocks of k_decode_h<M, BITS, BF16> that one compute unit holds at once (registers and LDS:
+// the bf16 staging and the pair table leave 3 blocks at b = 3, 4 at b <= 2).
+template <int M, int BITS, bool BF16>
+static int dh_blocks_per_cu() {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_h<M, BITS, BF16>, 64 * kDhWaves, 0) !=
+            hipSuccess || nb <= 0)
+      nb = 1;
+    per_cu = nb < 4 ? nb : 4;
+  }
+  return per_cu;
+}
+
 template <int M, int BITS>
 static hipError_t launch_dh_t(bool bf16, const DecodeArgs& a, hipStream_t st) {
-  // one resident round (4 blocks of 4 waves per compute unit, measured best against 2 and 8);
-  // waves stride over the steps
+  // exactly one resident round (at most 4 blocks of 4 waves per compute unit, measured best
+  // against 2 and 8), waves striding over the steps: a grid beyond what the chip holds at once
+  // would leave its last blocks to run alone on part of the chip
   const int64_t steps = (a.n + 16 * kDhVT - 1) / (16 * kDhVT);
   int64_t blocks = (steps + kDhWaves - 1) / kDhWaves;
-  const int64_t resident = 4 * (int64_t)dh_device_cus();
+  const int per_cu = bf16 ? dh_blocks_per_cu<M, BITS, true>() : dh_blocks_per_cu<M, BITS, false>();
+  const int64_t resident = (int64_t)per_cu * dh_device_cus();
   if (blocks > resident) blocks = resident;
   const dim3 g((unsigned)blocks), b(64 * kDhWaves);
   if (bf16) hipLaunchKernelGGL((k_decode_h<M, BITS, true>), g, b, 0, st, a);

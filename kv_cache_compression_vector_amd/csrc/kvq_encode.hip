@@ -346,6 +346,12 @@ static hipError_t launch_outliers_m(int bits, bool sym, const EncodeArgs& a, uin
 hipError_t launch_encode_outliers3(int m, int bits, bool sym, const EncodeArgs& a, uint32_t* part,
                                    hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
+  if (m == 128) {  // both passes on the matrix-core rotation
+    hipError_t e = launch_t128_outlier_pass<1>(bits, sym, a, st);
+    if (e == hipSuccess) e = launch_offsets_scan(a.ol_off, a.n, part, st);
+    if (e == hipSuccess) e = launch_t128_outlier_pass<2>(bits, sym, a, st);
+    return e;
+  }
   switch (m) {
     case 64: return launch_outliers_m<64>(bits, sym, a, part, st);
     case 128: return launch_outliers_m<128>(bits, sym, a, part, st);

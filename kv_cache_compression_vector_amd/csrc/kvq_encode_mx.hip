@@ -245,12 +245,22 @@ constexpr int kT128Rows = 16;   // vectors per wave tile
 
 // Block b takes the block tiles b, b + G, b + 2G, ... (G = the grid): at any moment the resident
 // blocks stream through one window of the rows.
-template <int BITS, bool SYM>
+//
+// Outlier side lists [kakeyaturbo PR #15, calibrated Lloyd-Max + outlier commit] take two passes
+// of this kernel around the scan of the counts (kvq_encode.hip): OL = 1 writes the records and
+// each vector's count of coordinates with |z| > T into offsets[v]; OL = 2 (after the scan) writes
+// only the entries. A lane holds the coordinates j = 8 J + 2 grp + h (J < 16, h < 2) of its
+// vector, the outlier bit of j at bit 2 J + h of its mask: with the four groups' masks, the rank
+// of an entry among the vector's outliers in ascending coordinate order is the number of set
+// bits of lower coordinates, counted group by group. Both passes decide |u / n| > T with the
+// same instructions, so their counts agree.
+template <int BITS, bool SYM, int OL = 0>
 __global__ __launch_bounds__(64 * kT128Waves) __attribute__((amdgpu_waves_per_eu(3)))
 void k_encode_t128(EncodeArgs a) {
   constexpr int M = 128, KS = 4, RCH = M / 8, ROWS = kT128Rows;
   constexpr int NWC = (M / 32) * BITS, NWT = NWC + 1, TILE = kT128Waves * ROWS;
   __shared__ uint4 s_reg[kT128Waves * ROWS * RCH];
+  __shared__ float s_z[OL == 2 ? kT128Waves * 32 * 64 : 1];  // entry pass: z[t] of each lane
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
   const int c = ln & 15, grp = ln >> 4;
   uint4 F[2][KS], FN[2][KS];
@@ -339,18 +349,78 @@ void k_encode_t128(EncodeArgs a) {
       n = bad ? __builtin_amdgcn_sqrtf(s2) * pow2f(ex) : n;
     }
     // rotation and quantiser, one m-tile at a time: plane bits t = 4 mt + i, pushed from t = 31
-    const Quant<BITS, SYM> q(a.tab, n);
-    QuantAcc<BITS, SYM> qa;
-#pragma unroll
-    for (int mt = 7; mt >= 0; --mt) {
+    auto mtile = [&](int mt) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bool neg = __builtin_popcount(ks & (mt & 3)) & 1;  // compile-time
         acc = mfma_bf16(neg ? FN[mt >> 2][ks] : F[mt >> 2][ks], X[ks], acc);
       }
+      return acc;
+    };
+    // row i of m-tile mt is coordinate 8 (4 (mt % 4) + i) + 2 grp + (mt >> 2): its mask bit
+    auto ol_bit = [](int mt, int i) { return 2 * (4 * (mt & 3) + i) + (mt >> 2); };
+    const float rn = n > 0.0f ? 1.0f / n : 0.0f;
+    const int64_t vec = rw0 + c;
+    if constexpr (OL == 2) {
+      // the lane's z values go to its LDS column (z[t] at row t), the outlier bits to olm
+      float* zc = s_z + wave * 32 * 64 + ln;
+      uint32_t olm = 0;
 #pragma unroll
-      for (int i = 3; i >= 0; --i) qa.push(acc[i], q);
+      for (int mt = 7; mt >= 0; --mt) {
+        const floatx4 acc = mtile(mt);
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          const float z = acc[i] * rn;
+          zc[64 * ol_bit(mt, i)] = z;
+          olm |= (fabsf(z) > a.tab.T ? 1u : 0u) << ol_bit(mt, i);
+        }
+      }
+      uint32_t mg[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) mg[g] = (uint32_t)__shfl((int)olm, c + 16 * g, 64);
+      if (olm != 0u && vec < a.n) {
+        const int64_t base = a.ol_off[vec];
+        int64_t end = a.ol_off[vec + 1];
+        if (end > a.ol_cap) end = a.ol_cap;
+        for (uint32_t rem = olm; rem != 0u; rem &= rem - 1u) {
+          const int t = __builtin_ctz(rem), J = t >> 1;
+          // set bits of coordinates below 8 J (lo) and below 8 J + 8 (lo_pair; all ones at J = 15)
+          const uint32_t lo = (1u << (2 * J)) - 1u, lo_pair = (4u << (2 * J)) - 1u;
+          uint32_t rank = __builtin_popcount(olm & ((1u << t) - 1u));
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            if (g != grp) rank += __builtin_popcount(mg[g] & (g < grp ? lo_pair : lo));
+          const int64_t pos = base + rank;
+          if (pos < end) {
+            static_cast<uint8_t*>(a.ol_idx)[pos] = (uint8_t)(8 * J + 2 * grp + (t & 1));
+            a.ol_val[pos] = (uint16_t)f32_to_bf16_rne(zc[64 * t]);
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      continue;  // the records were written by the first pass
+    }
+    const Quant<BITS, SYM> q(a.tab, n);
+    QuantAcc<BITS, SYM> qa;
+    uint32_t olm = 0;
+#pragma unroll
+    for (int mt = 7; mt >= 0; --mt) {
+      const floatx4 acc = mtile(mt);
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        qa.push(acc[i], q);
+        if constexpr (OL == 1) {
+          const float z = acc[i] * rn;
+          olm |= (fabsf(z) > a.tab.T ? 1u : 0u) << ol_bit(mt, i);
+        }
+      }
+    }
+    if constexpr (OL == 1) {
+      uint32_t cnt = __builtin_popcount(olm);
+      cnt += (uint32_t)__shfl_xor((int)cnt, 16, 64);
+      cnt += (uint32_t)__shfl_xor((int)cnt, 32, 64);
+      if (grp == 0 && vec < a.n) a.ol_off[vec] = cnt;
     }
     uint32_t pl[BITS];
     qa.planes(q, 0xFFFFFFFFu, pl);
@@ -386,13 +456,13 @@ void k_encode_t128(EncodeArgs a) {
   }
 }
 
-template <int BITS, bool SYM>
+template <int BITS, bool SYM, int OL = 0>
 static hipError_t launch_t128(const EncodeArgs& a, hipStream_t st) {
   constexpr int TILE = kT128Waves * kT128Rows;
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_encode_t128<BITS, SYM>, 64 * kT128Waves, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_encode_t128<BITS, SYM, OL>, 64 * kT128Waves, 0) !=
             hipSuccess || nb <= 0)
       nb = 1;
     per_cu = nb;
@@ -403,10 +473,33 @@ static hipError_t launch_t128(const EncodeArgs& a, hipStream_t st) {
   const int64_t tiles = (a.n + TILE - 1) / TILE;
   const int64_t resident = (int64_t)per_cu * cus;
   const int64_t blocks = tiles < resident ? tiles : resident;
-  hipLaunchKernelGGL((k_encode_t128<BITS, SYM>), dim3((unsigned)blocks), dim3(64 * kT128Waves), 0,
+  hipLaunchKernelGGL((k_encode_t128<BITS, SYM, OL>), dim3((unsigned)blocks), dim3(64 * kT128Waves), 0,
                      st, a);
   return hipGetLastError();
 }
+
+// The two outlier passes of coded length 128 (OL = 1: records and counts; OL = 2: entries,
+// which use neither the bit width nor the table's symmetry).
+template <int OL>
+hipError_t launch_t128_outlier_pass(int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
+  if constexpr (OL == 2) {
+    return launch_t128<1, true, 2>(a, st);
+  } else {
+    switch (bits * 2 + (sym ? 1 : 0)) {
+      case 2: return launch_t128<1, false, OL>(a, st);
+      case 3: return launch_t128<1, true, OL>(a, st);
+      case 4: return launch_t128<2, false, OL>(a, st);
+      case 5: return launch_t128<2, true, OL>(a, st);
+      case 6: return launch_t128<3, false, OL>(a, st);
+      case 7: return launch_t128<3, true, OL>(a, st);
+      case 8: return launch_t128<4, false, OL>(a, st);
+      case 9: return launch_t128<4, true, OL>(a, st);
+    }
+    return hipErrorInvalidValue;
+  }
+}
+template hipError_t launch_t128_outlier_pass<1>(int, bool, const EncodeArgs&, hipStream_t);
+template hipError_t launch_t128_outlier_pass<2>(int, bool, const EncodeArgs&, hipStream_t);
 
 static hipError_t launch_t128_b(int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
   switch (bits * 2 + (sym ? 1 : 0)) {

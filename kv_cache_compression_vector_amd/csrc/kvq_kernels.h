@@ -111,6 +111,10 @@ int64_t scan_partials(int64_t n);
 hipError_t launch_encode_outliers3(int m, int bits, bool sym, const EncodeArgs& a, uint32_t* part,
                                    hipStream_t st);
 hipError_t launch_encode_mx(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
+// The coded-length-128 outlier passes on the matrix-core encode: OL = 1 records + per-vector
+// counts into ol_off, OL = 2 (after the scan) the entries.
+template <int OL>
+hipError_t launch_t128_outlier_pass(int bits, bool sym, const EncodeArgs& a, hipStream_t st);
 bool pca_shape_supported(int D, int r);
 hipError_t launch_encode_pca(int D, int r, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
 hipError_t launch_decode_pca(int D, int r, int bits, bool bf16_out, const DecodeArgs& a,
