@@ -111,16 +111,30 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 
 }  // namespace
 
-template <int M, int BITS, bool BF16>
+// With OL, the vector's outlier entries [kakeyaturbo PR #15, calibrated Lloyd-Max + outlier
+// commit: sparse (index, value) overrides of the scaled residual] replace their coordinates'
+// centroids before the rotation. Element e of lane (q, vector) in block ab is coordinate
+// i = 32 ab + 8 (e % 4) + 2 q + e / 4, so an entry belongs to lane group q = (i % 8) / 2 at slot
+// 8 ab + e; each lane scans its vector's entries into a per-lane LDS slot row and a slot mask,
+// and merges the flagged slots into its B operands (bf16 value as the hi half, lo half 0).
+template <int M, int BITS, bool BF16, bool OL = false>
 __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
   constexpr int NB = M / 32, NWC = (M / 32) * BITS, NWT = NWC + 1;
   constexpr int C = dh_copies<BITS>(), NPAIR = 1 << (2 * BITS);
+  constexpr int NS = 8 * NB;  // override slots per lane (coordinates of its group)
   __shared__ uint32_t lut[2 * NPAIR * C];
   // bf16 rows of a wave's step (16 kDhVT rows of M bf16 = M/8 16-byte chunks, chunk index
   // XOR-swizzled with the row so the row-wise writes and chunk-wise reads spread over banks)
   constexpr int RCH = M / 8;
   __shared__ uint4 stage[BF16 ? kDhWaves * 16 * kDhVT * RCH : 1];
+  // override values: with bf16 rows they live in the last tile's row slice of the wave's stage
+  // (16 rows of M bf16 = 64 lanes x NS bf16), free until that tile's rows are assembled
+  __shared__ __attribute__((aligned(16))) uint16_t ov_own[(OL && !BF16) ? kDhWaves * 64 * NS : 8];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  uint16_t* const ovv =
+      (BF16 ? reinterpret_cast<uint16_t*>(stage + (wave * 16 * kDhVT + 16 * (kDhVT - 1)) * RCH)
+            : ov_own + wave * 64 * NS) + lane * NS;
+  static_assert(!OL || 16 * M * 2 == 64 * NS * 2, "override slots fill one tile's row slice");
   constexpr int RPK = 64 / RCH;  // rows per whole-row store instruction
   const int64_t lane_off = (int64_t)(lane / RCH) * a.ld + 8 * (lane % RCH);
   uint16_t* const ylast = static_cast<uint16_t*>(a.y) + (a.n - 1) * a.ld + 8 * (lane % RCH);
@@ -192,6 +206,23 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
     if (st + stride < n_steps) load(st + stride, wn);  // in flight during this step
 #pragma unroll
     for (int vt = 0; vt < kDhVT; ++vt) {
+      uint32_t ovm = 0;  // slots of this lane overridden by outlier entries
+      if constexpr (OL) {
+        // a lane past the end decodes the last record, whose row it stores again: with that
+        // record's entries, so the bytes are the same
+        int64_t v = st * 16 * kDhVT + 16 * vt + n16;
+        v = v < a.n ? v : a.n - 1;
+        int64_t k = a.ol_off[v], e = a.ol_off[v + 1];
+        if (e > a.ol_cap) e = a.ol_cap;
+        for (; k < e; ++k) {
+          const uint32_t i = static_cast<const uint8_t*>(a.ol_idx)[k];
+          if (i < (uint32_t)M && ((i & 7u) >> 1) == (uint32_t)q) {  // indices past m: ignored
+            const uint32_t slot = 8 * (i >> 5) + 4 * (i & 1u) + ((i & 31u) >> 3);
+            ovv[slot] = a.ol_val[k];
+            ovm |= 1u << slot;
+          }
+        }
+      }
       floatx4 y[NB][2];
 #pragma unroll
       for (int ab = 0; ab < NB; ++ab) {
@@ -204,6 +235,20 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
             const uint32_t off = pair_word<BITS, C>(yb, 2 * s) + (lane & (C - 1));
             hi[2 * half + s] = lut[off];
             lo[2 * half + s] = lut[NPAIR * C + off];
+          }
+        }
+        if constexpr (OL) {
+          const uint32_t mab = (ovm >> (8 * ab)) & 0xFFu;
+          if (mab != 0u) {
+            const uint4 ov = *reinterpret_cast<const uint4*>(ovv + 8 * ab);
+            const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {  // word w4 holds elements 2 w4 (low), 2 w4 + 1
+              const uint32_t msk = (((mab >> (2 * w4)) & 1u) ? 0x0000FFFFu : 0u) |
+                                   (((mab >> (2 * w4 + 1)) & 1u) ? 0xFFFF0000u : 0u);
+              hi[w4] = (hi[w4] & ~msk) | (ow[w4] & msk);
+              lo[w4] &= ~msk;
+            }
           }
         }
         const uint4 bh = make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -528,14 +573,14 @@ static int dh_device_cus() {
   return cus[dev];
 }
 
-// Blocks of k_decode_h<M, BITS, BF16> that one compute unit holds at once (registers and LDS:
-// the bf16 staging and the pair table leave 3 blocks at b = 3, 4 at b <= 2).
-template <int M, int BITS, bool BF16>
+// Blocks of k_decode_h<M, BITS, BF16, OL> that one compute unit holds at once (registers and
+// LDS: the bf16 staging and the pair table leave 3 blocks at b = 3, 4 at b <= 2).
+template <int M, int BITS, bool BF16, bool OL>
 static int dh_blocks_per_cu() {
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_h<M, BITS, BF16>, 64 * kDhWaves, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_h<M, BITS, BF16, OL>, 64 * kDhWaves, 0) !=
             hipSuccess || nb <= 0)
       nb = 1;
     per_cu = nb < 4 ? nb : 4;
@@ -543,20 +588,25 @@ static int dh_blocks_per_cu() {
   return per_cu;
 }
 
-template <int M, int BITS>
-static hipError_t launch_dh_t(bool bf16, const DecodeArgs& a, hipStream_t st) {
+template <int M, int BITS, bool BF16, bool OL>
+static hipError_t launch_dh_k(const DecodeArgs& a, hipStream_t st) {
   // exactly one resident round (at most 4 blocks of 4 waves per compute unit, measured best
   // against 2 and 8), waves striding over the steps: a grid beyond what the chip holds at once
   // would leave its last blocks to run alone on part of the chip
   const int64_t steps = (a.n + 16 * kDhVT - 1) / (16 * kDhVT);
   int64_t blocks = (steps + kDhWaves - 1) / kDhWaves;
-  const int per_cu = bf16 ? dh_blocks_per_cu<M, BITS, true>() : dh_blocks_per_cu<M, BITS, false>();
-  const int64_t resident = (int64_t)per_cu * dh_device_cus();
+  const int64_t resident = (int64_t)dh_blocks_per_cu<M, BITS, BF16, OL>() * dh_device_cus();
   if (blocks > resident) blocks = resident;
-  const dim3 g((unsigned)blocks), b(64 * kDhWaves);
-  if (bf16) hipLaunchKernelGGL((k_decode_h<M, BITS, true>), g, b, 0, st, a);
-  else hipLaunchKernelGGL((k_decode_h<M, BITS, false>), g, b, 0, st, a);
+  hipLaunchKernelGGL((k_decode_h<M, BITS, BF16, OL>), dim3((unsigned)blocks), dim3(64 * kDhWaves), 0,
+                     st, a);
   return hipGetLastError();
+}
+
+template <int M, int BITS>
+static hipError_t launch_dh_t(bool bf16, const DecodeArgs& a, hipStream_t st) {
+  const bool ol = a.ol_off != nullptr;
+  if (bf16) return ol ? launch_dh_k<M, BITS, true, true>(a, st) : launch_dh_k<M, BITS, true, false>(a, st);
+  return ol ? launch_dh_k<M, BITS, false, true>(a, st) : launch_dh_k<M, BITS, false, false>(a, st);
 }
 
 template <int D, int R, int BITS>
@@ -614,7 +664,10 @@ static hipError_t launch_dh_m(int bits, bool bf16, const DecodeArgs& a, hipStrea
   return hipErrorInvalidValue;
 }
 
-bool decode_h_supported(int D, int m, bool outliers) { return !outliers && D == m && (m == 64 || m == 128); }
+bool decode_h_supported(int D, int m, bool outliers) {
+  (void)outliers;  // outlier lists are merged into the B operands (one-byte indices at m <= 128)
+  return D == m && (m == 64 || m == 128);
+}
 
 hipError_t launch_decode_h(int m, int bits, bool bf16, const DecodeArgs& a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;

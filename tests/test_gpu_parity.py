@@ -222,6 +222,29 @@ def test_outlier_parity(D, bits, T_):
     compare_decoded(y.cpu().numpy(), yref, unpack_records(recn, D, bits)[1], "outlier decode")
 
 
+@pytest.mark.parametrize("D,bits,n", [(128, 2, 1000 + 7), (64, 3, 999), (128, 3, 33)])
+def test_outlier_decode_bf16_rows_with_a_ragged_tail(D, bits, n):
+    """Decode with side lists to bf16 rows when n is not a multiple of the kernel's 32-vector
+    step: the lanes past the end decode the last record again and store its row again, so they
+    must apply that record's entries too (the last row must equal the oracle's)."""
+    x = _rows(n, D, seed=3 * D + bits + n)
+    x[:, 5] *= 12  # heavy channel: many entries per vector, the last included
+    codec = kvq.Codec(D, bits, seed=11, outlier_T=1.5)
+    ol = kvq.Outliers(codec, n, capacity=n * D // 2, device=DEV)
+    say(f"outlier decode bf16 D={D} b={bits} n={n}")
+    rec, total = kvq.encode(codec, x, outliers=ol, want_total=True)
+    recn = rec.cpu().numpy()
+    off = ol.offsets.cpu().numpy().view(np.uint32)
+    idx = ol.idx.cpu().numpy()
+    val = ol.val.cpu().numpy().view(np.uint16)
+    assert off[-1] - off[-2] > 0, "the last vector carries entries"
+    y = kvq.decode(codec, rec, outliers=ol, dtype=torch.bfloat16)
+    y32 = y.float().cpu().numpy()
+    yref = oracle.decode(oracle_codec_like(codec), recn, off, idx[:total], val[:total])
+    compare_decoded(y32, yref, unpack_records(recn, D, bits)[1], "outlier decode (bf16)",
+                    extra_ulp_bf16=True)
+
+
 def test_outlier_capacity_overflow_reports_and_truncates():
     D, bits, n = 128, 2, 2000
     codec = kvq.Codec(D, bits, seed=5, outlier_T=1.0)
