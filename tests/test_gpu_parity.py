@@ -152,6 +152,46 @@ def test_score_packed_parity(D, bits, G):
     assert np.all(err <= bound), f"score error {err.max():.3g} (bound min {bound.min():.3g})"
 
 
+@pytest.mark.parametrize("T", [1, 15, 16, 63, 64, 255, 256, 257, 1000])
+def test_score_packed_ragged_lengths_and_strides(T):
+    """Every context length against the kernel's 16-token tiles, 64-token wave steps and
+    256-token segments, with padded record and score layouts (rec_sh = T + 5, rec_sb with 7
+    spare records; s_sh = T + 9, s_sb with 3 spare floats): scores within the normwise bar of the
+    oracle, and no score slot outside [0, T) of each row written."""
+    D, bits, G, B, Hkv = 128, 3, 2, 2, 3
+    Hq = Hkv * G
+    codec = kvq.Codec(D, bits, seed=23)
+    rec_sh, rec_sb = T + 5, Hkv * (T + 5) + 7
+    s_sh, s_sb = T + 9, Hq * (T + 9) + 3
+    k = _rows(B * rec_sb, D, seed=T + 77)
+    rec = kvq.encode(codec, k)
+    q = _rows(B * Hq, D, seed=T + 78).view(B, Hq, D)
+    say(f"score ragged T={T} B={B} Hkv={Hkv} G={G}")
+    SENT = 12345.0
+    buf = torch.full((B * s_sb,), SENT, dtype=torch.float32, device=DEV)
+    out = torch.as_strided(buf, (B, Hq, T), (s_sb, s_sh, 1))
+    kvq.score_packed(codec, q, rec, Hkv, T, rec_sb=rec_sb, rec_sh=rec_sh, out=out)
+    torch.cuda.synchronize()
+    hb = buf.cpu().numpy()
+    written = np.zeros(B * s_sb, bool)
+    for b_ in range(B):
+        for h in range(Hq):
+            written[b_ * s_sb + h * s_sh: b_ * s_sb + h * s_sh + T] = True
+    assert np.all(hb[~written] == SENT), "a score slot outside [0, T) was written"
+    s = out.cpu().numpy()
+    rec_h = rec.cpu().numpy()
+    oc = oracle_codec_like(codec)
+    q_h = bf16_host(q)
+    for b_ in range(B):
+        for h in range(Hq):
+            kv = h // G
+            rows = b_ * rec_sb + kv * rec_sh + np.arange(T)
+            recs = rec_h[rows]
+            ref = oracle.score(oc, np.repeat(q_h[b_, h][None], T, axis=0), recs)
+            check_scores(s[b_, h], ref, score_scale(oc, np.repeat(q_h[b_, h][None], T, axis=0), recs),
+                         f"score T={T} b={b_} h={h}")
+
+
 @pytest.mark.parametrize("cscale", [2.0 ** -30, 1.0, 2.0 ** 30])
 def test_score_packed_query_and_table_scales(cscale):
     """The score's f16 products hold each query head and the centroid table scaled by powers of
