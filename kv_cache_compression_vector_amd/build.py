@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 OBJ = os.path.join(HERE, "_obj")
-SOURCES = ["kvq_host.cpp", "kvq_encode.hip", "kvq_encode_mx.hip", "kvq_decode.hip",
+SOURCES = ["kvq_host.cpp", "kvq_encode.hip", "kvq_encode_mx.hip", "kvq_encode_kron.hip",
+           "kvq_decode.hip",
            "kvq_decode_h.hip", "kvq_score.hip", "kvq_pca.hip", "kvq_misc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -27,7 +28,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 # quantiser or the softmax reads every one of them (accumulator registers would cost a move
 # each), and the unified register file then holds two attention waves per SIMD.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
-EXTRA = {"kvq_encode_mx.hip": _VGPR_FORM, "kvq_decode_h.hip": _VGPR_FORM, "kvq_score.hip": _VGPR_FORM}
+EXTRA = {"kvq_encode_mx.hip": _VGPR_FORM, "kvq_encode_kron.hip": _VGPR_FORM, "kvq_decode_h.hip": _VGPR_FORM, "kvq_score.hip": _VGPR_FORM}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -431,6 +431,7 @@ static hipError_t launch_evict_m(int bits, bool sym, const EvictArgs& a, hipStre
 }
 
 hipError_t launch_evict(int m, int bits, bool sym, const EvictArgs& a, hipStream_t st) {
+  if (encode_kron_supported(m)) return launch_evict_kron(m, bits, sym, a, st);
   switch (m) {
     case 64: return launch_evict_m<64>(bits, sym, a, st);
     case 128: return launch_evict_m<128>(bits, sym, a, st);
@@ -589,6 +590,7 @@ static hipError_t launch_encode_m(int bits, bool sym, const EncodeArgs& a, hipSt
 hipError_t launch_encode(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
   // a scale rule needs the chosen centroids, which the lane-per-vector kernel forms
   if (a.scale_rule == 0 && encode_mx_supported(m)) return launch_encode_mx(m, bits, sym, a, st);
+  if (a.scale_rule == 0 && encode_kron_supported(m)) return launch_encode_kron(m, bits, sym, a, st);
   switch (m) {
     case 32: return launch_encode_m<32>(bits, sym, a, st);
     case 64: return launch_encode_m<64>(bits, sym, a, st);

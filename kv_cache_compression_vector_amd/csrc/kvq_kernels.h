@@ -111,6 +111,11 @@ int64_t scan_partials(int64_t n);
 hipError_t launch_encode_outliers3(int m, int bits, bool sym, const EncodeArgs& a, uint32_t* part,
                                    hipStream_t st);
 hipError_t launch_encode_mx(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
+// Coded length 256 and 512: the rotation's 32-point blocks on the matrix cores (no outlier list,
+// no scale rule), for plain encode and for eviction.
+bool encode_kron_supported(int m);
+hipError_t launch_encode_kron(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
+hipError_t launch_evict_kron(int m, int bits, bool sym, const EvictArgs& a, hipStream_t st);
 // The coded-length-128 outlier passes on the matrix-core encode: OL = 1 records + per-vector
 // counts into ol_off, OL = 2 (after the scan) the entries.
 template <int OL>
