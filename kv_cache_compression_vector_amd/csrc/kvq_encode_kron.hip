@@ -81,8 +81,11 @@ struct QuantBS {
 #pragma unroll
       for (int lv = 0; lv < LVL; ++lv) {
         const int cnt = (1 << (LVL - lv)) - 1, mid = cnt / 2;
+        // the decision bit is the sign of (threshold - a) (a zero difference is +0: not
+        // greater), shifted in with one alignbit; a compare only where a select follows
+        w[LVL - 1 - lv] = shift_in_sign(w[LVL - 1 - lv], s[mid] - a);
+        if (mid == 0) continue;
         const bool c = a > s[mid];
-        w[LVL - 1 - lv] = w[LVL - 1 - lv] + w[LVL - 1 - lv] + (c ? 1u : 0u);
 #pragma unroll
         for (int k = 0; k < mid; ++k) {
           // both candidates as opaque register values: a select of two array elements would be
@@ -110,6 +113,10 @@ struct QuantBS {
     }
   }
 };
+
+__device__ __forceinline__ uint4 neg_bf16(const uint4& a) {
+  return make_uint4(a.x ^ 0x80008000u, a.y ^ 0x80008000u, a.z ^ 0x80008000u, a.w ^ 0x80008000u);
+}
 
 // A_t for lane l: row r = l % 16, inputs k = 8 (l / 16) + e; entry (-1)^popcount(lo(t, r) & k).
 __device__ __forceinline__ uint4 kron_fragment(int t, int l) {
@@ -140,28 +147,45 @@ __device__ __forceinline__ void kron_tile(const Tables& tab, const uint4 (&A)[2]
   // output halves per pass: both at m = 256; one at a time at m = 512 (64 accumulators live,
   // the operands read from LDS again for the second half)
   constexpr int TP = O > 8 ? 1 : 2;
+  // top bits of the block index o whose butterfly stages run on the matrix cores (one fewer at
+  // m = 512 for general tables of 3 and 4 bits, whose 7 or 15 thresholds need the registers)
+  constexpr int FB = O > 8 && (SYM || BITS < 3) ? 2 : 1, NH = 1 << FB, NL = O / NH;
+  const uint4 AN[2] = {neg_bf16(A[0]), neg_bf16(A[1])};
   constexpr int LV = QuantBS<BITS, SYM>::LVL > 0 ? QuantBS<BITS, SYM>::LVL : 1;
   uint32_t* rec = rec_lds + v * NWT;
   uint32_t pl[2][O / 8][BITS];  // plane words of word group (4 t + g) m/256 + oh
   float n = 0.0f;
 #pragma unroll
   for (int t0 = 0; t0 < 2; t0 += TP) {
-    // Y[o] for the pass's output halves; in the first pass also the norm's sum of squares
+    // Y[o] for the pass's output halves, with the transform's stages over the top FB bits of o
+    // taken in the accumulation (acc[o] = sum_o' +-A Y-operand[o'] over the o' that differ from
+    // o in those bits only); in the first pass also the norm's sum of squares
     floatx4 acc[TP][O];
     float ss = 0.0f;
 #pragma unroll
-    for (int o = 0; o < O; ++o) {
-      const uint4 X = reg[swz<CH>(v, 4 * o + g)];
-      if (t0 == 0) {
-        const uint32_t xw[4] = {X.x, X.y, X.z, X.w};
+    for (int ol = 0; ol < NL; ++ol) {
+      uint4 X[NH];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xw[e]),
-                                               __builtin_bit_cast(bf16x2_t, xw[e]), ss, false);
+      for (int oh = 0; oh < NH; ++oh) {
+        X[oh] = reg[swz<CH>(v, 4 * (oh * NL + ol) + g)];
+        if (t0 == 0) {
+          const uint32_t xw[4] = {X[oh].x, X[oh].y, X[oh].z, X[oh].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xw[e]),
+                                                 __builtin_bit_cast(bf16x2_t, xw[e]), ss, false);
+        }
       }
-      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int tt = 0; tt < TP; ++tt) acc[tt][o] = mfma_bf16(A[t0 + tt], X, z);
+      for (int tt = 0; tt < TP; ++tt)
+#pragma unroll
+        for (int oh = 0; oh < NH; ++oh) {
+          floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int oi = 0; oi < NH; ++oi)
+            c = mfma_bf16((__builtin_popcount(oh & oi) & 1) ? AN[t0 + tt] : A[t0 + tt], X[oi], c);
+          acc[tt][oh * NL + ol] = c;
+        }
     }
     if (t0 == 0) {
       ss += __shfl_xor(ss, 16, 64);
@@ -189,9 +213,9 @@ __device__ __forceinline__ void kron_tile(const Tables& tab, const uint4 (&A)[2]
         n = bad ? __builtin_amdgcn_sqrtf(s2) * pow2f(ex) : n;
       }
     }
-    // the O-point transform over the blocks, in place
+    // the rest of the O-point transform over the blocks (the low bits of o), in place
 #pragma unroll
-    for (int h = 1; h < O; h <<= 1)
+    for (int h = 1; h < NL; h <<= 1)
 #pragma unroll
       for (int o = 0; o < O; ++o)
         if ((o & h) == 0)
@@ -213,9 +237,13 @@ __device__ __forceinline__ void kron_tile(const Tables& tab, const uint4 (&A)[2]
 #pragma unroll
         for (int p = 0; p < LV; ++p) w[p] = 0u;
 #pragma unroll
-        for (int o = 8 * oh + 7; o >= 8 * oh; --o)
+        for (int o = 8 * oh + 7; o >= 8 * oh; --o) {
 #pragma unroll
           for (int i = 3; i >= 0; --i) q.push(acc[tt][o][i], w, sgn);
+          // general tables of 3 and 4 bits: a few coordinates' searches at a time (scheduled
+          // wide, their candidate thresholds exhaust the registers)
+          if constexpr (!SYM && BITS >= 3) __builtin_amdgcn_sched_barrier(0);
+        }
         q.planes(w, sgn, pl[t0 + tt][oh]);
       }
   }
@@ -310,7 +338,8 @@ void k_encode_kron(EncodeArgs a) {
   using K = KR<M>;
   constexpr int NWT = (M / 32) * BITS + 1;
   __shared__ uint4 s_reg[K::WAVES * 16 * K::CH];
-  const int ln = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index as a scalar: tile indices, cache lookups and row bases stay wave-uniform
+  const int ln = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint4* reg = s_reg + wave * 16 * K::CH;
   const uint4 A[2] = {kron_fragment(0, ln), kron_fragment(1, ln)};
   const uint4 sm = kron_signs<M>(a.tab, ln);
@@ -352,7 +381,8 @@ void k_evict_kron(EvictArgs a) {
   using K = KR<M>;
   constexpr int NWT = (M / 32) * BITS + 1;
   __shared__ uint4 s_reg[K::WAVES * 16 * K::CH];
-  const int ln = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index as a scalar: tile indices, cache lookups and row bases stay wave-uniform
+  const int ln = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint4* reg = s_reg + wave * 16 * K::CH;
   const uint4 A[2] = {kron_fragment(0, ln), kron_fragment(1, ln)};
   const uint4 sm = kron_signs<M>(a.tab, ln);
