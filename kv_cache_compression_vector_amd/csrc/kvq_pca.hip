@@ -353,6 +353,265 @@ void k_encode_pq(EncodeArgs a, int64_t tiles_per_block) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Encode at r = 128 (D = 128, 256): the projection formed transposed, U^T = (s (.) B^T) x^T, as
+// the Hadamard encode at m = 128 forms its rotation, so that each lane ends with one whole
+// record word group of one vector. Row m of m-tile mt is projected coordinate
+// j = 8 (4 (mt mod 4) + i) + 2 g + (mt >> 2) for m = 4 g + i; lane l = 16 g + v then holds the
+// 32 coordinates of vector v whose index bits 1, 2 equal g, at plane positions 32 g + 4 mt + i.
+// The Sylvester rotation over the projected coordinates is five butterfly stages in registers
+// (index bits 0, 3..6: the bits of mt and i) and two across the lane groups (bits 1, 2: lanes
+// l ^ 16, l ^ 32); then the quantiser packs the lane's words with no other lane. No f32 staging
+// region: LDS holds the sign-folded basis (D r bf16), the mean term and each wave's records.
+constexpr int kPtWaves = 4;
+// 16-row MFMA column tiles per wave tile (two, sharing each basis read, measured no faster: the
+// kernel is bound by vector-ALU issue, not by the basis reads from LDS)
+constexpr int kPtRT = 1;
+
+// Projected coordinate of row m of m-tile mt.
+__host__ __device__ constexpr int pt_coord(int mt, int m) {
+  return 8 * (4 * (mt & 3) + (m & 3)) + 2 * (m >> 2) + (mt >> 2);
+}
+
+// LDS place (uint4) of chunk c of basis column j: the XOR key (j >> 1) mod 16 gives the 16
+// columns of one m-tile's A operand (index bits 1..4 varying) 16 distinct bank groups.
+template <int BCH>
+__device__ __forceinline__ int pt_swz(int j, int c) { return j * BCH + (c ^ ((j >> 1) & 15)); }
+
+template <int D, int BITS, bool SYM>
+__global__ __launch_bounds__(64 * kPtWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void k_encode_pt(EncodeArgs a, int64_t tiles_per_block) {
+  constexpr int R = 128, BCH = D / 8, KS = D / 32, NMT = R / 16;
+  constexpr int RT = kPtRT, ROWS = 16 * RT;
+  constexpr int NWC = (R / 32) * BITS, NWT = NWC + 1, TILE = ROWS * kPtWaves;
+  __shared__ uint4 s_bT[R * BCH];
+  __shared__ float4 s_mp[NMT * 4];  // -(s (.) B^T mu) at (mt, g): coordinates pt_coord(mt, 4 g + i)
+  __shared__ float s_mu[D];
+  __shared__ uint32_t s_rec[kPtWaves][ROWS * NWT];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), ln = tid & 63;
+  const int v = ln & 15, g = ln >> 4;
+  uint32_t* rec_lds = s_rec[wave];
+  int cur = -1;
+  const int64_t n_tiles = (a.n + TILE - 1) / TILE;
+  const int64_t t0 = blockIdx.x * tiles_per_block;
+  const int64_t t1 = t0 + tiles_per_block < n_tiles ? t0 + tiles_per_block : n_tiles;
+  // B operands: row 16 wave + v of the tile, chunk 4 ks + g (rows past the end repeat the last)
+  auto load_x = [&](int64_t tile, uint4 (&dst)[RT][KS]) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      int64_t row = tile * TILE + ROWS * wave + 16 * rt + v;
+      row = row < a.n ? row : a.n - 1;
+      const uint4* src = reinterpret_cast<const uint4*>(a.x + row * a.ld) + g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dst[rt][ks] = src[4 * ks];
+    }
+  };
+  uint4 nxt[RT][KS];
+  if (t0 < t1) load_x(t0, nxt);
+  for (int64_t tile = t0; tile < t1; ++tile) {
+    const int bi = basis_of_row(a.pca, tile * TILE);  // block tiles never straddle basis blocks
+    if (bi != cur) {
+      __syncthreads();
+      const uint16_t* Bk = a.pca.basis + (int64_t)bi * D * R;
+      uint16_t* bt16 = reinterpret_cast<uint16_t*>(s_bT);
+      if ((reinterpret_cast<uintptr_t>(Bk) & 15) == 0) {  // 16-byte pieces: 8 columns of one row d
+        for (int e8 = tid; e8 < D * R / 8; e8 += 64 * kPtWaves) {
+          const int d = e8 / (R / 8), j0 = 8 * (e8 % (R / 8));
+          const uint4 w = *reinterpret_cast<const uint4*>(Bk + (int64_t)d * R + j0);
+          // the sign masks of columns j0 .. j0 + 7 are the pair words j0/2 .. j0/2 + 3 (bits 15, 31)
+          const uint32_t f[4] = {w.x ^ a.tab.sign_pairs[j0 / 2], w.y ^ a.tab.sign_pairs[j0 / 2 + 1],
+                                 w.z ^ a.tab.sign_pairs[j0 / 2 + 2], w.w ^ a.tab.sign_pairs[j0 / 2 + 3]};
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            bt16[pt_swz<BCH>(j0 + t, d / 8) * 8 + d % 8] = (uint16_t)(f[t >> 1] >> (16 * (t & 1)));
+        }
+      } else {
+        for (int e = tid; e < D * R; e += 64 * kPtWaves) {
+          const int d = e / R, j = e % R;
+          const uint32_t flip = (a.tab.sign_pairs[j >> 1] >> (16 * (j & 1))) & 0x8000u;
+          bt16[pt_swz<BCH>(j, d / 8) * 8 + d % 8] = (uint16_t)(Bk[e] ^ flip);
+        }
+      }
+      const float* mu = a.pca.mean ? a.pca.mean + (int64_t)bi * D : nullptr;
+      for (int d = tid; d < D; d += 64 * kPtWaves) s_mu[d] = mu ? mu[d] : 0.0f;
+      __syncthreads();
+      // -(s (.) B^T mu)_j: two threads per column, halves of the column summed
+      {
+        const int j = tid >> 1, part = tid & 1;
+        float acc = 0.0f;
+        for (int c = part * (BCH / 2); c < (part + 1) * (BCH / 2); ++c) {
+          const uint4 w = s_bT[pt_swz<BCH>(j, c)];
+          const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc = fmaf(bf16lo_to_f32(u[e]), s_mu[8 * c + 2 * e], acc);
+            acc = fmaf(bf16hi_to_f32(u[e]), s_mu[8 * c + 2 * e + 1], acc);
+          }
+        }
+        acc += __shfl_xor(acc, 1, 64);
+        // coordinate j sits at (mt, g, i) with j = pt_coord(mt, 4 g + i)
+        const int mt = 4 * (j & 1) + (j >> 5), gg = (j >> 1) & 3, i = (j >> 3) & 3;
+        if (part == 0) reinterpret_cast<float*>(s_mp)[(4 * mt + gg) * 4 + i] = -acc;
+      }
+      __syncthreads();
+      cur = bi;
+    }
+    const int64_t rw0 = tile * TILE + ROWS * wave;
+    uint4 X[RT][KS];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) X[rt][ks] = nxt[rt][ks];
+    if (tile + 1 < t1) load_x(tile + 1, nxt);  // in flight while this tile computes
+    // the projection: accs[rt][mt][i] = y_j, j = pt_coord(mt, 4 g + i), of vector 16 rt + v
+    floatx4 accs[RT][NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const float4 m0 = s_mp[4 * mt + g];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) accs[rt][mt] = floatx4{m0.x, m0.y, m0.z, m0.w};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const uint4 A = s_bT[pt_swz<BCH>(pt_coord(mt, ln & 15), 4 * ks + (ln >> 4))];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) accs[rt][mt] = mfma_bf16(A, X[rt][ks], accs[rt][mt]);
+      }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+    floatx4 (&acc)[NMT] = accs[rt];
+    // norm of the projected vector: this lane's 32 coordinates, summed over the 4 groups
+    float ss = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ss = fmaf(acc[mt][i], acc[mt][i], ss);
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    float n = __builtin_amdgcn_sqrtf(ss);
+    const bool bad = ss_out_of_range(ss);
+    if (wave_any(bad)) {  // rescaled sum of squares (kvq_device.h), wave-uniform
+      uint32_t mb = 0;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t m = __float_as_uint(acc[mt][i]) & 0x7FFFFFFFu;
+          mb = mb > m ? mb : m;
+        }
+      uint32_t ot = (uint32_t)__shfl_xor((int)mb, 16, 64);
+      mb = mb > ot ? mb : ot;
+      ot = (uint32_t)__shfl_xor((int)mb, 32, 64);
+      mb = mb > ot ? mb : ot;
+      const int ex = max_exp_of_bits(mb);
+      const float sc = pow2f(-ex);
+      float s2 = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y = acc[mt][i] * sc;
+          s2 = fmaf(y, y, s2);
+        }
+      s2 += __shfl_xor(s2, 16, 64);
+      s2 += __shfl_xor(s2, 32, 64);
+      n = bad ? __builtin_amdgcn_sqrtf(s2) * pow2f(ex) : n;
+    }
+    // rotation: in-lane stages over the bits of i and mt, then the two lane-group bits
+#pragma unroll
+    for (int h = 1; h < 4; h <<= 1)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((i & h) == 0) {
+            const float x = acc[mt][i], y = acc[mt][i + h];
+            acc[mt][i] = x + y;
+            acc[mt][i + h] = x - y;
+          }
+#pragma unroll
+    for (int h = 1; h < NMT; h <<= 1)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        if ((mt & h) == 0)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = acc[mt][i], y = acc[mt + h][i];
+            acc[mt][i] = x + y;
+            acc[mt + h][i] = x - y;
+          }
+#pragma unroll
+    for (int gb = 1; gb < 4; gb <<= 1) {
+      const float sg = (g & gb) ? -1.0f : 1.0f;  // the upper lane of the pair takes a - b
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(acc[mt][i], sg, __shfl_xor(acc[mt][i], 16 * gb, 64));
+    }
+    // quantiser: plane bits t = 4 mt + i, pushed from t = 31 down
+    uint32_t pl[BITS];
+    {
+      const Quant<BITS, SYM> q(a.tab, n);
+      QuantAcc<BITS, SYM> qa;
+#pragma unroll
+      for (int mt = NMT - 1; mt >= 0; --mt)
+#pragma unroll
+        for (int i = 3; i >= 0; --i) qa.push(acc[mt][i], q);
+      qa.planes(q, 0xFFFFFFFFu, pl);
+    }
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) rec_lds[(16 * rt + v) * NWT + g * BITS + p] = pl[p];
+    if (g == 0) rec_lds[(16 * rt + v) * NWT + NWC] = __float_as_uint(n);
+    }
+    __builtin_amdgcn_wave_barrier();
+    {
+      constexpr int CH = ROWS * NWT / 4;  // 16-byte pieces of the wave tile's records
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(a.rec) + rw0 * NWT);
+      const uint4* src = reinterpret_cast<const uint4*>(rec_lds);
+      if (rw0 + ROWS <= a.n) {  // wave-uniform
+#pragma unroll
+        for (int k = 0; k < (CH + 63) / 64; ++k) {
+          const int id = k * 64 + ln;
+          if (id < CH) st_stream(dst + id, src[id]);
+        }
+      } else if (rw0 < a.n) {
+        const int valid_w = (int)(a.n - rw0) * NWT;  // words of whole valid records
+#pragma unroll
+        for (int k = 0; k < (CH + 63) / 64; ++k) {
+          const int id = k * 64 + ln;
+          if (4 * id + 4 <= valid_w) st_stream(dst + id, src[id]);
+        }
+        const int tw = valid_w % 4, w0 = valid_w - tw;  // a partial last piece, word by word
+        if (ln < tw) reinterpret_cast<uint32_t*>(a.rec)[rw0 * NWT + w0 + ln] = rec_lds[w0 + ln];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int D, int BITS, bool SYM>
+static hipError_t enc_pt_t(const EncodeArgs& a, hipStream_t st) {
+  constexpr int TILE = 16 * kPtRT * kPtWaves;
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_encode_pt<D, BITS, SYM>, 64 * kPtWaves, 0) !=
+            hipSuccess || nb <= 0)
+      nb = 1;
+    return nb;
+  }();
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t tiles = (a.n + TILE - 1) / TILE;
+  const int64_t resident = (int64_t)per_cu * cus;
+  const int64_t per = (tiles + resident - 1) / resident;
+  hipLaunchKernelGGL((k_encode_pt<D, BITS, SYM>), dim3((unsigned)((tiles + per - 1) / per)),
+                     dim3(64 * kPtWaves), 0, st, a, per);
+  return hipGetLastError();
+}
+
 template <int D, int BITS, bool SYM>
 static hipError_t enc_pq_t(const EncodeArgs& a, hipStream_t st) {
   const int64_t tiles = (a.n + kPqTile - 1) / kPqTile;
@@ -517,6 +776,7 @@ static PcaGrid pca_grid(int64_t n) {
 template <int D, int R, int BITS, bool SYM>
 static hipError_t enc_t(const EncodeArgs& a, hipStream_t st) {
   if constexpr (R == 64 && D <= 128) return enc_pq_t<D, BITS, SYM>(a, st);
+  if constexpr (R == 128) return enc_pt_t<D, BITS, SYM>(a, st);
   const PcaGrid g = pca_grid<D, R>(a.n);
   hipLaunchKernelGGL((k_encode_pca<D, R, BITS, SYM>), dim3(g.blocks), dim3(64 * PcaShape<D, R>::W), 0, st,
                      a, g.per_block);

@@ -116,7 +116,7 @@ def _pca_fit(D, r, seed, mean_shift=None):
     return mu, basis
 
 
-@pytest.mark.parametrize("D,r", [(128, 64), (256, 64), (128, 32)])
+@pytest.mark.parametrize("D,r", [(128, 64), (256, 64), (128, 32), (128, 128), (256, 128)])
 @pytest.mark.parametrize("k", EXPS)
 def test_projection_rows_across_the_bf16_range(D, r, k):
     """Rows and mean scaled together by 2^k: the projected vector scales by 2^k exactly."""
@@ -161,7 +161,7 @@ def test_eviction_across_the_bf16_range(k):
 
 
 @pytest.mark.parametrize("ratio", [4.0, 16.0])
-@pytest.mark.parametrize("D,r", [(128, 64), (256, 64), (128, 32)])
+@pytest.mark.parametrize("D,r", [(128, 64), (256, 64), (128, 32), (128, 128)])
 def test_projection_with_a_dominant_mean(D, r, ratio):
     """Rows x = mu + e with ||mu|| = ratio * ||e|| (keys with large channel biases): the kernel's
     f32 B^T x - B^T mu cancels most of its magnitude; codes, decode and scores must still meet
@@ -206,7 +206,8 @@ def _offset_view(n, rb, offset):
     return buf, v
 
 
-@pytest.mark.parametrize("D,bits,r", [(128, 3, 0), (64, 2, 0), (256, 2, 0), (512, 4, 0), (128, 3, 64)])
+@pytest.mark.parametrize("D,bits,r", [(128, 3, 0), (64, 2, 0), (256, 2, 0), (512, 4, 0), (128, 3, 64),
+                                       (128, 3, 128)])
 def test_records_four_byte_aligned(D, bits, r):
     """Records at 4 and 8 bytes past a 16-byte boundary encode, decode and score to the same
     bytes and values as aligned ones."""
