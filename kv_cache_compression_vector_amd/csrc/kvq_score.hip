@@ -31,6 +31,26 @@ __device__ __forceinline__ floatx4_t mfma16(const uint4& a, const uint4& b, floa
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Max / sum over the 16 lanes of a DPP row (quad swaps, then half-row and row mirrors: each step
+// pairs every lane with one of the other half it has not yet combined with); every lane of the
+// row gets the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f32<0x141>(x));  // row_half_mirror
+  return fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x141>(x);
+  return x + dpp_f32<0x140>(x);
+}
+
 // bf16 hi + lo of an f32 (both round to nearest even): hi + lo = x to ~2^-17 relative.
 __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
   hi = f32_to_bf16_rne(x);
@@ -636,6 +656,10 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
   float qm[4], qsc[4], mrun[4], lrun[4];  // q . mu, product scale, softmax state of heads 4 oct + kk
   const float cpow = table_pow<BK>(k.tab);
   const uint32_t sel01 = planes_sel01(oct), sel2 = planes_sel2(oct);
+  // V gather: rotation that brings bit tok (and 16 + tok) of a plane word to slot sl (16 + sl)
+  uint32_t vrot[2 * BV];
+#pragma unroll
+  for (int sl = 0; sl < 2 * BV; ++sl) vrot[sl] = (uint32_t)(tok - sl) & 31u;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     mrun[kk] = -INFINITY;
@@ -730,21 +754,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
       const float nv1 = __uint_as_float(vst[wave][(16 + tok) * NWV + NWV - 1]) * a.tv.inv_m;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        float mx = fmaxf(lg[0][kk], lg[1][kk]);
-        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
+        const float mx = row16_max(fmaxf(lg[0][kk], lg[1][kk]));
         const float mn = fmaxf(mrun[kk], mx);
         // mn = -inf: no token of this head so far (or a head slot >= G); nothing to rescale
         const float corr = mn == -INFINITY ? 1.0f : __expf(mrun[kk] - mn);
         const float p0 = lg[0][kk] == -INFINITY ? 0.0f : __expf(lg[0][kk] - mn);
         const float p1 = lg[1][kk] == -INFINITY ? 0.0f : __expf(lg[1][kk] - mn);
-        float ps = p0 + p1;
-        ps += __shfl_xor(ps, 1, 64);
-        ps += __shfl_xor(ps, 2, 64);
-        ps += __shfl_xor(ps, 4, 64);
-        ps += __shfl_xor(ps, 8, 64);
+        const float ps = row16_sum(p0 + p1);
         lrun[kk] = fmaf(lrun[kk], corr, ps);
         mrun[kk] = mn;
         pst[wave][4 * oct + kk][tok] = p0 * nv0;
@@ -754,9 +770,18 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
       __builtin_amdgcn_wave_barrier();
       // B operand: weights of head tok for tokens 8 oct + [0, 8), bf16 hi and lo
       const float c = cst[wave][tok];
+      if (__ballot(c != 1.0f) != 0ull) {  // some head's running maximum moved (rare once settled)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) acc[ct] *= c;
-      uint4 bhi, blo;
+        for (int ct = 0; ct < CT; ++ct) acc[ct] *= c;
+      }
+      // B operands: the unit's weights of head tok for tokens 8 oct + [0, 8) as bf16 hi and lo.
+      // Interleaved form (low code widths): for A = {hi, lo, hi, lo} of two token pairs (an
+      // entry's two table words as one read returns them), bh[q] = {hi(pair 2q), hi(2q),
+      // hi(2q + 1), hi(2q + 1)} takes hi + lo of the centroids times hi of the weights and
+      // bl[q] = {lo(2q), 0, lo(2q + 1), 0} hi times lo. Otherwise A = all hi or all lo (fewer
+      // registers) with bhi, blo = the weights' hi and lo.
+      constexpr bool IL = BV <= 2 && BK <= 3;
+      uint4 bh[2], bl[2];
       {
         const float4 w0 = *reinterpret_cast<const float4*>(&pst[wave][tok][8 * oct]);
         const float4 w1 = *reinterpret_cast<const float4*>(&pst[wave][tok][8 * oct + 4]);
@@ -764,12 +789,28 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
         uint32_t hi[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) split_bf16(w[e], hi[e], lo[e]);
-        bhi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
-                         hi[6] | (hi[7] << 16));
-        blo = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
-                         lo[6] | (lo[7] << 16));
+        uint32_t hp[4], lp[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          hp[d] = hi[2 * d] | (hi[2 * d + 1] << 16);
+          lp[d] = lo[2 * d] | (lo[2 * d + 1] << 16);
+        }
+        if constexpr (IL) {
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            bh[qq] = make_uint4(hp[2 * qq], hp[2 * qq], hp[2 * qq + 1], hp[2 * qq + 1]);
+            bl[qq] = make_uint4(lp[2 * qq], 0u, lp[2 * qq + 1], 0u);
+          }
+        } else {
+          bh[0] = make_uint4(hp[0], hp[1], hp[2], hp[3]);  // bhi
+          bl[0] = make_uint4(lp[0], lp[1], lp[2], lp[3]);  // blo
+        }
       }
-      // A operands: centroids at position P = 32 g + 16 h2 + tok of tokens 8 oct + [0, 8)
+      // A operands: centroids at positions P = 32 g + 16 h2 + tok of tokens 8 oct + [0, 8). The
+      // pair index of tokens (2 e2, 2 e2 + 1) at both positions of a lane comes from one pass:
+      // plane p of token t of the pair is rotated so that its bits tok and 16 + tok land on
+      // slot 2 p + t and 16 + 2 p + t, the rotated words are merged by bit masks, and the two
+      // indices are the low and high 16-bit halves.
 #pragma unroll
       for (int g = 0; g < GV; ++g) {
         uint32_t wv[8][BV];
@@ -777,26 +818,39 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
         for (int e = 0; e < 8; ++e)
 #pragma unroll
           for (int p = 0; p < BV; ++p) wv[e][p] = vst[wave][(8 * oct + e) * NWV + g * BV + p];
+        uint32_t ah[2][4], al[2][4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          uint32_t y = 0u;  // only the placed slots' bits are set: each slot is one v_and_or
+#pragma unroll
+          for (int sl = 2 * BV - 1; sl >= 0; --sl) {
+            const uint32_t w = wv[2 * e2 + (sl & 1)][sl >> 1];
+            y |= __builtin_amdgcn_alignbit(w, w, vrot[sl]) & ((1u << sl) | (1u << (16 + sl)));
+          }
+          const uint32_t i0 = y & 0xFFFFu, i1 = y >> 16;
+          ah[0][e2] = lutv[i0 * CV + (lane & (CV - 1))];
+          al[0][e2] = lutv[(NPV + i0) * CV + (lane & (CV - 1))];
+          ah[1][e2] = lutv[i1 * CV + (lane & (CV - 1))];
+          al[1][e2] = lutv[(NPV + i1) * CV + (lane & (CV - 1))];
+        }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const int j = 16 * h2 + tok;
-          uint32_t ah[4], al[4];
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            uint32_t idx = 0;
-#pragma unroll
-            for (int p = 0; p < BV; ++p)
-              idx |= (__builtin_amdgcn_ubfe(wv[2 * e2][p], j, 1) << (2 * p)) |
-                     (__builtin_amdgcn_ubfe(wv[2 * e2 + 1][p], j, 1) << (2 * p + 1));
-            ah[e2] = lutv[idx * CV + (lane & (CV - 1))];
-            al[e2] = lutv[(NPV + idx) * CV + (lane & (CV - 1))];
-          }
-          const uint4 ahi = make_uint4(ah[0], ah[1], ah[2], ah[3]);
-          const uint4 alo = make_uint4(al[0], al[1], al[2], al[3]);
           floatx4_t& c4 = acc[2 * g + h2];
-          c4 = mfma16(ahi, bhi, c4);
-          c4 = mfma16(ahi, blo, c4);
-          c4 = mfma16(alo, bhi, c4);
+          if constexpr (IL) {
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+              const uint4 av = make_uint4(ah[h2][2 * qq], al[h2][2 * qq], ah[h2][2 * qq + 1],
+                                          al[h2][2 * qq + 1]);
+              c4 = mfma16(av, bh[qq], c4);
+              c4 = mfma16(av, bl[qq], c4);
+            }
+          } else {
+            const uint4 ahi = make_uint4(ah[h2][0], ah[h2][1], ah[h2][2], ah[h2][3]);
+            const uint4 alo = make_uint4(al[h2][0], al[h2][1], al[h2][2], al[h2][3]);
+            c4 = mfma16(ahi, bh[0], c4);
+            c4 = mfma16(ahi, bl[0], c4);
+            c4 = mfma16(alo, bh[0], c4);
+          }
         }
       }
       __builtin_amdgcn_wave_barrier();  // vst, pst and cst are refilled by the next unit

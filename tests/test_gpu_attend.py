@@ -48,7 +48,7 @@ def _check(kc, vc, q, krec, vrec, B, Hkv, T, scale, softcap, out, okc, ovc, head
 
 @pytest.mark.parametrize("D,kb,vb,G,T", [(128, 3, 2, 4, 1), (128, 3, 2, 4, 17), (128, 3, 2, 6, 300),
                                          (128, 2, 3, 8, 1000), (64, 4, 1, 1, 777),
-                                         (64, 1, 3, 2, 2049)])
+                                         (64, 1, 3, 2, 2049), (128, 4, 3, 8, 65), (128, 1, 1, 4, 333)])
 def test_attend_parity_hadamard(D, kb, vb, G, T):
     B, Hkv = 2, 2
     kc, vc = kvq.Codec(D, kb, seed=31), kvq.Codec(D, vb, seed=32)
