@@ -343,13 +343,29 @@ static hipError_t launch_outliers_m(int bits, bool sym, const EncodeArgs& a, uin
   return launch_emit_t<M>(a, st);
 }
 
+static int64_t align16(int64_t b) { return (b + 15) & ~int64_t(15); }
+
+int64_t outlier_stage_bytes(int m, int64_t n) {
+  if (m != 128 || n <= 0) return 0;
+  const int64_t tiles = (n + 15) / 16;
+  return align16(4 * tiles) + align16(kOutlierStage * tiles) + align16(2 * kOutlierStage * tiles) + 16;
+}
+
 hipError_t launch_encode_outliers3(int m, int bits, bool sym, const EncodeArgs& a, uint32_t* part,
                                    hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
-  if (m == 128) {  // both passes on the matrix-core rotation
-    hipError_t e = launch_t128_outlier_pass<1>(bits, sym, a, st);
-    if (e == hipSuccess) e = launch_offsets_scan(a.ol_off, a.n, part, st);
-    if (e == hipSuccess) e = launch_t128_outlier_pass<2>(bits, sym, a, st);
+  if (m == 128) {  // both passes on the matrix-core rotation, entries staged in between
+    const int64_t tiles = (a.n + 15) / 16;
+    uint8_t* w = reinterpret_cast<uint8_t*>(part) + align16(4 * scan_partials(a.n));
+    w = reinterpret_cast<uint8_t*>(align16(reinterpret_cast<int64_t>(w)));
+    EncodeArgs b = a;
+    b.stg_flag = reinterpret_cast<uint32_t*>(w);
+    b.stg_idx = w + align16(4 * tiles);
+    b.stg_val = reinterpret_cast<uint16_t*>(b.stg_idx + align16(kOutlierStage * tiles));
+    hipError_t e = launch_t128_outlier_pass<1>(bits, sym, b, st);
+    if (e == hipSuccess) e = launch_offsets_scan(b.ol_off, b.n, part, st);
+    if (e == hipSuccess) e = launch_outlier_copy(b, st);
+    if (e == hipSuccess) e = launch_t128_outlier_pass<2>(bits, sym, b, st);
     return e;
   }
   switch (m) {

@@ -254,13 +254,18 @@ constexpr int kT128Rows = 16;   // vectors per wave tile
 // of an entry among the vector's outliers in ascending coordinate order is the number of set
 // bits of lower coordinates, counted group by group. Both passes decide |u / n| > T with the
 // same instructions, so their counts agree.
+// Read once: the first pass also stages each 16-vector wave tile's entries, in CSR order, in the
+// workspace (the tile-local offset of a vector is the prefix of its tile's counts), when the
+// tile has at most kOutlierStage of them, and flags the tile. After the scan k_outlier_copy
+// moves a staged tile's entries to [offsets[first vector], + count) without touching its rows,
+// and the second pass visits only the tiles over the budget (found 64 flags at a time).
 template <int BITS, bool SYM, int OL = 0>
 __global__ __launch_bounds__(64 * kT128Waves) __attribute__((amdgpu_waves_per_eu(3)))
 void k_encode_t128(EncodeArgs a) {
   constexpr int M = 128, KS = 4, RCH = M / 8, ROWS = kT128Rows;
   constexpr int NWC = (M / 32) * BITS, NWT = NWC + 1, TILE = kT128Waves * ROWS;
   __shared__ uint4 s_reg[kT128Waves * ROWS * RCH];
-  __shared__ float s_z[OL == 2 ? kT128Waves * 32 * 64 : 1];  // entry pass: z[t] of each lane
+  __shared__ float s_z[OL != 0 ? kT128Waves * 32 * 64 : 1];  // outlier passes: z[t] of each lane
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
   const int c = ln & 15, grp = ln >> 4;
   uint4 F[2][KS], FN[2][KS];
@@ -302,13 +307,57 @@ void k_encode_t128(EncodeArgs a) {
       }
     }
   };
+  // the block tiles this wave computes: b, b + G, ...; in the entry pass only those whose wave
+  // tile was not staged, from ballots over the flags of 64 block tiles at a time
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int64_t fl_base = (int64_t)blockIdx.x - 64 * G;  // block tile of mask bit 0
+  uint64_t fl_mask = 0;
+  auto next_tile = [&](int64_t tile) -> int64_t {
+    if constexpr (OL != 2) {
+      return tile + G;
+    } else {
+      while (fl_mask == 0) {
+        fl_base += 64 * G;
+        if (fl_base >= n_tiles) return n_tiles;
+        const int64_t tl = fl_base + (int64_t)ln * G;
+        const int64_t r = tl * TILE + ROWS * wave_u;
+        fl_mask = __ballot(tl < n_tiles && r < a.n && a.stg_flag[r / ROWS] != 0u);
+      }
+      const int j = __builtin_ctzll(fl_mask);
+      fl_mask &= fl_mask - 1;
+      return fl_base + (int64_t)j * G;
+    }
+  };
+  // lane (grp, c)'s entries of the vector whose CSR entries start at base, clipped to [., end),
+  // from its outlier mask olm and its LDS column of z values
+  auto emit = [&](uint32_t olm, const float* zc, uint8_t* idx, uint16_t* val, int64_t base, int64_t end) {
+    uint32_t mg[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) mg[g] = (uint32_t)__shfl((int)olm, c + 16 * g, 64);
+    for (uint32_t rem = olm; rem != 0u; rem &= rem - 1u) {
+      const int t = __builtin_ctz(rem), J = t >> 1;
+      // set bits of coordinates below 8 J (lo) and below 8 J + 8 (lo_pair; all ones at J = 15)
+      const uint32_t lo = (1u << (2 * J)) - 1u, lo_pair = (4u << (2 * J)) - 1u;
+      uint32_t rank = __builtin_popcount(olm & ((1u << t) - 1u));
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (g != grp) rank += __builtin_popcount(mg[g] & (g < grp ? lo_pair : lo));
+      const int64_t pos = base + rank;
+      if (pos < end) {
+        idx[pos] = (uint8_t)(8 * J + 2 * grp + (t & 1));
+        val[pos] = (uint16_t)f32_to_bf16_rne(zc[64 * t]);
+      }
+    }
+  };
+  const int64_t first = OL == 2 ? next_tile(0) : (int64_t)blockIdx.x;
   uint4 nxt[4];
-  if ((int64_t)blockIdx.x < n_tiles) load_tile(blockIdx.x, nxt);
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += G) {
+  if (first < n_tiles) load_tile(first, nxt);
+  for (int64_t tile = first, tn; tile < n_tiles; tile = tn) {
     const int64_t rw0 = tile * TILE + ROWS * wave;
 #pragma unroll
     for (int k = 0; k < 4; ++k) reg[woff[k]] = nxt[k];
-    if (tile + G < n_tiles) load_tile(tile + G, nxt);  // in flight while this tile computes
+    tn = next_tile(tile);
+    if (tn < n_tiles) load_tile(tn, nxt);  // in flight while this tile computes
     __builtin_amdgcn_wave_barrier();
     uint4 X[KS];
 #pragma unroll
@@ -376,34 +425,21 @@ void k_encode_t128(EncodeArgs a) {
           olm |= (fabsf(z) > a.tab.T ? 1u : 0u) << ol_bit(mt, i);
         }
       }
-      uint32_t mg[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) mg[g] = (uint32_t)__shfl((int)olm, c + 16 * g, 64);
-      if (olm != 0u && vec < a.n) {
-        const int64_t base = a.ol_off[vec];
-        int64_t end = a.ol_off[vec + 1];
+      if (vec >= a.n) olm = 0u;
+      int64_t base = 0, end = 0;
+      if (vec < a.n) {
+        base = a.ol_off[vec];
+        end = a.ol_off[vec + 1];
         if (end > a.ol_cap) end = a.ol_cap;
-        for (uint32_t rem = olm; rem != 0u; rem &= rem - 1u) {
-          const int t = __builtin_ctz(rem), J = t >> 1;
-          // set bits of coordinates below 8 J (lo) and below 8 J + 8 (lo_pair; all ones at J = 15)
-          const uint32_t lo = (1u << (2 * J)) - 1u, lo_pair = (4u << (2 * J)) - 1u;
-          uint32_t rank = __builtin_popcount(olm & ((1u << t) - 1u));
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            if (g != grp) rank += __builtin_popcount(mg[g] & (g < grp ? lo_pair : lo));
-          const int64_t pos = base + rank;
-          if (pos < end) {
-            static_cast<uint8_t*>(a.ol_idx)[pos] = (uint8_t)(8 * J + 2 * grp + (t & 1));
-            a.ol_val[pos] = (uint16_t)f32_to_bf16_rne(zc[64 * t]);
-          }
-        }
       }
+      emit(olm, zc, static_cast<uint8_t*>(a.ol_idx), a.ol_val, base, end);
       __builtin_amdgcn_wave_barrier();
       continue;  // the records were written by the first pass
     }
     const Quant<BITS, SYM> q(a.tab, n);
     QuantAcc<BITS, SYM> qa;
     uint32_t olm = 0;
+    float* zc1 = s_z + wave * 32 * 64 + ln;  // OL = 1: z of this lane's outlier coordinates
 #pragma unroll
     for (int mt = 7; mt >= 0; --mt) {
       const floatx4 acc = mtile(mt);
@@ -412,15 +448,34 @@ void k_encode_t128(EncodeArgs a) {
         qa.push(acc[i], q);
         if constexpr (OL == 1) {
           const float z = acc[i] * rn;
-          olm |= (fabsf(z) > a.tab.T ? 1u : 0u) << ol_bit(mt, i);
+          const bool o = fabsf(z) > a.tab.T;
+          olm |= (o ? 1u : 0u) << ol_bit(mt, i);
+          if (o) zc1[64 * ol_bit(mt, i)] = z;
         }
       }
     }
     if constexpr (OL == 1) {
-      uint32_t cnt = __builtin_popcount(olm);
+      if (vec >= a.n) olm = 0u;
+      const uint32_t own = __builtin_popcount(olm);
+      uint32_t cnt = own;
       cnt += (uint32_t)__shfl_xor((int)cnt, 16, 64);
       cnt += (uint32_t)__shfl_xor((int)cnt, 32, 64);
       if (grp == 0 && vec < a.n) a.ol_off[vec] = cnt;
+      // tile-local CSR offsets: prefix of the 16 vectors' counts (every group computes it)
+      uint32_t incl = cnt;
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, d, 16);
+        if (c >= d) incl += y;
+      }
+      const uint32_t total = (uint32_t)__shfl((int)incl, 15, 16);
+      if (rw0 < a.n) {  // wave-uniform
+        const int64_t t16 = rw0 / ROWS;
+        if (total <= (uint32_t)kOutlierStage)
+          emit(olm, zc1, a.stg_idx + t16 * kOutlierStage, a.stg_val + t16 * kOutlierStage,
+               incl - cnt, kOutlierStage);
+        if (ln == 0) a.stg_flag[t16] = total <= (uint32_t)kOutlierStage ? 0u : 1u;
+      }
     }
     uint32_t pl[BITS];
     qa.planes(q, 0xFFFFFFFFu, pl);
@@ -500,6 +555,36 @@ hipError_t launch_t128_outlier_pass(int bits, bool sym, const EncodeArgs& a, hip
 }
 template hipError_t launch_t128_outlier_pass<1>(int, bool, const EncodeArgs&, hipStream_t);
 template hipError_t launch_t128_outlier_pass<2>(int, bool, const EncodeArgs&, hipStream_t);
+
+// Staged outlier entries into the CSR (after the scan): wave tile t of 16 vectors, when its
+// flag is 0, copies its entries to [offsets[16 t], offsets[min(16 t + 16, n)]), clipped to the
+// capacity. One wave per tile, many in flight: the flag, offset and entry loads of different
+// tiles overlap.
+__global__ __launch_bounds__(256) void k_outlier_copy(EncodeArgs a) {
+  const int ln = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tiles = (a.n + kT128Rows - 1) / kT128Rows;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < tiles; t += (int64_t)gridDim.x * 4) {
+    if (a.stg_flag[t] != 0u) continue;
+    const int64_t r0 = t * kT128Rows, vend = r0 + kT128Rows < a.n ? r0 + kT128Rows : a.n;
+    const int64_t base = a.ol_off[r0], total = (int64_t)a.ol_off[vend] - base;
+    const uint8_t* si = a.stg_idx + t * kOutlierStage;
+    const uint16_t* sv = a.stg_val + t * kOutlierStage;
+    for (int64_t i = ln; i < total; i += 64)
+      if (base + i < a.ol_cap) {
+        static_cast<uint8_t*>(a.ol_idx)[base + i] = si[i];
+        a.ol_val[base + i] = sv[i];
+      }
+  }
+}
+
+hipError_t launch_outlier_copy(const EncodeArgs& a, hipStream_t st) {
+  const int64_t tiles = (a.n + kT128Rows - 1) / kT128Rows;
+  int64_t blocks = (tiles + 3) / 4;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(k_outlier_copy, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 static hipError_t launch_t128_b(int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
   switch (bits * 2 + (sym ? 1 : 0)) {

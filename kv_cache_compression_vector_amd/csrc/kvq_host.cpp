@@ -293,7 +293,8 @@ size_t kvq_encode_workspace_bytes(const kvq_codec* codec, int64_t n) {
   Resolved r;
   if (resolve_codec(codec, r) != KVQ_OK || n < 0) return 0;
   if (!r.outliers) return 0;
-  return (size_t)(16 + 4 * kvq::scan_partials(n));
+  // the scan's block sums, then (coded length 128) the entries staged per 16-vector tile
+  return (size_t)(16 + 4 * kvq::scan_partials(n) + 16 + kvq::outlier_stage_bytes(r.m, n));
 }
 
 kvq_status kvq_codec_tables(const kvq_codec* codec, float* centroids_host,

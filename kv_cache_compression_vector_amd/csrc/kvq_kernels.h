@@ -19,6 +19,11 @@ struct EncodeArgs {
   void* ol_idx;             // u8 entries for m <= 256, u16 above
   uint16_t* ol_val;
   int64_t ol_cap;
+  // staged outlier entries of the matrix-core encode at m = 128 (workspace): per 16-vector
+  // tile a flag (0: its entries are staged, in order, at tile * kOutlierStage) and the entries
+  uint32_t* stg_flag;
+  uint8_t* stg_idx;
+  uint16_t* stg_val;
   // PCA projection (PCA kernels only)
   Basis pca;                // PCA kernels only
   // stored scale: 0 the norm; 1 matched norm; 2 inner-product preserving; 3 least squares
@@ -108,6 +113,11 @@ bool encode_mx_supported(int m);
 // Outlier lists in three passes (count + records, offsets scan, entries); `part` holds
 // scan_partials(n) u32 of workspace.
 int64_t scan_partials(int64_t n);
+// Outlier entries staged per 16-vector tile by the first pass at m = 128 (a tile with more
+// entries is recomputed by the second pass), and the workspace bytes that staging takes after
+// the scan partials (0 for other coded lengths).
+constexpr int kOutlierStage = 128;
+int64_t outlier_stage_bytes(int m, int64_t n);
 hipError_t launch_encode_outliers3(int m, int bits, bool sym, const EncodeArgs& a, uint32_t* part,
                                    hipStream_t st);
 hipError_t launch_encode_mx(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
@@ -120,6 +130,8 @@ hipError_t launch_evict_kron(int m, int bits, bool sym, const EvictArgs& a, hipS
 // counts into ol_off, OL = 2 (after the scan) the entries.
 template <int OL>
 hipError_t launch_t128_outlier_pass(int bits, bool sym, const EncodeArgs& a, hipStream_t st);
+// The entries the first pass staged, copied into the CSR (after the scan).
+hipError_t launch_outlier_copy(const EncodeArgs& a, hipStream_t st);
 bool pca_shape_supported(int D, int r);
 hipError_t launch_encode_pca(int D, int r, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
 hipError_t launch_decode_pca(int D, int r, int bits, bool bf16_out, const DecodeArgs& a,

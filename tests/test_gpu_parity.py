@@ -229,8 +229,12 @@ def test_score_packed_query_and_table_scales(cscale):
 
 
 @pytest.mark.parametrize("D,bits,T_", [(128, 2, 2.0), (64, 3, 1.5), (256, 2, 2.5), (128, 4, 2.0),
-                                       (512, 4, 2.0), (512, 2, 1.8)])
+                                       (512, 4, 2.0), (512, 2, 1.8), (128, 3, 1.85), (128, 2, 1.3)])
 def test_outlier_parity(D, bits, T_):
+    """Every vector's CSR entries against the oracle's. At coded length 128 the entries of a
+    16-vector tile are staged by the first pass when there are at most 128 of them and copied
+    after the scan; T = 1.85 leaves some tiles over that budget (recomputed from the rows), T =
+    1.3 all of them."""
     n = 3000 + 13
     x = _rows(n, D, seed=D + bits)
     x[:, 3] *= 16  # heavy channel
@@ -283,6 +287,29 @@ def test_outlier_decode_bf16_rows_with_a_ragged_tail(D, bits, n):
     yref = oracle.decode(oracle_codec_like(codec), recn, off, idx[:total], val[:total])
     compare_decoded(y32, yref, unpack_records(recn, D, bits)[1], "outlier decode (bf16)",
                     extra_ulp_bf16=True)
+
+
+@pytest.mark.parametrize("T_", [2.2, 1.85, 1.3])
+def test_outlier_list_cut_at_capacity_is_a_prefix(T_):
+    """A list cut short by the capacity holds exactly the first `capacity` entries of the full
+    list (staged tiles are copied, tiles over the staging budget recomputed, both clipped)."""
+    D, bits, n = 128, 2, 2000 + 5
+    codec = kvq.Codec(D, bits, seed=8, outlier_T=T_)
+    x = _rows(n, D, seed=41)
+    x[:, 7] *= 10
+    full = kvq.Outliers(codec, n, capacity=n * D, device=DEV)
+    rec_f, total = kvq.encode(codec, x, outliers=full, want_total=True)
+    cap = total // 2 + 3
+    part = kvq.Outliers(codec, n, capacity=cap, device=DEV)
+    say(f"outlier list cut at {cap} of {total} (T={T_})")
+    with pytest.raises(kvq.KvqError) as ei:
+        kvq.encode(codec, x, outliers=part, want_total=True)
+    assert ei.value.name == "KVQ_E_CAPACITY"
+    rec_p = kvq.encode(codec, x, outliers=part)
+    torch.cuda.synchronize()
+    assert torch.equal(rec_p, rec_f)
+    assert torch.equal(part.offsets, full.offsets)
+    assert torch.equal(part.idx[:cap], full.idx[:cap]) and torch.equal(part.val[:cap], full.val[:cap])
 
 
 def test_outlier_capacity_overflow_reports_and_truncates():
