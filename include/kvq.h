@@ -164,7 +164,9 @@ typedef struct kvq_cache {
 size_t kvq_record_bytes(const kvq_codec* codec);
 
 /* Workspace bytes kvq_encode needs for n vectors when codec->outlier_T > 0 (0 otherwise): the
- * block sums of the scan that turns per-vector outlier counts into CSR offsets. */
+ * block sums of the scan that turns per-vector outlier counts into CSR offsets and, at coded
+ * length 128, per 16-vector tile a flag and room for 128 entries (3 bytes each) that the first
+ * pass stages so that the rows are read once (about 24.3 bytes per vector). */
 size_t kvq_encode_workspace_bytes(const kvq_codec* codec, int64_t n);
 
 /* Host copies of the tables the kernels use, for inspection and tests: centroids f32[2^b],
