@@ -439,7 +439,7 @@ void k_encode_t128(EncodeArgs a) {
     const Quant<BITS, SYM> q(a.tab, n);
     QuantAcc<BITS, SYM> qa;
     uint32_t olm = 0;
-    float* zc1 = s_z + wave * 32 * 64 + ln;  // OL = 1: z of this lane's outlier coordinates
+    float* zc1 = s_z + wave * 32 * 64 + ln;  // OL = 1: z of this lane's coordinates
 #pragma unroll
     for (int mt = 7; mt >= 0; --mt) {
       const floatx4 acc = mtile(mt);
@@ -450,7 +450,9 @@ void k_encode_t128(EncodeArgs a) {
           const float z = acc[i] * rn;
           const bool o = fabsf(z) > a.tab.T;
           olm |= (o ? 1u : 0u) << ol_bit(mt, i);
-          if (o) zc1[64 * ol_bit(mt, i)] = z;
+          // every z, not only the outliers': a branch per coordinate would cost exec-mask
+          // switching and split the rotation products the compiler shares across m-tiles
+          zc1[64 * ol_bit(mt, i)] = z;
         }
       }
     }
@@ -558,18 +560,19 @@ template hipError_t launch_t128_outlier_pass<2>(int, bool, const EncodeArgs&, hi
 
 // Staged outlier entries into the CSR (after the scan): wave tile t of 16 vectors, when its
 // flag is 0, copies its entries to [offsets[16 t], offsets[min(16 t + 16, n)]), clipped to the
-// capacity. One wave per tile, many in flight: the flag, offset and entry loads of different
-// tiles overlap.
+// capacity. Each 16-lane group takes its own tile, so a wave has the flag, offset and entry
+// loads of four tiles in flight.
 __global__ __launch_bounds__(256) void k_outlier_copy(EncodeArgs a) {
-  const int ln = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ln = threadIdx.x & 63, sub = ln & 15;
   const int64_t tiles = (a.n + kT128Rows - 1) / kT128Rows;
-  for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < tiles; t += (int64_t)gridDim.x * 4) {
+  for (int64_t t = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (ln >> 4); t < tiles;
+       t += (int64_t)gridDim.x * 16) {
     if (a.stg_flag[t] != 0u) continue;
     const int64_t r0 = t * kT128Rows, vend = r0 + kT128Rows < a.n ? r0 + kT128Rows : a.n;
     const int64_t base = a.ol_off[r0], total = (int64_t)a.ol_off[vend] - base;
     const uint8_t* si = a.stg_idx + t * kOutlierStage;
     const uint16_t* sv = a.stg_val + t * kOutlierStage;
-    for (int64_t i = ln; i < total; i += 64)
+    for (int64_t i = sub; i < total; i += 16)
       if (base + i < a.ol_cap) {
         static_cast<uint8_t*>(a.ol_idx)[base + i] = si[i];
         a.ol_val[base + i] = sv[i];
@@ -579,7 +582,7 @@ __global__ __launch_bounds__(256) void k_outlier_copy(EncodeArgs a) {
 
 hipError_t launch_outlier_copy(const EncodeArgs& a, hipStream_t st) {
   const int64_t tiles = (a.n + kT128Rows - 1) / kT128Rows;
-  int64_t blocks = (tiles + 3) / 4;
+  int64_t blocks = (tiles + 15) / 16;  // 16 tiles per block
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) return hipSuccess;
   hipLaunchKernelGGL(k_outlier_copy, dim3((unsigned)blocks), dim3(256), 0, st, a);
