@@ -13,42 +13,6 @@
 
 namespace kvq {
 
-// The centroid the quantiser picks for rotated coordinate u (code = #{k : u > n t_k}), decided
-// with the quantiser's own thresholds. Symmetric tables: the magnitude cell from |u|, the sign
-// from u (u <= 0 takes the lower half: c[L/2 - 1 - j] = -c[L/2 + j]).
-template <int BITS, bool SYM>
-__device__ __forceinline__ float chosen_centroid(float u, const Quant<BITS, SYM>& q, const Tables& tab) {
-  constexpr int L = 1 << BITS, NT = Quant<BITS, SYM>::NT;
-  int cnt = 0;
-  if constexpr (SYM) {
-#pragma unroll
-    for (int k = 0; k < NT; ++k) cnt += fabsf(u) > q.thr[k] ? 1 : 0;
-    float mag = tab.c[L / 2];
-#pragma unroll
-    for (int j = 1; j < L / 2; ++j) mag = cnt == j ? tab.c[L / 2 + j] : mag;
-    return (q.nz && u > 0.0f) ? mag : -mag;
-  } else {
-#pragma unroll
-    for (int k = 0; k < NT; ++k) cnt += u > q.thr[k] ? 1 : 0;
-    float c = tab.c[0];
-#pragma unroll
-    for (int j = 1; j < L; ++j) c = cnt == j ? tab.c[j] : c;
-    return c;
-  }
-}
-
-// Stored scale of a rule from n = ||v||, zu = sum_i u_i z^_i (u = H (s .* v) = n z) and
-// zz = sum_i z^_i^2 [turboquant_plus log: EDEN and matched-norm scales]. Decode gives
-// x^ = (scale/m) s .* H z^, so: 1 matched norm n sqrt(m / zz) (||x^|| = ||v||); 2 inner-product
-// preserving n^2 m / zu (<x^, v> = ||v||^2); 3 least squares zu / zz (<v - x^, x^> = 0).
-// A rule whose denominator is not positive keeps the norm.
-__device__ __forceinline__ float rule_scale(int rule, float n, float zu, float zz, int m) {
-  if (rule == 1 && zz > 0.0f) return n * sqrtf((float)m / zz);
-  if (rule == 2 && zu > 0.0f) return n * (n * (float)m / zu);
-  if (rule == 3 && zz > 0.0f) return zu / zz;
-  return n;
-}
-
 template <int M, int BITS, bool SYM, bool RULE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LV<M>::WAVES)))
 void k_encode(EncodeArgs a) {
@@ -604,9 +568,9 @@ static hipError_t launch_encode_m(int bits, bool sym, const EncodeArgs& a, hipSt
 }
 
 hipError_t launch_encode(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
-  // a scale rule needs the chosen centroids, which the lane-per-vector kernel forms
-  if (a.scale_rule == 0 && encode_mx_supported(m)) return launch_encode_mx(m, bits, sym, a, st);
-  if (a.scale_rule == 0 && encode_kron_supported(m)) return launch_encode_kron(m, bits, sym, a, st);
+  // the lane-per-vector kernel: coded length 32, and 64 with a scale rule
+  if (encode_mx_supported(m, a.scale_rule)) return launch_encode_mx(m, bits, sym, a, st);
+  if (encode_kron_supported(m)) return launch_encode_kron(m, bits, sym, a, st);
   switch (m) {
     case 32: return launch_encode_m<32>(bits, sym, a, st);
     case 64: return launch_encode_m<64>(bits, sym, a, st);

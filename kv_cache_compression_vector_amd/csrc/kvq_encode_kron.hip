@@ -138,9 +138,11 @@ __device__ __forceinline__ uint4 kron_fragment(int t, int l) {
 // One wave tile: the 16 rows staged in `reg` by the caller (signs already flipped); writes the
 // 16 records (NWT words each) into rec_lds, which aliases reg and is written only after every
 // operand read. The caller stores rec_lds.
-template <int M, int BITS, bool SYM>
+// RULE: the stored scale is the codec's scale rule (scale_rule, from the chosen centroids) instead
+// of the norm.
+template <int M, int BITS, bool SYM, bool RULE = false>
 __device__ __forceinline__ void kron_tile(const Tables& tab, const uint4 (&A)[2], const uint4* reg,
-                                          uint32_t* rec_lds, int ln) {
+                                          uint32_t* rec_lds, int ln, int scale_rule = 0) {
   using K = KR<M>;
   constexpr int O = K::O, CH = K::CH, NWC = (M / 32) * BITS, NWT = NWC + 1;
   const int v = ln & 15, g = ln >> 4;
@@ -148,13 +150,15 @@ __device__ __forceinline__ void kron_tile(const Tables& tab, const uint4 (&A)[2]
   // the operands read from LDS again for the second half)
   constexpr int TP = O > 8 ? 1 : 2;
   // top bits of the block index o whose butterfly stages run on the matrix cores (one fewer at
-  // m = 512 for general tables of 3 and 4 bits, whose 7 or 15 thresholds need the registers)
-  constexpr int FB = O > 8 && (SYM || BITS < 3) ? 2 : 1, NH = 1 << FB, NL = O / NH;
+  // m = 512 for general tables of 3 and 4 bits, whose 7 or 15 thresholds need the registers, and
+  // with a scale rule, whose centroid selection needs them)
+  constexpr int FB = O > 8 && (SYM || BITS < 3) && !RULE ? 2 : 1, NH = 1 << FB, NL = O / NH;
   const uint4 AN[2] = {neg_bf16(A[0]), neg_bf16(A[1])};
   constexpr int LV = QuantBS<BITS, SYM>::LVL > 0 ? QuantBS<BITS, SYM>::LVL : 1;
   uint32_t* rec = rec_lds + v * NWT;
   uint32_t pl[2][O / 8][BITS];  // plane words of word group (4 t + g) m/256 + oh
   float n = 0.0f;
+  float zu = 0.0f, zz = 0.0f;   // RULE
 #pragma unroll
   for (int t0 = 0; t0 < 2; t0 += TP) {
     // Y[o] for the pass's output halves, with the transform's stages over the top FB bits of o
@@ -239,10 +243,17 @@ __device__ __forceinline__ void kron_tile(const Tables& tab, const uint4 (&A)[2]
 #pragma unroll
         for (int o = 8 * oh + 7; o >= 8 * oh; --o) {
 #pragma unroll
-          for (int i = 3; i >= 0; --i) q.push(acc[tt][o][i], w, sgn);
-          // general tables of 3 and 4 bits: a few coordinates' searches at a time (scheduled
-          // wide, their candidate thresholds exhaust the registers)
-          if constexpr (!SYM && BITS >= 3) __builtin_amdgcn_sched_barrier(0);
+          for (int i = 3; i >= 0; --i) {
+            q.push(acc[tt][o][i], w, sgn);
+            if constexpr (RULE) {
+              const float zh = chosen_centroid<BITS, SYM>(acc[tt][o][i], q, tab);
+              zu = fmaf(acc[tt][o][i], zh, zu);
+              zz = fmaf(zh, zh, zz);
+            }
+          }
+          // general tables of 3 and 4 bits, or a scale rule: a few coordinates' searches at a
+          // time (scheduled wide, their candidate thresholds exhaust the registers)
+          if constexpr ((!SYM && BITS >= 3) || RULE) __builtin_amdgcn_sched_barrier(0);
         }
         q.planes(w, sgn, pl[t0 + tt][oh]);
       }
@@ -256,7 +267,15 @@ __device__ __forceinline__ void kron_tile(const Tables& tab, const uint4 (&A)[2]
 #pragma unroll
       for (int p = 0; p < BITS; ++p) rec[G * BITS + p] = pl[t][oh][p];
     }
-  if (g == 0) rec[NWC] = __float_as_uint(n);
+  float stored = n;
+  if constexpr (RULE) {
+    zu += __shfl_xor(zu, 16, 64);
+    zu += __shfl_xor(zu, 32, 64);
+    zz += __shfl_xor(zz, 16, 64);
+    zz += __shfl_xor(zz, 32, 64);
+    stored = n > 0.0f ? rule_scale(scale_rule, n, zu, zz, M) : 0.0f;
+  }
+  if (g == 0) rec[NWC] = __float_as_uint(stored);
 }
 
 // Load piece k of a tile into registers: row RPI k + l / CH, chunk l % CH (the rows' 16-byte
@@ -332,7 +351,7 @@ __device__ __forceinline__ uint4 kron_signs(const Tables& tab, int ln) {
 
 // Plain encode: wave tiles of 16 rows (rows past the end repeat the last row), tile w of the
 // grid's 4 G waves then w + 4 G, ...
-template <int M, int BITS, bool SYM>
+template <int M, int BITS, bool SYM, bool RULE>
 __global__ __launch_bounds__(64 * KR<M>::WAVES) __attribute__((amdgpu_waves_per_eu(KR<M>::OCC)))
 void k_encode_kron(EncodeArgs a) {
   using K = KR<M>;
@@ -363,7 +382,7 @@ void k_encode_kron(EncodeArgs a) {
     if (tile + stride < n_tiles) load(tile + stride, nxt);
     __builtin_amdgcn_wave_barrier();
     uint32_t* rec_lds = reinterpret_cast<uint32_t*>(reg);
-    kron_tile<M, BITS, SYM>(a.tab, A, reg, rec_lds, ln);
+    kron_tile<M, BITS, SYM, RULE>(a.tab, A, reg, rec_lds, ln, a.scale_rule);
     __builtin_amdgcn_wave_barrier();
     const int64_t r0 = tile * 16;
     const int valid = a.n - r0 < 16 ? (int)(a.n - r0) : 16;
@@ -447,15 +466,21 @@ static int64_t kron_grid(int per_cu, int64_t block_tiles) {
   return block_tiles < resident ? block_tiles : resident;
 }
 
-template <int M, int BITS, bool SYM>
-static hipError_t launch_encode_kron_t(const EncodeArgs& a, hipStream_t st) {
+template <int M, int BITS, bool SYM, bool RULE>
+static hipError_t launch_encode_kron_r(const EncodeArgs& a, hipStream_t st) {
   constexpr int W = KR<M>::WAVES;
-  static const int per_cu = kron_per_cu(k_encode_kron<M, BITS, SYM>, 64 * W);
+  static const int per_cu = kron_per_cu(k_encode_kron<M, BITS, SYM, RULE>, 64 * W);
   const int64_t tiles = (a.n + 15) / 16;
   const int64_t blocks = kron_grid(per_cu, (tiles + W - 1) / W);
   if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL((k_encode_kron<M, BITS, SYM>), dim3((unsigned)blocks), dim3(64 * W), 0, st, a);
+  hipLaunchKernelGGL((k_encode_kron<M, BITS, SYM, RULE>), dim3((unsigned)blocks), dim3(64 * W), 0, st, a);
   return hipGetLastError();
+}
+
+template <int M, int BITS, bool SYM>
+static hipError_t launch_encode_kron_t(const EncodeArgs& a, hipStream_t st) {
+  return a.scale_rule != 0 ? launch_encode_kron_r<M, BITS, SYM, true>(a, st)
+                           : launch_encode_kron_r<M, BITS, SYM, false>(a, st);
 }
 
 template <int M, int BITS, bool SYM>

@@ -259,8 +259,10 @@ constexpr int kT128Rows = 16;   // vectors per wave tile
 // tile has at most kOutlierStage of them, and flags the tile. After the scan k_outlier_copy
 // moves a staged tile's entries to [offsets[first vector], + count) without touching its rows,
 // and the second pass visits only the tiles over the budget (found 64 flags at a time).
-template <int BITS, bool SYM, int OL = 0>
-__global__ __launch_bounds__(64 * kT128Waves) __attribute__((amdgpu_waves_per_eu(3)))
+// RULE: the record stores the codec's scale rule (from zu = sum u z^, zz = sum z^^2 over the
+// chosen centroids, summed over the vector's four lane groups) instead of the norm.
+template <int BITS, bool SYM, int OL = 0, bool RULE = false>
+__global__ __launch_bounds__(64 * kT128Waves) __attribute__((amdgpu_waves_per_eu(RULE ? 2 : 3)))
 void k_encode_t128(EncodeArgs a) {
   constexpr int M = 128, KS = 4, RCH = M / 8, ROWS = kT128Rows;
   constexpr int NWC = (M / 32) * BITS, NWT = NWC + 1, TILE = kT128Waves * ROWS;
@@ -440,12 +442,18 @@ void k_encode_t128(EncodeArgs a) {
     QuantAcc<BITS, SYM> qa;
     uint32_t olm = 0;
     float* zc1 = s_z + wave * 32 * 64 + ln;  // OL = 1: z of this lane's coordinates
+    float zu = 0.0f, zz = 0.0f;              // RULE
 #pragma unroll
     for (int mt = 7; mt >= 0; --mt) {
       const floatx4 acc = mtile(mt);
 #pragma unroll
       for (int i = 3; i >= 0; --i) {
         qa.push(acc[i], q);
+        if constexpr (RULE) {
+          const float zh = chosen_centroid<BITS, SYM>(acc[i], q, a.tab);
+          zu = fmaf(acc[i], zh, zu);
+          zz = fmaf(zh, zh, zz);
+        }
         if constexpr (OL == 1) {
           const float z = acc[i] * rn;
           const bool o = fabsf(z) > a.tab.T;
@@ -481,11 +489,19 @@ void k_encode_t128(EncodeArgs a) {
     }
     uint32_t pl[BITS];
     qa.planes(q, 0xFFFFFFFFu, pl);
+    float stored = n;
+    if constexpr (RULE) {
+      zu += __shfl_xor(zu, 16, 64);
+      zu += __shfl_xor(zu, 32, 64);
+      zz += __shfl_xor(zz, 16, 64);
+      zz += __shfl_xor(zz, 32, 64);
+      stored = n > 0.0f ? rule_scale(a.scale_rule, n, zu, zz, M) : 0.0f;
+    }
     // the tile's records, staged in the (now free) region: lane (grp, c) writes words
-    // grp * b .. grp * b + b - 1 of record c; group 0 writes the norm
+    // grp * b .. grp * b + b - 1 of record c; group 0 writes the stored scale
 #pragma unroll
     for (int p = 0; p < BITS; ++p) rec_lds[c * NWT + grp * BITS + p] = pl[p];
-    if (grp == 0) rec_lds[c * NWT + NWC] = __float_as_uint(n);
+    if (grp == 0) rec_lds[c * NWT + NWC] = __float_as_uint(stored);
     __builtin_amdgcn_wave_barrier();
     // the wave tile's records are contiguous in memory: coalesced 16-byte stores
     {
@@ -513,13 +529,13 @@ void k_encode_t128(EncodeArgs a) {
   }
 }
 
-template <int BITS, bool SYM, int OL = 0>
+template <int BITS, bool SYM, int OL = 0, bool RULE = false>
 static hipError_t launch_t128(const EncodeArgs& a, hipStream_t st) {
   constexpr int TILE = kT128Waves * kT128Rows;
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_encode_t128<BITS, SYM, OL>, 64 * kT128Waves, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_encode_t128<BITS, SYM, OL, RULE>, 64 * kT128Waves, 0) !=
             hipSuccess || nb <= 0)
       nb = 1;
     per_cu = nb;
@@ -530,7 +546,7 @@ static hipError_t launch_t128(const EncodeArgs& a, hipStream_t st) {
   const int64_t tiles = (a.n + TILE - 1) / TILE;
   const int64_t resident = (int64_t)per_cu * cus;
   const int64_t blocks = tiles < resident ? tiles : resident;
-  hipLaunchKernelGGL((k_encode_t128<BITS, SYM, OL>), dim3((unsigned)blocks), dim3(64 * kT128Waves), 0,
+  hipLaunchKernelGGL((k_encode_t128<BITS, SYM, OL, RULE>), dim3((unsigned)blocks), dim3(64 * kT128Waves), 0,
                      st, a);
   return hipGetLastError();
 }
@@ -589,18 +605,23 @@ hipError_t launch_outlier_copy(const EncodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-static hipError_t launch_t128_b(int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
+template <bool RULE>
+static hipError_t launch_t128_r(int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
   switch (bits * 2 + (sym ? 1 : 0)) {
-    case 2: return launch_t128<1, false>(a, st);
-    case 3: return launch_t128<1, true>(a, st);
-    case 4: return launch_t128<2, false>(a, st);
-    case 5: return launch_t128<2, true>(a, st);
-    case 6: return launch_t128<3, false>(a, st);
-    case 7: return launch_t128<3, true>(a, st);
-    case 8: return launch_t128<4, false>(a, st);
-    case 9: return launch_t128<4, true>(a, st);
+    case 2: return launch_t128<1, false, 0, RULE>(a, st);
+    case 3: return launch_t128<1, true, 0, RULE>(a, st);
+    case 4: return launch_t128<2, false, 0, RULE>(a, st);
+    case 5: return launch_t128<2, true, 0, RULE>(a, st);
+    case 6: return launch_t128<3, false, 0, RULE>(a, st);
+    case 7: return launch_t128<3, true, 0, RULE>(a, st);
+    case 8: return launch_t128<4, false, 0, RULE>(a, st);
+    case 9: return launch_t128<4, true, 0, RULE>(a, st);
   }
   return hipErrorInvalidValue;
+}
+
+static hipError_t launch_t128_b(int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
+  return a.scale_rule != 0 ? launch_t128_r<true>(bits, sym, a, st) : launch_t128_r<false>(bits, sym, a, st);
 }
 
 template <int M, int BITS, bool SYM>
@@ -630,7 +651,7 @@ static hipError_t launch_mx_m(int bits, bool sym, const EncodeArgs& a, hipStream
   return hipErrorInvalidValue;
 }
 
-bool encode_mx_supported(int m) { return m == 64 || m == 128; }
+bool encode_mx_supported(int m, int scale_rule) { return m == 128 || (m == 64 && scale_rule == 0); }
 
 hipError_t launch_encode_mx(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;

@@ -108,8 +108,8 @@ struct TailCopyArgs {
 };
 
 hipError_t launch_encode(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
-// Rotation on the matrix cores (coded length 64 or 128, no outlier list).
-bool encode_mx_supported(int m);
+// Rotation on the matrix cores (coded length 128, or 64 without a scale rule; no outlier list).
+bool encode_mx_supported(int m, int scale_rule);
 // Outlier lists in three passes (count + records, offsets scan, entries); `part` holds
 // scan_partials(n) u32 of workspace.
 int64_t scan_partials(int64_t n);
@@ -121,8 +121,8 @@ int64_t outlier_stage_bytes(int m, int64_t n);
 hipError_t launch_encode_outliers3(int m, int bits, bool sym, const EncodeArgs& a, uint32_t* part,
                                    hipStream_t st);
 hipError_t launch_encode_mx(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
-// Coded length 256 and 512: the rotation's 32-point blocks on the matrix cores (no outlier list,
-// no scale rule), for plain encode and for eviction.
+// Coded length 256 and 512: the rotation's 32-point blocks on the matrix cores (no outlier list),
+// for plain encode and for eviction.
 bool encode_kron_supported(int m);
 hipError_t launch_encode_kron(int m, int bits, bool sym, const EncodeArgs& a, hipStream_t st);
 hipError_t launch_evict_kron(int m, int bits, bool sym, const EvictArgs& a, hipStream_t st);

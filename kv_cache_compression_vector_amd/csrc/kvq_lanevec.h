@@ -397,6 +397,44 @@ struct QuantAcc {
   }
 };
 
+// The centroid the quantiser picks for rotated coordinate u (code = #{k : u > n t_k}), decided
+// with the quantiser's own thresholds. Symmetric tables: the magnitude cell from |u|, the sign
+// from u (u <= 0 takes the lower half: c[L/2 - 1 - j] = -c[L/2 + j]).
+// QT: a quantiser holding those thresholds times the norm in thr[] (Quant, or the binary-search
+// one of the Kronecker encode: both keep the same NT thresholds) and whether the norm is > 0.
+template <int BITS, bool SYM, class QT>
+__device__ __forceinline__ float chosen_centroid(float u, const QT& q, const Tables& tab) {
+  constexpr int L = 1 << BITS, NT = SYM ? L / 2 - 1 : L - 1;
+  int cnt = 0;
+  if constexpr (SYM) {
+#pragma unroll
+    for (int k = 0; k < NT; ++k) cnt += fabsf(u) > q.thr[k] ? 1 : 0;
+    float mag = tab.c[L / 2];
+#pragma unroll
+    for (int j = 1; j < L / 2; ++j) mag = cnt == j ? tab.c[L / 2 + j] : mag;
+    return (q.nz && u > 0.0f) ? mag : -mag;
+  } else {
+#pragma unroll
+    for (int k = 0; k < NT; ++k) cnt += u > q.thr[k] ? 1 : 0;
+    float c = tab.c[0];
+#pragma unroll
+    for (int j = 1; j < L; ++j) c = cnt == j ? tab.c[j] : c;
+    return c;
+  }
+}
+
+// Stored scale of a rule from n = ||v||, zu = sum_i u_i z^_i (u = H (s .* v) = n z) and
+// zz = sum_i z^_i^2 [turboquant_plus log: EDEN and matched-norm scales]. Decode gives
+// x^ = (scale/m) s .* H z^, so: 1 matched norm n sqrt(m / zz) (||x^|| = ||v||); 2 inner-product
+// preserving n^2 m / zu (<x^, v> = ||v||^2); 3 least squares zu / zz (<v - x^, x^> = 0).
+// A rule whose denominator is not positive keeps the norm.
+__device__ __forceinline__ float rule_scale(int rule, float n, float zu, float zz, int m) {
+  if (rule == 1 && zz > 0.0f) return n * sqrtf((float)m / zz);
+  if (rule == 2 && zu > 0.0f) return n * (n * (float)m / zu);
+  if (rule == 3 && zz > 0.0f) return zu / zz;
+  return n;
+}
+
 // All record code words of a lane-owned vector (Q == 1): out[g*BITS + p]. Word g, bit t holds
 // the coordinate at plane position 32g + t; bits are shifted in from t = 31 down to 0.
 template <int M, int BITS, bool SYM>
