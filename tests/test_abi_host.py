@@ -230,3 +230,16 @@ def test_stream_control_refusals():
     assert _status(L.kvq_stream_fill, P(FAKE + 4), 32, 7, None)[0] == "KVQ_E_STRIDE"
     # zero bytes is a no-op that touches nothing
     assert _status(L.kvq_stream_fill, None, 0, 7, None)[0] == "KVQ_OK"
+
+
+def test_encode_workspace_holds_the_staged_outlier_entries_at_coded_length_128():
+    """At coded length 128 the workspace also holds, per 16-vector tile, a flag and 128 staged
+    entries of 3 bytes (the rows are then read once); other lengths need the scan sums only."""
+    L = kvq.lib()
+    for n in (1, 15, 16, 17, 1000, 1 << 20):
+        tiles = (n + 15) // 16
+        w128 = L.kvq_encode_workspace_bytes(kvq.Codec(128, 2, outlier_T=2.0).ref, n)
+        w64 = L.kvq_encode_workspace_bytes(kvq.Codec(64, 2, outlier_T=2.0).ref, n)
+        assert w128 >= w64 + tiles * (4 + 128 * 3), (n, w128, w64)
+        assert w64 < 64 + n  # the scan's block sums: a few bytes per 4096 vectors
+    assert L.kvq_encode_workspace_bytes(kvq.Codec(128, 2).ref, 1000) == 0
