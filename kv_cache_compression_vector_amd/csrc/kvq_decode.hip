@@ -3,89 +3,14 @@
 // x^ = (n/M) s (.) H_M z^, z^_i = centroid[code_i], outlier entries replacing their coordinate
 // before the inverse rotation [kakeyaturbo PR #15, commit "M5": LUT, outlier scatter, y = z^ n,
 // x = H y sign / wht_len]. The Hadamard network runs in place (H is its own inverse up to
-// 1/M). Without a side list a vector lives in one lane's registers (kvq_lanevec.h); with a
-// side list the 8-coordinates-per-lane layout lets each lane test the entries of its vector.
+// 1/M). This file holds the decode with an outlier list at m = 256, 512: the 8-coordinates-
+// per-lane layout lets each lane test the entries of its vector. Every other Hadamard shape
+// decodes on the matrix cores (kvq_decode_h.hip).
 #include "kvq_device.h"
 #include "kvq_kernels.h"
 #include "kvq_lanevec.h"
 
 namespace kvq {
-
-template <int M, int BITS, bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LV<M>::WAVES)))
-void k_decode_lv(DecodeArgs a) {
-  using L = LV<M>;
-  using St = Stage<L::K>;
-  constexpr int NWC = (M / 32) * BITS, NWT = NWC + 1;
-  __shared__ __attribute__((aligned(16))) uint32_t s_sign[LV<M>::Q > 1 ? M / 2 : 4];
-  __shared__ float lut[16];
-  __shared__ uint4 s_tile[BF16 ? 4 * St::WORDS : 4];
-  build_sign_table<M>(a.tab, s_sign);
-  if (threadIdx.x < 16) lut[threadIdx.x] = a.tab.c[threadIdx.x];
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q = lane % L::Q, vw = lane / L::Q;
-  uint4* tile = s_tile + (BF16 ? wave * St::WORDS : 0);
-  const int64_t n_iter = (a.n + L::VPW - 1) / L::VPW;
-  const int64_t stride = (int64_t)gridDim.x * 4;
-  // lanes past the end decode the last record (their rows are not stored): the wave stays
-  // whole for the staged store and the quad exchanges
-  auto rec_of = [&](int64_t it) {
-    const int64_t vec = it * L::VPW + vw;
-    return reinterpret_cast<const uint32_t*>(a.rec) + (vec < a.n ? vec : a.n - 1) * NWT;
-  };
-  // one lane per vector: the next iteration's record is loaded while this one computes
-  uint32_t wn[L::Q == 1 ? NWT : 1];
-  const int64_t it0 = (int64_t)blockIdx.x * 4 + wave;
-  if constexpr (L::Q == 1) {
-    if (it0 < n_iter) load_words<NWT>(rec_of(it0), wn);
-  }
-  for (int64_t it = it0; it < n_iter; it += stride) {
-    const int64_t vec = it * L::VPW + vw;
-    float zh[L::K];
-    float scale;
-    if constexpr (L::Q == 1) {
-      uint32_t w[NWC];
-#pragma unroll
-      for (int i = 0; i < NWC; ++i) w[i] = wn[i];
-      scale = __uint_as_float(wn[NWC]) * a.tab.inv_m;
-      if (it + stride < n_iter) load_words<NWT>(rec_of(it + stride), wn);
-      unpack_lookup_words<M, BITS>(w, LdsLut{lut}, zh);
-    } else {
-      const uint32_t* r32 = rec_of(it);
-      unpack_lookup_lv<M, BITS>(r32, q, LdsLut{lut}, zh);
-      scale = __uint_as_float(r32[NWC]) * a.tab.inv_m;
-    }
-    fwht_regs<L::K>(zh);
-    fwht_cross<L::Q, L::K>(zh, q);
-    const uint32_t* sm = part_signs<M>(a.tab, s_sign, q);
-    if constexpr (BF16) {
-#pragma unroll
-      for (int c = 0; c < L::K / 8; ++c) {
-        const uint4 m = *reinterpret_cast<const uint4*>(sm + 4 * c);
-        uint4 o;
-        o.x = pack_bf16x2(zh[8 * c + 0] * scale, zh[8 * c + 1] * scale) ^ m.x;
-        o.y = pack_bf16x2(zh[8 * c + 2] * scale, zh[8 * c + 3] * scale) ^ m.y;
-        o.z = pack_bf16x2(zh[8 * c + 4] * scale, zh[8 * c + 5] * scale) ^ m.z;
-        o.w = pack_bf16x2(zh[8 * c + 6] * scale, zh[8 * c + 7] * scale) ^ m.w;
-        tile[lane * St::S + c] = o;
-      }
-      stage_rows_out<M>(static_cast<uint16_t*>(a.y), a.ld, it * L::VPW, a.n, tile);
-    } else if (vec < a.n) {
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<float*>(a.y) + vec * a.ld + q * L::K);
-#pragma unroll
-      for (int c = 0; c < L::K / 4; ++c) {
-        const uint32_t m0 = sm[2 * c], m1 = sm[2 * c + 1];
-        uint4 o;
-        o.x = __float_as_uint(zh[4 * c + 0] * scale) ^ (m0 << 16);
-        o.y = __float_as_uint(zh[4 * c + 1] * scale) ^ (m0 & 0x80000000u);
-        o.z = __float_as_uint(zh[4 * c + 2] * scale) ^ (m1 << 16);
-        o.w = __float_as_uint(zh[4 * c + 3] * scale) ^ (m1 & 0x80000000u);
-        st_stream(dst + c, o);
-      }
-    }
-  }
-}
 
 // Codes of the 8 coordinates of chunk c, looked up in the centroid table in LDS.
 template <int M, int BITS>
@@ -153,31 +78,25 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 }
 
 template <int M, int BITS>
-static hipError_t launch_decode_t(bool ol, bool bf16, const DecodeArgs& a, hipStream_t st) {
-  const int vpw = ol ? 64 / (M / 8) : LV<M>::VPW;
+static hipError_t launch_decode_t(bool bf16, const DecodeArgs& a, hipStream_t st) {
+  const int vpw = 64 / (M / 8);
   const int64_t n_iter = (a.n + vpw - 1) / vpw;
   int64_t blocks = (n_iter + 3) / 4;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) return hipSuccess;
   const dim3 g((unsigned)blocks), b(256);
-  if (ol) {
-    if (bf16) hipLaunchKernelGGL((k_decode<M, BITS, true, true>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((k_decode<M, BITS, true, false>), g, b, 0, st, a);
-  } else {
-    if (bf16) hipLaunchKernelGGL((k_decode_lv<M, BITS, true>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((k_decode_lv<M, BITS, false>), g, b, 0, st, a);
-  }
+  if (bf16) hipLaunchKernelGGL((k_decode<M, BITS, true, true>), g, b, 0, st, a);
+  else hipLaunchKernelGGL((k_decode<M, BITS, true, false>), g, b, 0, st, a);
   return hipGetLastError();
 }
 
 template <int M>
-static hipError_t launch_decode_m(int bits, bool ol, bool bf16, const DecodeArgs& a,
-                                  hipStream_t st) {
+static hipError_t launch_decode_m(int bits, bool bf16, const DecodeArgs& a, hipStream_t st) {
   switch (bits) {
-    case 1: return launch_decode_t<M, 1>(ol, bf16, a, st);
-    case 2: return launch_decode_t<M, 2>(ol, bf16, a, st);
-    case 3: return launch_decode_t<M, 3>(ol, bf16, a, st);
-    case 4: return launch_decode_t<M, 4>(ol, bf16, a, st);
+    case 1: return launch_decode_t<M, 1>(bf16, a, st);
+    case 2: return launch_decode_t<M, 2>(bf16, a, st);
+    case 3: return launch_decode_t<M, 3>(bf16, a, st);
+    case 4: return launch_decode_t<M, 4>(bf16, a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -190,11 +109,11 @@ hipError_t launch_decode(int D, int m, bool proj, int bits, bool ol, bool bf16, 
     if (decode_pca_h_supported(D, m)) return launch_decode_pca_h(D, m, bits, bf16, a, st);
     return launch_decode_pca(D, m, bits, bf16, a, st);
   }
+  if (!ol) return hipErrorInvalidValue;  // every Hadamard shape without a list is above
+  // Hadamard codec with an outlier list at m = 256, 512 (two-byte indices)
   switch (m) {
-    case 64: return launch_decode_m<64>(bits, ol, bf16, a, st);
-    case 128: return launch_decode_m<128>(bits, ol, bf16, a, st);
-    case 256: return launch_decode_m<256>(bits, ol, bf16, a, st);
-    case 512: return launch_decode_m<512>(bits, ol, bf16, a, st);
+    case 256: return launch_decode_m<256>(bits, bf16, a, st);
+    case 512: return launch_decode_m<512>(bits, bf16, a, st);
   }
   return hipErrorInvalidValue;
 }

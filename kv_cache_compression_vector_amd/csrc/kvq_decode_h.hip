@@ -1,4 +1,4 @@
-// kvq_decode_h.hip — Hadamard-codec decode (m = 64, 128) with the inverse rotation split between
+// kvq_decode_h.hip — Hadamard-codec decode (m = 64 .. 512) with the inverse rotation split between
 // the matrix cores and the vector ALUs.
 //
 // x^ = (n/m) s (.) H_m z^ [kakeyaturbo PR #15, "M4 Phase A" (inverse rotation, then the norm),
@@ -30,7 +30,11 @@ namespace kvq {
 namespace {
 
 constexpr int kDhWaves = 4;
-constexpr int kDhVT = 2;  // 16-vector tiles per wave step
+constexpr int kDhVT = 2;  // 16-vector tiles per wave step (m <= 128)
+
+// 16-vector tiles per wave step: one at m = 256, 512 (the bf16 staging of 16 rows is 8 or 16 KB)
+template <int M>
+constexpr int dh_vt() { return M <= 128 ? kDhVT : 1; }
 
 template <int BITS>
 constexpr int dh_copies() { return BITS <= 3 ? 32 : 4; }
@@ -117,22 +121,33 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 // i = 32 ab + 8 (e % 4) + 2 q + e / 4, so an entry belongs to lane group q = (i % 8) / 2 at slot
 // 8 ab + e; each lane scans its vector's entries into a per-lane LDS slot row and a slot mask,
 // and merges the flagged slots into its B operands (bf16 value as the hi half, lo half 0).
+//
+// m = 256, 512 (no outlier list): the same structure with NB = 8, 16 blocks. Plane position
+// (2q + h) m/8 + 4a + q' of a lane's coordinates then lies in word group 2q + h (m = 256) or
+// 4q + 2h + a / 8 (m = 512), bits 4 (a mod 8) + q': the lane loads m/64 word groups. One
+// 16-vector tile per step, and the output signs come from LDS (16 blocks x 4 words per lane
+// would not fit beside the 128 accumulators).
 template <int M, int BITS, bool BF16, bool OL = false>
 __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
+  static_assert(!OL || M <= 128, "outlier lists at m <= 128 only");
   constexpr int NB = M / 32, NWC = (M / 32) * BITS, NWT = NWC + 1;
   constexpr int C = dh_copies<BITS>(), NPAIR = 1 << (2 * BITS);
   constexpr int NS = 8 * NB;  // override slots per lane (coordinates of its group)
+  constexpr int VT = dh_vt<M>();
+  constexpr int NWG = M <= 128 ? 1 : M / 64;  // record word groups a lane reads
+  constexpr bool SG_LDS = M > 128;
   __shared__ uint32_t lut[2 * NPAIR * C];
-  // bf16 rows of a wave's step (16 kDhVT rows of M bf16 = M/8 16-byte chunks, chunk index
+  __shared__ uint4 s_sg[SG_LDS ? NB * 4 : 1];  // sign masks of block a', lane group q
+  // bf16 rows of a wave's step (16 VT rows of M bf16 = M/8 16-byte chunks, chunk index
   // XOR-swizzled with the row so the row-wise writes and chunk-wise reads spread over banks)
   constexpr int RCH = M / 8;
-  __shared__ uint4 stage[BF16 ? kDhWaves * 16 * kDhVT * RCH : 1];
+  __shared__ uint4 stage[BF16 ? kDhWaves * 16 * VT * RCH : 1];
   // override values: with bf16 rows they live in the last tile's row slice of the wave's stage
   // (16 rows of M bf16 = 64 lanes x NS bf16), free until that tile's rows are assembled
   __shared__ __attribute__((aligned(16))) uint16_t ov_own[(OL && !BF16) ? kDhWaves * 64 * NS : 8];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   uint16_t* const ovv =
-      (BF16 ? reinterpret_cast<uint16_t*>(stage + (wave * 16 * kDhVT + 16 * (kDhVT - 1)) * RCH)
+      (BF16 ? reinterpret_cast<uint16_t*>(stage + (wave * 16 * VT + 16 * (VT - 1)) * RCH)
             : ov_own + wave * 64 * NS) + lane * NS;
   static_assert(!OL || 16 * M * 2 == 64 * NS * 2, "override slots fill one tile's row slice");
   constexpr int RPK = 64 / RCH;  // rows per whole-row store instruction
@@ -162,55 +177,66 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
   }
   // signs of this lane's outputs d = 32 a' + 8q + [0, 8), as bf16-pair (or f32) sign masks:
   // byte q of sign word a' (a wave-uniform index, so a scalar load)
-  uint32_t sg[NB][4];
-#pragma unroll
-  for (int ap = 0; ap < NB; ++ap) {
-    const uint32_t byte = (a.tab.sign_words[ap] >> (8 * q)) & 0xFFu;
+  uint32_t sg[SG_LDS ? 1 : NB][4];
+  auto sign_masks = [&](int ap, int qq, uint32_t (&m4)[4]) {
+    const uint32_t byte = (a.tab.sign_words[ap] >> (8 * qq)) & 0xFFu;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {  // outputs 2h, 2h + 1 of the byte
       const uint32_t s0 = (byte >> (2 * h)) & 1u, s1 = (byte >> (2 * h + 1)) & 1u;
-      sg[ap][h] = BF16 ? ((s0 << 15) | (s1 << 31)) : (s0 | (s1 << 1));
+      m4[h] = BF16 ? ((s0 << 15) | (s1 << 31)) : (s0 | (s1 << 1));
     }
+  };
+  if constexpr (SG_LDS) {
+    for (int i = tid; i < NB * 4; i += 64 * kDhWaves) {
+      uint32_t m4[4];
+      sign_masks(i / 4, i % 4, m4);
+      s_sg[i] = make_uint4(m4[0], m4[1], m4[2], m4[3]);
+    }
+  } else {
+#pragma unroll
+    for (int ap = 0; ap < NB; ++ap) sign_masks(ap, q, sg[ap]);
   }
   __syncthreads();
   pair_copies<BITS, C>(lut, tid, 64 * kDhWaves);
   __syncthreads();
   const uint32_t* rec32 = reinterpret_cast<const uint32_t*>(a.rec);
-  const int64_t n_steps = (a.n + 16 * kDhVT - 1) / (16 * kDhVT);
+  const int64_t n_steps = (a.n + 16 * VT - 1) / (16 * VT);
   const int64_t stride = (int64_t)gridDim.x * kDhWaves;
-  // the lane's words (group q, all planes) and the norm of the vectors of a step
-  auto load = [&](int64_t st, uint32_t (&w)[kDhVT][BITS + 1]) {
+  // the lane's words (word groups q m/128 .. + NWG - 1, all planes) and the norm of the vectors
+  // of a step
+  constexpr int NW = NWG * BITS;
+  auto load = [&](int64_t st, uint32_t (&w)[VT][NW + 1]) {
 #pragma unroll
-    for (int vt = 0; vt < kDhVT; ++vt) {
-      int64_t v = st * 16 * kDhVT + 16 * vt + n16;
+    for (int vt = 0; vt < VT; ++vt) {
+      int64_t v = st * 16 * VT + 16 * vt + n16;
       v = v < a.n ? v : a.n - 1;
       const uint32_t* r = rec32 + v * NWT;
 #pragma unroll
-      for (int p = 0; p < BITS; ++p) w[vt][p] = r[(q * M / 128) * BITS + p];
-      w[vt][BITS] = r[NWC];
+      for (int p = 0; p < NW; ++p) w[vt][p] = r[(q * M / 128) * BITS + p];
+      w[vt][NW] = r[NWC];
     }
   };
   int64_t st = (int64_t)blockIdx.x * kDhWaves + wave;
-  uint32_t wn[kDhVT][BITS + 1];
+  uint32_t wn[VT][NW + 1];
   if (st < n_steps) load(st, wn);
   // let the first step's words land before the loop, so the wait at the loop head only covers
   // the path round the loop, where the previous step's stores may stay in flight
   // (vmcnt(0) expcnt(7) lgkmcnt(15))
   __builtin_amdgcn_s_waitcnt(0x0F70);
   for (; st < n_steps; st += stride) {
-    uint32_t w[kDhVT][BITS + 1];
+    uint32_t w[VT][NW + 1];
 #pragma unroll
-    for (int vt = 0; vt < kDhVT; ++vt)
+    for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
-      for (int p = 0; p <= BITS; ++p) w[vt][p] = wn[vt][p];
+      for (int p = 0; p <= NW; ++p) w[vt][p] = wn[vt][p];
     if (st + stride < n_steps) load(st + stride, wn);  // in flight during this step
 #pragma unroll
-    for (int vt = 0; vt < kDhVT; ++vt) {
+    for (int vt = 0; vt < VT; ++vt) {
       uint32_t ovm = 0;  // slots of this lane overridden by outlier entries
       if constexpr (OL) {
         // a lane past the end decodes the last record, whose row it stores again: with that
         // record's entries, so the bytes are the same
-        int64_t v = st * 16 * kDhVT + 16 * vt + n16;
+        int64_t v = st * 16 * VT + 16 * vt + n16;
         v = v < a.n ? v : a.n - 1;
         int64_t k = a.ol_off[v], e = a.ol_off[v + 1];
         if (e > a.ol_cap) e = a.ol_cap;
@@ -229,7 +255,10 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
         uint32_t hi[4], lo[4];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const uint32_t yb = gather_bytes<BITS>(w[vt], ((2 * q + half) * (M / 8)) % 32 + 4 * ab);
+          // word group (local j) and bit of plane position (2q + half) m/8 + 4 ab
+          const int j = M <= 128 ? 0 : M == 256 ? half : 2 * half + (ab >> 3);
+          const int sh = M <= 128 ? ((2 * q + half) * (M / 8)) % 32 + 4 * ab : 4 * (ab & 7);
+          const uint32_t yb = gather_bytes<BITS>(w[vt] + j * BITS, sh);
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             const uint32_t off = pair_word<BITS, C>(yb, 2 * s) + (lane & (C - 1));
@@ -274,21 +303,29 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
               y[ab + h][t] = u - v;
             }
           }
-      const float sc = __uint_as_float(w[vt][BITS]) * a.tab.inv_m;
+      const float sc = __uint_as_float(w[vt][NW]) * a.tab.inv_m;
+      auto sgn = [&](int ap, int h) -> uint32_t {
+        if constexpr (SG_LDS) {
+          const uint4 m4 = s_sg[ap * 4 + q];
+          return h == 0 ? m4.x : h == 1 ? m4.y : h == 2 ? m4.z : m4.w;
+        } else {
+          return sg[ap][h];
+        }
+      };
       if constexpr (BF16) {
         const int row = 16 * vt + n16;
 #pragma unroll
         for (int ap = 0; ap < NB; ++ap) {
           const floatx4 y0 = y[ap][0], y1 = y[ap][1];
           const int ch = 4 * ap + q;  // columns 32 a' + 8q .. + 7
-          stage[(wave * 16 * kDhVT + row) * RCH + (ch ^ (row & (RCH - 1)))] =
-              make_uint4(bf16_pair(y0[0] * sc, y0[1] * sc) ^ sg[ap][0],
-                         bf16_pair(y0[2] * sc, y0[3] * sc) ^ sg[ap][1],
-                         bf16_pair(y1[0] * sc, y1[1] * sc) ^ sg[ap][2],
-                         bf16_pair(y1[2] * sc, y1[3] * sc) ^ sg[ap][3]);
+          stage[(wave * 16 * VT + row) * RCH + (ch ^ (row & (RCH - 1)))] =
+              make_uint4(bf16_pair(y0[0] * sc, y0[1] * sc) ^ sgn(ap, 0),
+                         bf16_pair(y0[2] * sc, y0[3] * sc) ^ sgn(ap, 1),
+                         bf16_pair(y1[0] * sc, y1[1] * sc) ^ sgn(ap, 2),
+                         bf16_pair(y1[2] * sc, y1[3] * sc) ^ sgn(ap, 3));
         }
       } else {
-        int64_t v = st * 16 * kDhVT + 16 * vt + n16;
+        int64_t v = st * 16 * VT + 16 * vt + n16;
         // a lane past the end decoded the last record: it stores the last row's own bytes again
         v = v < a.n ? v : a.n - 1;
 #pragma unroll
@@ -300,7 +337,7 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
           float r[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            r[j] = __uint_as_float(__float_as_uint(o[j]) ^ (((sg[ap][j >> 1] >> (j & 1)) & 1u) << 31));
+            r[j] = __uint_as_float(__float_as_uint(o[j]) ^ (((sgn(ap, j >> 1) >> (j & 1)) & 1u) << 31));
           *reinterpret_cast<float4*>(yp) = make_float4(r[0], r[1], r[2], r[3]);
           *reinterpret_cast<float4*>(yp + 4) = make_float4(r[4], r[5], r[6], r[7]);
         }
@@ -310,14 +347,14 @@ __global__ __launch_bounds__(64 * kDhWaves) void k_decode_h(DecodeArgs a) {
       // whole rows: each instruction writes 64 consecutive 16-byte chunks of the step's rows,
       // as streaming (nontemporal) stores: the rows are not read again by this kernel
       __builtin_amdgcn_wave_barrier();
-      constexpr int CH = 16 * kDhVT * RCH / 64;
+      constexpr int CH = 16 * VT * RCH / 64;
       uint4 out[CH];
 #pragma unroll
       for (int k = 0; k < CH; ++k) {
         const int id = 64 * k + lane, row = id / RCH, ch = id % RCH;
-        out[k] = stage[(wave * 16 * kDhVT + row) * RCH + (ch ^ (row & (RCH - 1)))];
+        out[k] = stage[(wave * 16 * VT + row) * RCH + (ch ^ (row & (RCH - 1)))];
       }
-      const int64_t v0 = st * 16 * kDhVT;  // the step's first row
+      const int64_t v0 = st * 16 * VT;  // the step's first row
       uint16_t* const yp = static_cast<uint16_t*>(a.y) + v0 * a.ld + lane_off;
 #pragma unroll
       for (int k = 0; k < CH; ++k) {
@@ -593,7 +630,7 @@ static hipError_t launch_dh_k(const DecodeArgs& a, hipStream_t st) {
   // exactly one resident round (at most 4 blocks of 4 waves per compute unit, measured best
   // against 2 and 8), waves striding over the steps: a grid beyond what the chip holds at once
   // would leave its last blocks to run alone on part of the chip
-  const int64_t steps = (a.n + 16 * kDhVT - 1) / (16 * kDhVT);
+  const int64_t steps = (a.n + 16 * dh_vt<M>() - 1) / (16 * dh_vt<M>());
   int64_t blocks = (steps + kDhWaves - 1) / kDhWaves;
   const int64_t resident = (int64_t)dh_blocks_per_cu<M, BITS, BF16, OL>() * dh_device_cus();
   if (blocks > resident) blocks = resident;
@@ -604,9 +641,13 @@ static hipError_t launch_dh_k(const DecodeArgs& a, hipStream_t st) {
 
 template <int M, int BITS>
 static hipError_t launch_dh_t(bool bf16, const DecodeArgs& a, hipStream_t st) {
-  const bool ol = a.ol_off != nullptr;
-  if (bf16) return ol ? launch_dh_k<M, BITS, true, true>(a, st) : launch_dh_k<M, BITS, true, false>(a, st);
-  return ol ? launch_dh_k<M, BITS, false, true>(a, st) : launch_dh_k<M, BITS, false, false>(a, st);
+  if constexpr (M > 128) {  // no outlier list here (decode_h_supported)
+    return bf16 ? launch_dh_k<M, BITS, true, false>(a, st) : launch_dh_k<M, BITS, false, false>(a, st);
+  } else {
+    const bool ol = a.ol_off != nullptr;
+    if (bf16) return ol ? launch_dh_k<M, BITS, true, true>(a, st) : launch_dh_k<M, BITS, true, false>(a, st);
+    return ol ? launch_dh_k<M, BITS, false, true>(a, st) : launch_dh_k<M, BITS, false, false>(a, st);
+  }
 }
 
 template <int D, int R, int BITS>
@@ -665,14 +706,16 @@ static hipError_t launch_dh_m(int bits, bool bf16, const DecodeArgs& a, hipStrea
 }
 
 bool decode_h_supported(int D, int m, bool outliers) {
-  (void)outliers;  // outlier lists are merged into the B operands (one-byte indices at m <= 128)
-  return D == m && (m == 64 || m == 128);
+  // outlier lists are merged into the B operands at m <= 128 (one-byte indices)
+  return D == m && (m == 64 || m == 128 || ((m == 256 || m == 512) && !outliers));
 }
 
 hipError_t launch_decode_h(int m, int bits, bool bf16, const DecodeArgs& a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
   if (m == 64) return launch_dh_m<64>(bits, bf16, a, st);
   if (m == 128) return launch_dh_m<128>(bits, bf16, a, st);
+  if (m == 256) return launch_dh_m<256>(bits, bf16, a, st);
+  if (m == 512) return launch_dh_m<512>(bits, bf16, a, st);
   return hipErrorInvalidValue;
 }
 

@@ -559,7 +559,8 @@ struct LaneLut {
   }
 };
 
-// Q == 1 with the record's code words already in registers (lets a caller load them early).
+// Codes of a whole record (one lane per vector) looked up in lut, the record's code words
+// already in registers (lets a caller load them early).
 template <int M, int BITS, class Lut>
 __device__ __forceinline__ void unpack_lookup_words(const uint32_t (&w)[(M / 32) * BITS],
                                                     const Lut& lut, float (&zh)[M]) {
@@ -570,43 +571,6 @@ __device__ __forceinline__ void unpack_lookup_words(const uint32_t (&w)[(M / 32)
 #pragma unroll
     for (int p = 0; p < BITS; ++p) code |= ((w[(pos >> 5) * BITS + p] >> (pos & 31)) & 1u) << p;
     zh[k] = lut(code);
-  }
-}
-
-// Codes of this lane part's K coordinates looked up in the centroid table lut.
-//  Q == 1: words = the whole record's code words. Q > 1: words g as laid out above.
-template <int M, int BITS, class Lut>
-__device__ __forceinline__ void unpack_lookup_lv(const uint32_t* __restrict__ r32, int q,
-                                                 const Lut& lut,
-                                                 float (&zh)[LV<M>::K]) {
-  constexpr int Q = LV<M>::Q, K = LV<M>::K, NWC = (M / 32) * BITS;
-  if constexpr (Q == 1) {
-    uint32_t w[NWC];
-    load_words<NWC>(r32, w);
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int pos = plane_pos(k, M);
-      uint32_t code = 0;
-#pragma unroll
-      for (int p = 0; p < BITS; ++p) code |= ((w[(pos >> 5) * BITS + p] >> (pos & 31)) & 1u) << p;
-      zh[k] = lut(code);
-    }
-  } else {
-    const int sh = 16 * (q & 1);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int g = (M == 256) ? s : 2 * s + (q >> 1);
-      uint32_t w[BITS];
-#pragma unroll
-      for (int p = 0; p < BITS; ++p) w[p] = r32[g * BITS + p] >> sh;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        uint32_t code = 0;
-#pragma unroll
-        for (int p = 0; p < BITS; ++p) code |= ((w[p] >> t) & 1u) << p;
-        zh[8 * t + s] = lut(code);
-      }
-    }
   }
 }
 

@@ -194,7 +194,6 @@ template <int D, int BITS, bool SYM>
 __global__ __launch_bounds__(64 * kPqWaves) __attribute__((amdgpu_waves_per_eu(3)))
 void k_encode_pq(EncodeArgs a, int64_t tiles_per_block) {
   constexpr int R = 64, NT = R / 16, BCH = D / 8;
-  constexpr int CCH = D / 8;                       // input row in 16-byte chunks
   constexpr int RCH = 16;                          // region row stride: 16 chunks (64 f32)
   constexpr int NWC = 2 * BITS, NWT = NWC + 1;
   constexpr int KS = D / 32;                       // k-steps of the projection
@@ -775,12 +774,16 @@ static PcaGrid pca_grid(int64_t n) {
 
 template <int D, int R, int BITS, bool SYM>
 static hipError_t enc_t(const EncodeArgs& a, hipStream_t st) {
-  if constexpr (R == 64 && D <= 128) return enc_pq_t<D, BITS, SYM>(a, st);
-  if constexpr (R == 128) return enc_pt_t<D, BITS, SYM>(a, st);
-  const PcaGrid g = pca_grid<D, R>(a.n);
-  hipLaunchKernelGGL((k_encode_pca<D, R, BITS, SYM>), dim3(g.blocks), dim3(64 * PcaShape<D, R>::W), 0, st,
-                     a, g.per_block);
-  return hipGetLastError();
+  if constexpr (R == 64 && D <= 128) {
+    return enc_pq_t<D, BITS, SYM>(a, st);
+  } else if constexpr (R == 128) {
+    return enc_pt_t<D, BITS, SYM>(a, st);
+  } else {
+    const PcaGrid g = pca_grid<D, R>(a.n);
+    hipLaunchKernelGGL((k_encode_pca<D, R, BITS, SYM>), dim3(g.blocks), dim3(64 * PcaShape<D, R>::W), 0,
+                       st, a, g.per_block);
+    return hipGetLastError();
+  }
 }
 
 template <int D, int R>
