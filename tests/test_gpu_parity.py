@@ -90,7 +90,7 @@ def test_edge_vectors_zero_single_and_scaled():
     assert empty.shape[0] == 0
 
 
-@pytest.mark.parametrize("D,bits", [(128, 2), (64, 3), (128, 1)])
+@pytest.mark.parametrize("D,bits", [(128, 2), (64, 3), (128, 1), (256, 3), (512, 4), (512, 1)])
 @pytest.mark.parametrize("n", [1, 17, 255, 257, 4099])
 def test_decode_strided_output_and_ragged_n(D, bits, n):
     """Decode into rows wider than D (ld = D + 24): the columns past D stay untouched; vector
