@@ -289,6 +289,34 @@ def test_outlier_decode_bf16_rows_with_a_ragged_tail(D, bits, n):
                     extra_ulp_bf16=True)
 
 
+@pytest.mark.parametrize("D,cut", [(128, "none"), (128, "half"), (64, "half"), (256, "half")])
+def test_outlier_decode_with_a_list_cut_at_capacity(D, cut):
+    """Decode applies exactly the entries below the capacity (none at capacity 0): the vectors
+    whose span is cut keep their first entries, those past the cut keep none."""
+    bits, n = 2, 1500 + 9
+    x = _rows(n, D, seed=D + 61)
+    x[:, 9] *= 14
+    codec = kvq.Codec(D, bits, seed=13, outlier_T=1.6)
+    full = kvq.Outliers(codec, n, capacity=n * D // 2, device=DEV)
+    rec, total = kvq.encode(codec, x, outliers=full, want_total=True)
+    cap = 0 if cut == "none" else total // 2 + 5
+    part = kvq.Outliers(codec, n, capacity=cap, device=DEV)
+    say(f"outlier decode with the list cut at {cap} of {total} entries, D={D}")
+    rec_p = kvq.encode(codec, x, outliers=part)
+    torch.cuda.synchronize()
+    assert torch.equal(rec_p, rec)
+    recn = rec.cpu().numpy()
+    off = part.offsets.cpu().numpy().view(np.uint32)
+    idx = part.idx.cpu().numpy()[:cap]
+    val = part.val.cpu().numpy().view(np.uint16)[:cap]
+    yref = oracle.decode(oracle_codec_like(codec), recn, off, idx, val)
+    norms = unpack_records(recn, D, bits)[1]
+    for dt in (torch.float32, torch.bfloat16):
+        y = kvq.decode(codec, rec_p, outliers=part, dtype=dt)
+        compare_decoded(y.float().cpu().numpy(), yref, norms, f"decode cut at {cap} ({dt})",
+                        extra_ulp_bf16=dt == torch.bfloat16)
+
+
 @pytest.mark.parametrize("T_", [2.2, 1.85, 1.3])
 def test_outlier_list_cut_at_capacity_is_a_prefix(T_):
     """A list cut short by the capacity holds exactly the first `capacity` entries of the full
