@@ -64,10 +64,10 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
       zh[j] = __uint_as_float(__float_as_uint(zh[j] * scale) ^ (((sbyte >> j) & 1u) << 31));
     if constexpr (BF16) {
       uint4 o;
-      o.x = f32_to_bf16_rne(zh[0]) | (f32_to_bf16_rne(zh[1]) << 16);
-      o.y = f32_to_bf16_rne(zh[2]) | (f32_to_bf16_rne(zh[3]) << 16);
-      o.z = f32_to_bf16_rne(zh[4]) | (f32_to_bf16_rne(zh[5]) << 16);
-      o.w = f32_to_bf16_rne(zh[6]) | (f32_to_bf16_rne(zh[7]) << 16);
+      o.x = pack_bf16x2(zh[0], zh[1]);
+      o.y = pack_bf16x2(zh[2], zh[3]);
+      o.z = pack_bf16x2(zh[4], zh[5]);
+      o.w = pack_bf16x2(zh[6], zh[7]);
       st_stream(static_cast<uint16_t*>(a.y) + vec * a.ld + 8 * c, o);  // rows are written once
     } else {
       float* yr = static_cast<float*>(a.y) + vec * a.ld + 8 * c;

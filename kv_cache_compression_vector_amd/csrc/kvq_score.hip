@@ -57,6 +57,17 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
   lo = f32_to_bf16_rne(x - __uint_as_float(hi << 16));
 }
 
+// The same split of two f32 at once, as packed pairs (x0 in the low halves): two
+// v_cvt_pk_bf16_f32 (round to nearest even, as above) around the two residuals.
+__device__ __forceinline__ void split_bf16_pair(float x0, float x1, uint32_t& hp, uint32_t& lp) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const f2 v = {x0, x1};
+  hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+  const f2 r = {x0 - __uint_as_float(hp << 16), x1 - __uint_as_float(hp & 0xFFFF0000u)};
+  lp = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, b2));
+}
+
 // Pair-table index of the coordinates at bits sh + pr, sh + pr + 1 of the b plane words w:
 // bit 2p + i of the index = plane p of coordinate i. For b = 2, 3 the planes' bit pairs are
 // gathered into one word (byte p = plane p) and brought together by one 24-bit multiply:
@@ -786,15 +797,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_attend(AttendArgs a) {
         const float4 w0 = *reinterpret_cast<const float4*>(&pst[wave][tok][8 * oct]);
         const float4 w1 = *reinterpret_cast<const float4*>(&pst[wave][tok][8 * oct + 4]);
         const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        uint32_t hi[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) split_bf16(w[e], hi[e], lo[e]);
         uint32_t hp[4], lp[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          hp[d] = hi[2 * d] | (hi[2 * d + 1] << 16);
-          lp[d] = lo[2 * d] | (lo[2 * d + 1] << 16);
-        }
+        for (int d = 0; d < 4; ++d) split_bf16_pair(w[2 * d], w[2 * d + 1], hp[d], lp[d]);
         if constexpr (IL) {
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq) {
