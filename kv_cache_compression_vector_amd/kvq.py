@@ -329,20 +329,50 @@ class Cache:
         return self.tail[idx]
 
 
-def append_evict_chunk(codec: Codec, caches: list[Cache], new_rows: list[torch.Tensor] | None,
-                       t_new: int):
-    n = len(caches)
-    arr = (ctypes.POINTER(_Cache) * n)(*[ctypes.pointer(c._s) for c in caches])
+class CacheSet:
+    """A fixed list of caches with its C pointer array built once, for repeated
+    append_evict_chunk calls (a serving loop appends to the same caches every step)."""
+
+    def __init__(self, caches: list[Cache]):
+        self.caches = list(caches)
+        n = len(self.caches)
+        self.arr = (ctypes.POINTER(_Cache) * n)(*[ctypes.pointer(c._s) for c in self.caches])
+        self.rows = (ctypes.c_void_p * n)()
+        self.ev = (ctypes.c_int64 * n)()
+
+    def __len__(self):
+        return len(self.caches)
+
+
+def append_evict_chunk(codec: Codec, caches, new_rows, t_new: int):
+    """Append t_new rows to each cache and evict whole chunks (kvq_append_evict_chunk).
+
+    caches: a list of Cache or a CacheSet. new_rows: None (t_new = 0), a list with one bf16
+    tensor of >= t_new contiguous rows per cache, or one bf16 tensor [n_caches, >= t_new, D]
+    whose rows are contiguous within each cache (any stride between caches). Returns the
+    chunks evicted per cache."""
+    cs = caches if isinstance(caches, CacheSet) else CacheSet(caches)
+    n = len(cs)
     rows = None
     if t_new > 0:
-        assert new_rows is not None and len(new_rows) == n
-        for r in new_rows:
-            assert r.dtype == torch.bfloat16 and r.is_contiguous() and r.shape[0] >= t_new
-        rows = (ctypes.c_void_p * n)(*[r.data_ptr() for r in new_rows])
-    ev = (ctypes.c_int64 * n)()
-    dev = caches[0].tail if n else None
-    _check(lib().kvq_append_evict_chunk(codec.ref, arr, n, rows, t_new, _stream(dev), ev))
-    return list(ev)
+        assert new_rows is not None
+        if isinstance(new_rows, torch.Tensor):
+            D = cs.caches[0].codec.head_dim if n else 0
+            assert new_rows.dtype == torch.bfloat16 and new_rows.dim() == 3 and new_rows.shape[0] == n
+            assert new_rows.shape[1] >= t_new and new_rows.shape[2] == D
+            assert new_rows.stride(2) == 1 and new_rows.stride(1) == D
+            base, step = new_rows.data_ptr(), new_rows.stride(0) * 2
+            for i in range(n):
+                cs.rows[i] = base + i * step
+        else:
+            assert len(new_rows) == n
+            for i, r in enumerate(new_rows):
+                assert r.dtype == torch.bfloat16 and r.is_contiguous() and r.shape[0] >= t_new
+                cs.rows[i] = r.data_ptr()
+        rows = cs.rows
+    dev = cs.caches[0].tail if n else None
+    _check(lib().kvq_append_evict_chunk(codec.ref, cs.arr, n, rows, t_new, _stream(dev), cs.ev))
+    return list(cs.ev)
 
 
 def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:

@@ -387,6 +387,33 @@ def test_append_evict_matches_oracle_model():
     _append_evict_against_model(200, 16, 1500, [700, 1, 1, 129, 0, 1, 300, 5, 0, 1])
 
 
+def test_append_evict_with_a_cache_set_and_one_row_tensor():
+    """The binding's reusable CacheSet with one [n_caches, t, D] row tensor (rows of different
+    caches at any stride) drives the same calls as a list of caches and per-cache tensors: the
+    packed regions and tails end bit-identical, across evictions."""
+    D, bits, L = 128, 3, 3
+    codec = kvq.Codec(D, bits, seed=91)
+    mk = lambda: [kvq.Cache(codec, packed_cap=2048, tail_cap=700, window=160, margin=16, device=DEV)
+                  for _ in range(L)]
+    a, b = mk(), mk()
+    cs = kvq.CacheSet(b)
+    say(f"append/evict through a CacheSet, {L} caches")
+    big = _rows(L * 1200, D, seed=5).view(L, 1200, D)
+    t = 0
+    for t_new in (300, 1, 1, 129, 0, 250, 1, 77):
+        rows = big[:, t:t + t_new] if t_new else None
+        ev_a = kvq.append_evict_chunk(codec, a, [rows[i] for i in range(L)] if t_new else None, t_new)
+        ev_b = kvq.append_evict_chunk(codec, cs, rows, t_new)
+        assert ev_a == ev_b
+        t += t_new
+    torch.cuda.synchronize()
+    for ca, cb in zip(a, b):
+        assert (ca.packed_len, ca.tail_len, ca.tail_head) == (cb.packed_len, cb.tail_len, cb.tail_head)
+        assert ca.packed_len > 0
+        assert torch.equal(ca.packed[: ca.packed_len], cb.packed[: cb.packed_len])
+        assert torch.equal(ca.tail_rows(), cb.tail_rows())
+
+
 def test_append_evict_tail_ring_wraps():
     """A 480-row tail ring whose head passes its end several times: the evicted chunks read
     rows across the wrap."""
